@@ -1,0 +1,199 @@
+"""Batch-1 decode benchmark on one MI355X.
+
+Workload: the 2B-class dense decoder (28 layers, hidden 2048, 16 query / 8 KV
+heads of 128, SwiGLU 8192, vocab 32000, BF16 weights ~N(0, 0.02)), BF16 KV
+cache prefilled with N(0, 1) to 4096 positions, greedy decode at batch 1.
+One step = one decode_step call = one persistent-kernel launch that runs all
+28 layers, the LM head and the argmax; the token of step i+1 is the argmax of
+step i, read on the device (no host round trip inside the timed region).
+
+Prints one JSON line (see the keys below).  --gpus N with N > 1 exits: this
+build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak, GB/s
+
+
+def algorithmic_bytes(cfg, pos: int) -> tuple[int, int]:
+    """(weight bytes, KV bytes) one step at `pos` must read at least once.
+
+    Weights: every BF16 matrix of every layer, the two norm gains per layer,
+    the embedding row, the final norm and the LM head.  KV: K and V of
+    positions [0, pos] for every layer and KV head (the step's own K/V
+    included)."""
+    H, d = cfg.hidden, cfg.head_dim
+    per_layer = 2 * (2 * H + (cfg.n_q_heads + 2 * cfg.n_kv_heads) * d * H + H * cfg.n_q_heads * d
+                     + 3 * cfg.ffn * H)
+    w = cfg.n_layers * per_layer + 2 * H + 2 * H + 2 * cfg.vocab * H
+    kv = (pos + 1) * cfg.n_layers * 2 * cfg.n_kv_heads * d * 2
+    return w, kv
+
+
+def cpu_baseline(cfg, host, steps: int = 3):
+    """Time the CPU oracle (float64, as it stands) on a few decode steps."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from oracle import OracleCache, OracleModel
+    from synth import gen
+
+    om = OracleModel(cfg, host)
+    oc = OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim)
+    for li in range(cfg.n_layers):
+        k, v = gen.kv_prefill_bf16(cfg, li)
+        oc.k[li][:cfg.prefill] = k
+        oc.v[li][:cfg.prefill] = v
+    toks = gen.prompt_tokens(cfg, steps + 1)
+    t0 = time.perf_counter()
+    om.step(oc, int(toks[0]), cfg.prefill)          # dequantises and caches the weights
+    t_first = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(steps):
+        om.step(oc, int(toks[i + 1]), cfg.prefill + 1 + i)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    return {"value": steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"{steps} float64 oracle decode steps of the same workload at positions "
+                       f"{cfg.prefill + 1}..{cfg.prefill + steps} after one untimed step "
+                       f"({t_first:.1f} s) that converted and cached the weights; "
+                       f"host cpu_count {os.cpu_count()}")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--trace", default="",
+                    help="after the timed region, run one traced step and save its per-task stamps (.npy)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has no "
+              "multi-GPU mode in this build", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from memory_bound_gemv_amd.device_model import DeviceModel
+    from synth import CONFIGS, gen
+
+    cfg = CONFIGS["dense2b"]
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    host = gen.dense_weights(cfg)
+    dm = DeviceModel(cfg, host, gen.page_table(cfg), device=dev, k_max=1)
+    for li in range(cfg.n_layers):
+        k, v = gen.kv_prefill_bf16(cfg, li)
+        dm.prefill_bf16(li, k, v)
+    dm.init()
+    torch.cuda.synchronize()
+    t_gen = time.perf_counter() - t_gen
+    info = dm.info()
+
+    stream = torch.cuda.current_stream(dev)
+    buf = torch.tensor([int(gen.prompt_tokens(cfg, 1)[0])], dtype=torch.int32, device=dev)
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device=dev)
+    n_slots = cfg.n_decode                     # positions prefill .. prefill + 255
+    pos_of = lambda i: cfg.prefill + (i % n_slots)
+
+    for i in range(args.warmup):
+        dm.step(buf, pos_of(i), logits, buf)
+    torch.cuda.synchronize()
+    if dm.status() != 0:
+        raise RuntimeError("device status after warm-up")
+
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    start.record(stream)
+    for i in range(args.steps):
+        dm.step(buf, pos_of(args.warmup + i), logits, buf)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    st = dm.status()
+    if st != 0:
+        raise RuntimeError(f"device status {st}")
+    ms = start.elapsed_time(end)
+    ms_per_step = ms / args.steps
+    tok_s = args.steps / (ms / 1e3)
+
+    wbytes, _ = algorithmic_bytes(cfg, 0)
+    kv_avg = float(np.mean([algorithmic_bytes(cfg, pos_of(args.warmup + i))[1] for i in range(args.steps)]))
+    step_bytes = wbytes + kv_avg
+    achieved = step_bytes / (ms_per_step / 1e3) / 1e9
+
+    if args.trace:
+        from memory_bound_gemv_amd import _mbg as M
+        M.mbg_set_trace(dm.ctx, True)
+        dm.step(buf, pos_of(args.warmup + args.steps), logits, buf)
+        rec = M.mbg_read_trace(dm.ctx, info.n_tasks)
+        M.mbg_set_trace(dm.ctx, False)
+        np.save(args.trace, rec)
+        np.save(args.trace.replace(".npy", "_meta.npy"),
+                np.array([info.clock_khz, info.grid, cfg.n_layers], dtype=np.int64))
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * 1024 * 1024 // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+    out = {
+        "metric": "batch-1 decode tokens/s and achieved HBM GB/s (MBU % of peak) on 1 MI355X",
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {
+            "workload": "dense 2B decoder: 28 layers, hidden 2048, 16 query / 8 KV heads of 128, SwiGLU 8192, "
+                        "vocab 32000, BF16 weights N(0,0.02), BF16 KV prefilled N(0,1) to 4096 positions, "
+                        "batch 1, greedy decode at positions 4096..4351",
+            "weight_dtype": "bf16", "kv_dtype": "bf16", "accumulate": "fp32",
+            "global_batch": 1, "seq_len": cfg.prefill, "parallelism": "none (1 GPU)",
+            "kernel": info.variant.decode(), "grid": info.grid, "launches_per_step": info.launches_per_step,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4),
+            "traffic": None,
+        },
+        "bytes_per_step": {"weights": wbytes, "kv_avg": round(kv_avg), "total": round(step_bytes)},
+        "bound_tokens_s": round(PEAK_HBM_GBS * 1e9 / step_bytes, 1),
+        "wall_tokens_s": round(args.steps / wall, 2),
+        "setup_s": round(t_gen, 1),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(cfg, host)
+    print(json.dumps(out), flush=True)
+    dm.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,264 @@
+/*
+ * mbg: batch-1 transformer decode on one MI355X (gfx950), one kernel launch
+ * per decode step.
+ *
+ * What a step computes.  At batch 1 every generated token is a chain of
+ * matrix-vector products that streams every active weight byte from HBM
+ * once (Kog article "Real-time LLM inference on standard GPUs: 3k tokens/s
+ * per request", section on memory bandwidth as the bottleneck).  A step
+ * embeds one token, runs every decoder layer (RMSNorm, Q/K/V projections,
+ * RoPE, K/V write into a paged cache, grouped single-query attention over
+ * positions [0, pos], output projection, RMSNorm, SwiGLU FFN or a routed
+ * mixture of experts) and ends with the LM head and an argmax.  The whole
+ * chain runs as one persistent kernel instead of a launch per operation
+ * (same article, sections on where standard stacks lose microseconds and on
+ * the monokernel runtime; the "Muse Spark Open: 1,109 tokens/s" megakernel
+ * article, sections on the launch baseline and the kernel boundary).
+ *
+ * Conventions for every call:
+ *   - "device" pointers point into HIP device memory of the current device;
+ *     "host" pointers into ordinary process memory.
+ *   - Matrices are row-major [rows][cols] with cols contiguous, 16-byte
+ *     aligned rows.  BF16 is the top half of an IEEE binary32.  FP8 is OCP
+ *     E4M3FN.  MXFP4 is OCP E2M1 (element 2i in the low nibble of byte i)
+ *     with one E8M0 scale byte per 32 consecutive elements of a row.
+ *   - The caller owns every buffer (weights, KV pool, page table, workspace,
+ *     outputs).  The library never allocates or frees device memory; an
+ *     mbg_ctx is a host object.
+ *   - Calls that take a stream enqueue work on it and return without
+ *     waiting.  A stream is a hipStream_t passed as void* (NULL = the null
+ *     stream).
+ *   - Return value 0 on success, a negative MBG_E_* code otherwise; no
+ *     exception crosses this boundary.  mbg_last_error() gives the text of
+ *     the last failure on the calling thread.
+ */
+#ifndef MBG_H
+#define MBG_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---------------------------------------------------------------- errors */
+#define MBG_OK 0
+#define MBG_E_INVALID_ARG -1     /* null pointer, bad shape, misaligned row  */
+#define MBG_E_UNSUPPORTED -2     /* shape/dtype combination not compiled in  */
+#define MBG_E_DTYPE_MISMATCH -3  /* tensor dtype or scale not what it must be */
+#define MBG_E_RANGE -4           /* pos/k/token outside the configured range */
+#define MBG_E_WORKSPACE -5       /* workspace missing or smaller than needed */
+#define MBG_E_HIP -6             /* a HIP runtime call failed                */
+#define MBG_E_TIMEOUT -7         /* a device wait exceeded its deadline      */
+
+/* ---------------------------------------------------------------- dtypes */
+#define MBG_BF16 1
+#define MBG_FP8_E4M3 2  /* one binary32 scale per row: value = code * scale[row] */
+#define MBG_MXFP4 3     /* scale = E8M0 bytes [rows][cols/32]                   */
+#define MBG_FP32 4
+
+/*
+ * A weight tensor: `n` stacked matrices of shape [rows][cols] (n = 1 for a
+ * plain matrix, n = experts for stacked expert weights).
+ *   BF16:  data = uint16 [n][rows][cols];            scale = NULL
+ *   FP8:   data = uint8  [n][rows][cols];            scale = float [n][rows]
+ *   MXFP4: data = uint8  [n][rows][cols/2];          scale = uint8 [n][rows][cols/32]
+ * A 1-D tensor (norm gains) has rows = 1.  data/scale are device pointers.
+ */
+typedef struct {
+    int32_t dtype;
+    int32_t n;
+    int64_t rows;
+    int64_t cols;
+    const void *data;
+    const void *scale;
+} mbg_tensor;
+
+/* One decoder layer.  Dense layers fill w_gate/w_up/w_down; MoE layers fill
+ * w_router, exp_gate_up, exp_down and (if n_shared > 0) sh_gate_up, sh_down.
+ * Shapes (H hidden, d head_dim, F ffn, E experts, M moe_ffn, S n_shared):
+ *   attn_norm, ffn_norm: BF16 [1][H]
+ *   wq: BF16 [Hq*d][H]    wk, wv: BF16 [Hkv*d][H]    wo: BF16 [H][Hq*d]
+ *   w_gate, w_up: BF16 [F][H]    w_down: BF16 [H][F]
+ *   w_router: BF16 [E][H]
+ *   exp_gate_up: MXFP4 n=E [2M][H] (rows 0..M-1 gate, M..2M-1 up)
+ *   exp_down:    MXFP4 n=E [H][M]
+ *   sh_gate_up:  MXFP4 n=S [2M][H]    sh_down: MXFP4 n=S [H][M]
+ */
+typedef struct {
+    mbg_tensor attn_norm, wq, wk, wv, wo, ffn_norm;
+    mbg_tensor w_gate, w_up, w_down;
+    mbg_tensor w_router, exp_gate_up, exp_down, sh_gate_up, sh_down;
+} mbg_layer;
+
+typedef struct {
+    const mbg_layer *layers; /* host array [n_layers]; read during init only */
+    mbg_tensor embed;        /* BF16 [V][H] */
+    mbg_tensor final_norm;   /* BF16 [1][H] */
+    mbg_tensor lm_head;      /* BF16 or FP8 [V][H] */
+} mbg_weights;
+
+/*
+ * Paged KV cache.  pool (device) holds
+ *     [n_layers][n_pages][2 (K, V)][n_kv_heads][page_size][head_dim]
+ * elements of `dtype` (MBG_BF16 or MBG_FP8_E4M3).  Position t of a layer
+ * lives in physical page page_table[t / page_size], slot t % page_size.
+ * page_table (device int32 [ceil(max_pos / page_size)]) maps logical to
+ * physical pages; the identity table is a contiguous cache.  scales (device
+ * float [n_layers][n_kv_heads][2], FP8 only, NULL for BF16) give
+ * value = decode(code) * scale per (layer, KV head, K or V).  Paged FP8 KV
+ * with a per-head scale is what the wmrh.cn Kimi-K3 long-context report
+ * deploys (test environment table; warnings section, where both engines
+ * fell back to a scale of 1.0 because none was supplied).
+ */
+typedef struct {
+    int32_t dtype;
+    int32_t n_pages;
+    void *pool;
+    const int32_t *page_table;
+    const float *scales;
+} mbg_kv;
+
+typedef struct {
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+    int32_t n_experts, top_k, n_shared, moe_ffn; /* n_experts = 0: dense */
+    float rope_theta; /* RoPE base; pairs (i, i + d/2) turn by pos * theta^(-2i/d) */
+    float rms_eps;    /* RMSNorm: x / sqrt(mean(x^2) + eps) * g */
+    int32_t page_size;
+    int32_t max_pos;  /* KV capacity in positions */
+    int32_t k_max;    /* widest verify window, 1..4 */
+} mbg_config;
+
+/* What an initialised context runs (the 163.com Ling-3.0-flash article,
+ * section on the FP8 LM head and MTP pitfall, reports a silent fallback
+ * that read FP8 weights as BF16; this lets a caller check at start-up which
+ * path is really active). */
+typedef struct {
+    int32_t grid;             /* workgroups of the persistent kernel */
+    int32_t block;            /* threads per workgroup */
+    int32_t n_tasks;          /* tasks per step */
+    int32_t launches_per_step;
+    int32_t lm_dtype, kv_dtype, expert_dtype, attn_dtype;
+    int32_t attn_splits;      /* split-KV partitions per KV head */
+    int32_t trace;            /* 1 while in-kernel trace stamps are on (mbg_set_trace) */
+    int64_t weight_bytes_per_step; /* bytes of weights one step reads (dense/shared; MoE routed excluded) */
+    int64_t workspace_bytes;
+    int64_t clock_khz;        /* rate of the device clock the trace stamps count */
+    char variant[64];
+} mbg_info;
+
+typedef struct mbg_ctx mbg_ctx;
+
+/* ------------------------------------------------------ decode context */
+
+/* Bytes of device workspace a context for `cfg` needs. */
+int mbg_workspace_size(const mbg_config *cfg, size_t *bytes);
+
+/* Host-only check of a configuration, weight set and KV description: shapes,
+ * dtypes, scale presence, alignment, supported combinations.  Makes no HIP
+ * call and touches no device memory.  w or kv may be NULL to check less. */
+int mbg_validate(const mbg_config *cfg, const mbg_weights *w, const mbg_kv *kv);
+
+/* Validate, build the static per-step task list and dependency counters in
+ * the caller's workspace (device, >= mbg_workspace_size bytes, 256-byte
+ * aligned) with copies enqueued on `stream`, and return a host context.
+ * The weights, KV pool and workspace must outlive the context. */
+int mbg_decode_init(const mbg_config *cfg, const mbg_weights *w, const mbg_kv *kv,
+                    void *d_workspace, size_t workspace_bytes, void *stream, mbg_ctx **out);
+
+/* One decode step, one kernel launch on the init stream.  Reads the token
+ * id at d_token[0] (device int32; may alias the previous step's d_argmax so
+ * a greedy loop needs no host round trip), writes K/V of every layer at
+ * `pos`, attends over [0, pos], and writes logits (device float [vocab], may
+ * be NULL) and the argmax (device int32 [1], lowest index among equal
+ * maxima).  Token ids outside [0, vocab) are clamped on the device and
+ * latch MBG_E_RANGE (reported by mbg_get_status).  Returns MBG_E_RANGE if
+ * pos is outside [0, max_pos). */
+int mbg_decode_step(mbg_ctx *ctx, const int32_t *d_token, int32_t pos,
+                    float *d_logits, int32_t *d_argmax);
+
+/* Verify window: k tokens (device int32 [k], 1 <= k <= k_max) at positions
+ * pos .. pos+k-1 in one launch, each weight byte read once for all k.
+ * Token j attends [0, pos + j], the window's earlier tokens included
+ * (163.com Ling-3.0-flash article, section on MTP speculative decoding: the
+ * target model checks a 4-token window in one pass).  Writes K/V at all k
+ * positions, logits [k][vocab] (may be NULL) and argmax [k].  Accepting a
+ * prefix and rolling back is the caller's job: the next call's pos decides
+ * which cached positions count. */
+int mbg_decode_verify(mbg_ctx *ctx, const int32_t *d_tokens, int32_t k, int32_t pos,
+                      float *d_logits, int32_t *d_argmax);
+
+/* Wait for the init stream, then return the latched device status (0, or
+ * MBG_E_TIMEOUT / MBG_E_RANGE from a kernel) and clear it. */
+int mbg_get_status(mbg_ctx *ctx);
+
+/* Describe the active configuration (see mbg_info). */
+int mbg_query(const mbg_ctx *ctx, mbg_info *info);
+
+/* Set the device wait deadline in microseconds (default 2,000,000).  A wait
+ * on a dependency counter that exceeds it makes its workgroup record
+ * MBG_E_TIMEOUT and leave; every other wait then ends the same way, so the
+ * launch always drains. */
+int mbg_set_timeout_us(mbg_ctx *ctx, int64_t us);
+
+/* Per-task self-profiling.  With `on` != 0, every later step makes thread 0
+ * of each workgroup record, for each task it runs, eight uint64 words: the
+ * device clock at task start, when its dependency wait was satisfied, when
+ * its input vector was loaded, when its weight/KV stream finished, and at
+ * task end; then (op | layer << 8 | tile << 32) and two zero words.  An external profiler
+ * sees one long kernel per step, so the kernel times itself (the "Muse Spark
+ * Open: 1,109 tokens/s" article describes the same in-kernel stamps, section
+ * on where the step time goes).  Stamps do not change any result. */
+int mbg_set_trace(mbg_ctx *ctx, int on);
+
+/* Wait for the init stream and copy the last step's trace records (n_tasks
+ * records of 8 uint64, in task-list order) into host memory; *n_out is the
+ * record count.  Fails with MBG_E_INVALID_ARG if tracing is off. */
+int mbg_read_trace(mbg_ctx *ctx, uint64_t *host_records, size_t max_records, size_t *n_out);
+
+/* Text of the last error on this thread ("" if none). */
+const char *mbg_last_error(void);
+
+/* Free the host context.  Does not touch caller memory. */
+void mbg_destroy(mbg_ctx *ctx);
+
+/* ------------------------------------------------ standalone operations */
+
+/* Bytes of device workspace mbg_lm_head needs for k columns. */
+int mbg_lm_head_workspace_size(int32_t k, size_t *bytes);
+
+/* LM head GEMV fused with argmax: logits[j][v] = sum_i W[v][i] * x[j][i]
+ * for j < k (1..4), W BF16 or FP8 (scale applied after accumulation), x
+ * device float [k][H].  Writes logits (device float [k][V], may be NULL)
+ * and argmax (device int32 [k]).  d_workspace (>= the size above) must be
+ * zero-filled before its first use; every call leaves it zeroed again.
+ * Calls sharing one workspace must not overlap.  The 163.com Ling-3.0-flash
+ * article singles the 157,184 x 2,560 LM head out as a block read whole for
+ * every token (section "optimisation 2"). */
+int mbg_lm_head(const mbg_tensor *w, const float *d_x, int32_t k, float *d_logits,
+                int32_t *d_argmax, void *d_workspace, size_t workspace_bytes, void *stream);
+
+/* Online FP8 quantisation of a BF16 matrix with one scale per row (163.com
+ * Ling-3.0-flash article, "optimisation 2: online FP8 LM head
+ * quantisation"): scale[r] = max_i |W[r][i]| / 448 in binary32 (1.0 for an
+ * all-zero row), codes[r][i] = E4M3FN(W[r][i] / scale[r]) with the division
+ * in binary32, rounded to nearest-even and saturated at +-448.
+ * d_w device uint16 [rows][cols]; d_codes device uint8 [rows][cols];
+ * d_scales device float [rows].  cols must be a multiple of 16. */
+int mbg_quantize_fp8_rows(const uint16_t *d_w, int64_t rows, int64_t cols, uint8_t *d_codes,
+                          float *d_scales, void *stream);
+
+/* Write n consecutive positions pos0 .. pos0+n-1 of one layer's K and V
+ * into the paged cache in its storage format (BF16 nearest-even, or FP8
+ * value / scale in binary32, nearest-even, saturating), the same rounding a
+ * decode step applies to the K/V it produces.  d_k, d_v: device float
+ * [n][n_kv_heads][head_dim].  Used to fill a cache from a prefill. */
+int mbg_kv_write(const mbg_config *cfg, const mbg_kv *kv, int32_t layer, int32_t pos0, int32_t n,
+                 const float *d_k, const float *d_v, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MBG_H */

@@ -1,0 +1,644 @@
+// C-ABI of the decode library: validation, workspace plan, static task list,
+// one cooperative launch per decode step.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "mbg.h"
+#include "layout.h"
+#include "ops.h"
+
+using namespace mbg;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(MBG_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define HIP_TRY(call)                                   \
+    do {                                                \
+        hipError_t e_ = (call);                         \
+        if (e_ != hipSuccess) return hip_fail(e_, #call); \
+    } while (0)
+
+constexpr int kMaxGrid = 1024;   // workgroups of the persistent kernel (upper bound)
+constexpr int kMaxSplits = 64;   // split-KV partitions per KV head (upper bound)
+constexpr int kBlock = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Workspace sections, in bytes from the base.
+struct Plan {
+    size_t status, keys, ctr, head_ctr, task_off, tasks, layers, inv_freq;
+    size_t xres, qbuf, part, attn, hbuf, route_w, route_idx, trace, total;
+    size_t n_ctr, max_tasks, zero_bytes;
+};
+
+Plan make_plan(const mbg_config& c) {
+    Plan p{};
+    const size_t k = (size_t)c.k_max;
+    const size_t L = (size_t)c.n_layers;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t o = off;
+        off = align_up(off + bytes, 256);
+        return o;
+    };
+    p.status = take(16);
+    p.keys = take(8 * 4);
+    p.n_ctr = L * PH_COUNT;
+    p.ctr = take(4 * p.n_ctr);
+    p.head_ctr = take(4 * L * (size_t)c.n_kv_heads);
+    p.zero_bytes = off;  // everything above starts at zero
+    p.task_off = take(4 * (kMaxGrid + 1));
+    p.max_tasks = (size_t)kMaxGrid * (8 * L + 1);
+    p.tasks = take(sizeof(Task) * p.max_tasks);
+    p.layers = take(sizeof(LayerPtrs) * L);
+    p.inv_freq = take(8 * (size_t)(c.head_dim / 2));
+    p.xres = take(4 * k * c.hidden);
+    p.qbuf = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
+    p.part = take(4 * k * (size_t)c.n_q_heads * kMaxSplits * (c.head_dim + 2));
+    p.attn = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
+    size_t hw = (size_t)c.ffn;
+    const size_t moe_w = (size_t)(c.top_k + c.n_shared) * c.moe_ffn;
+    if (moe_w > hw) hw = moe_w;
+    p.hbuf = take(4 * k * hw);
+    p.route_w = take(4 * k * (size_t)(c.top_k > 0 ? c.top_k : 1));
+    p.route_idx = take(4 * k * (size_t)(c.top_k > 0 ? c.top_k : 1));
+    p.trace = take(64 * p.max_tasks);
+    p.total = off;
+    return p;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_tensor(const mbg_tensor& t, const char* name, int dtype, int64_t n, int64_t rows, int64_t cols) {
+    if (t.data == nullptr) return fail(MBG_E_INVALID_ARG, "%s: data is NULL", name);
+    if (t.dtype != dtype)
+        return fail(MBG_E_DTYPE_MISMATCH, "%s: dtype %d, expected %d", name, t.dtype, dtype);
+    if (t.n != n || t.rows != rows || t.cols != cols)
+        return fail(MBG_E_INVALID_ARG, "%s: shape [%d][%lld][%lld], expected [%lld][%lld][%lld]", name, t.n,
+                    (long long)t.rows, (long long)t.cols, (long long)n, (long long)rows, (long long)cols);
+    if (!aligned16(t.data)) return fail(MBG_E_INVALID_ARG, "%s: data not 16-byte aligned", name);
+    const bool needs_scale = dtype == MBG_FP8_E4M3 || dtype == MBG_MXFP4;
+    if (needs_scale && t.scale == nullptr) return fail(MBG_E_DTYPE_MISMATCH, "%s: scale missing", name);
+    if (!needs_scale && t.scale != nullptr)
+        return fail(MBG_E_DTYPE_MISMATCH, "%s: scale given for a dtype without one", name);
+    return MBG_OK;
+}
+
+int check_config(const mbg_config* c) {
+    if (!c) return fail(MBG_E_INVALID_ARG, "config is NULL");
+    if (c->n_layers < 1 || c->hidden <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->vocab <= 0)
+        return fail(MBG_E_INVALID_ARG, "config: non-positive dimension");
+    if (c->hidden % 32 != 0) return fail(MBG_E_UNSUPPORTED, "config: hidden %d not a multiple of 32", c->hidden);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(MBG_E_UNSUPPORTED, "config: head_dim %d (64 or 128 supported)", c->head_dim);
+    if (c->n_q_heads % c->n_kv_heads != 0)
+        return fail(MBG_E_INVALID_ARG, "config: n_q_heads %d not a multiple of n_kv_heads %d", c->n_q_heads,
+                    c->n_kv_heads);
+    if (c->n_experts < 0 || c->top_k < 0 || c->n_shared < 0 || c->moe_ffn < 0 || c->ffn < 0)
+        return fail(MBG_E_INVALID_ARG, "config: negative size");
+    if (c->n_experts == 0) {
+        if (c->ffn <= 0 || c->ffn % 8 != 0)
+            return fail(MBG_E_UNSUPPORTED, "config: ffn %d must be a positive multiple of 8", c->ffn);
+    } else {
+        if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts)
+            return fail(MBG_E_UNSUPPORTED, "config: top_k %d (1..8, <= n_experts)", c->top_k);
+        if (c->moe_ffn <= 0 || c->moe_ffn % 32 != 0)
+            return fail(MBG_E_UNSUPPORTED, "config: moe_ffn %d must be a positive multiple of 32", c->moe_ffn);
+    }
+    if (c->page_size <= 0 || c->max_pos <= 0) return fail(MBG_E_INVALID_ARG, "config: page_size/max_pos");
+    if (c->k_max < 1 || c->k_max > 4) return fail(MBG_E_UNSUPPORTED, "config: k_max %d (1..4)", c->k_max);
+    if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(MBG_E_INVALID_ARG, "config: rope_theta/rms_eps");
+    return MBG_OK;
+}
+
+StepVariant variant_of(const mbg_config* c, int kv_dtype) {
+    StepVariant v;
+    v.hidden = c->hidden;
+    v.ffn = c->n_experts > 0 ? 0 : c->ffn;
+    v.qdim = c->n_q_heads * c->head_dim;
+    v.moe_ffn = c->n_experts > 0 ? c->moe_ffn : 0;
+    v.head_dim = c->head_dim;
+    v.group = c->n_q_heads / c->n_kv_heads;
+    v.kv_fmt = kv_dtype == MBG_FP8_E4M3 ? 2 : 1;
+    v.moe = c->n_experts > 0 ? 1 : 0;
+    return v;
+}
+
+int device_cus(int* cus) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    HIP_TRY(hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev));
+    return MBG_OK;
+}
+
+}  // namespace
+
+struct mbg_ctx {
+    mbg_config cfg;
+    StepArgs base;
+    hipStream_t stream;
+    int grid;
+    int lds[5];
+    const void* fn[5];
+    uint32_t epoch;
+    int64_t wall_khz;
+    int64_t timeout_us;
+    int64_t weight_bytes;
+    size_t ws_bytes;
+    int lm_dtype, kv_dtype;
+    int n_tasks;
+    int trace_on;
+    unsigned long long* trace_buf;
+    char variant[64];
+};
+
+extern "C" {
+
+const char* mbg_last_error(void) { return g_err.c_str(); }
+
+int mbg_workspace_size(const mbg_config* cfg, size_t* bytes) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!bytes) return fail(MBG_E_INVALID_ARG, "bytes is NULL");
+    *bytes = make_plan(*cfg).total;
+    return MBG_OK;
+}
+
+int mbg_validate(const mbg_config* c, const mbg_weights* w, const mbg_kv* kv) {
+    int rc = check_config(c);
+    if (rc) return rc;
+    const int64_t H = c->hidden, d = c->head_dim, Hq = c->n_q_heads, Hkv = c->n_kv_heads;
+    if (kv) {
+        if (kv->dtype != MBG_BF16 && kv->dtype != MBG_FP8_E4M3)
+            return fail(MBG_E_UNSUPPORTED, "kv: dtype %d (BF16 or FP8 E4M3)", kv->dtype);
+        if (!kv->pool || !kv->page_table) return fail(MBG_E_INVALID_ARG, "kv: pool/page_table is NULL");
+        if (kv->n_pages <= 0) return fail(MBG_E_INVALID_ARG, "kv: n_pages %d", kv->n_pages);
+        if (kv->dtype == MBG_FP8_E4M3 && !kv->scales)
+            return fail(MBG_E_DTYPE_MISMATCH, "kv: FP8 cache without per-head scales");
+        if (kv->dtype == MBG_BF16 && kv->scales)
+            return fail(MBG_E_DTYPE_MISMATCH, "kv: BF16 cache given scales");
+        if (!aligned16(kv->pool)) return fail(MBG_E_INVALID_ARG, "kv: pool not 16-byte aligned");
+        if (!step_variant_supported(variant_of(c, kv->dtype)))
+            return fail(MBG_E_UNSUPPORTED,
+                        "no compiled kernel for hidden %d, ffn %d, %d x %d query heads, %d per KV head, %s KV, %s",
+                        c->hidden, c->n_experts ? c->moe_ffn : c->ffn, c->n_q_heads, c->head_dim, (int)(Hq / Hkv),
+                        kv->dtype == MBG_BF16 ? "BF16" : "FP8", c->n_experts ? "MoE" : "dense");
+    }
+    if (!w) return MBG_OK;
+    if (!w->layers) return fail(MBG_E_INVALID_ARG, "weights: layers is NULL");
+    if ((rc = check_tensor(w->embed, "embed", MBG_BF16, 1, c->vocab, H))) return rc;
+    if ((rc = check_tensor(w->final_norm, "final_norm", MBG_BF16, 1, 1, H))) return rc;
+    if (w->lm_head.dtype != MBG_BF16 && w->lm_head.dtype != MBG_FP8_E4M3)
+        return fail(MBG_E_UNSUPPORTED, "lm_head: dtype %d (BF16 or FP8 E4M3)", w->lm_head.dtype);
+    if ((rc = check_tensor(w->lm_head, "lm_head", w->lm_head.dtype, 1, c->vocab, H))) return rc;
+    char nm[64];
+    for (int l = 0; l < c->n_layers; ++l) {
+        const mbg_layer& L = w->layers[l];
+#define CHK(field, dt, n, r, cc)                                   \
+    snprintf(nm, sizeof nm, "layers[%d]." #field, l);              \
+    if ((rc = check_tensor(L.field, nm, dt, n, r, cc))) return rc;
+        CHK(attn_norm, MBG_BF16, 1, 1, H)
+        CHK(ffn_norm, MBG_BF16, 1, 1, H)
+        CHK(wq, MBG_BF16, 1, Hq * d, H)
+        CHK(wk, MBG_BF16, 1, Hkv * d, H)
+        CHK(wv, MBG_BF16, 1, Hkv * d, H)
+        CHK(wo, MBG_BF16, 1, H, Hq * d)
+        if (c->n_experts == 0) {
+            CHK(w_gate, MBG_BF16, 1, c->ffn, H)
+            CHK(w_up, MBG_BF16, 1, c->ffn, H)
+            CHK(w_down, MBG_BF16, 1, H, c->ffn)
+        } else {
+            CHK(w_router, MBG_BF16, 1, c->n_experts, H)
+            CHK(exp_gate_up, MBG_MXFP4, c->n_experts, 2 * (int64_t)c->moe_ffn, H)
+            CHK(exp_down, MBG_MXFP4, c->n_experts, H, c->moe_ffn)
+            if (c->n_shared > 0) {
+                CHK(sh_gate_up, MBG_MXFP4, c->n_shared, 2 * (int64_t)c->moe_ffn, H)
+                CHK(sh_down, MBG_MXFP4, c->n_shared, H, c->moe_ffn)
+            }
+        }
+#undef CHK
+    }
+    return MBG_OK;
+}
+
+int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* kv, void* d_ws, size_t ws_bytes,
+                    void* stream, mbg_ctx** out) {
+    if (!out) return fail(MBG_E_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    if (!w || !kv) return fail(MBG_E_INVALID_ARG, "weights and kv are required");
+    int rc = mbg_validate(cfg, w, kv);
+    if (rc) return rc;
+    const mbg_config& c = *cfg;
+    if (c.n_experts > 0) return fail(MBG_E_UNSUPPORTED, "MoE layers are not compiled into this build");
+    const Plan plan = make_plan(c);
+    if (!d_ws || ws_bytes < plan.total)
+        return fail(MBG_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, plan.total);
+    if (((uintptr_t)d_ws & 255u) != 0) return fail(MBG_E_WORKSPACE, "workspace not 256-byte aligned");
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+
+    int cus = 0;
+    if ((rc = device_cus(&cus))) return rc;
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    int wall_khz = 0;
+    HIP_TRY(hipDeviceGetAttribute(&wall_khz, hipDeviceAttributeWallClockRate, dev));
+    int coop = 0;
+    HIP_TRY(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
+    if (!coop) return fail(MBG_E_UNSUPPORTED, "device does not support cooperative launches");
+
+    // page table entries must address the pool
+    const int n_lpages = (c.max_pos + c.page_size - 1) / c.page_size;
+    {
+        std::vector<int32_t> pt(n_lpages);
+        HIP_TRY(hipMemcpy(pt.data(), kv->page_table, sizeof(int32_t) * n_lpages, hipMemcpyDeviceToHost));
+        for (int i = 0; i < n_lpages; ++i)
+            if (pt[i] < 0 || pt[i] >= kv->n_pages)
+                return fail(MBG_E_RANGE, "page_table[%d] = %d outside [0, %d)", i, pt[i], kv->n_pages);
+    }
+
+    mbg_ctx* x = new mbg_ctx();
+    x->cfg = c;
+    x->stream = s;
+    x->epoch = 0;
+    x->wall_khz = wall_khz;
+    x->timeout_us = 2000000;
+    x->ws_bytes = ws_bytes;
+    x->lm_dtype = w->lm_head.dtype;
+    x->kv_dtype = kv->dtype;
+    const StepVariant v = variant_of(&c, kv->dtype);
+    snprintf(x->variant, sizeof x->variant, "step_d%d_g%d_%s_%s", v.head_dim, v.group,
+             v.kv_fmt == 1 ? "bf16kv" : "fp8kv", v.moe ? "moe" : "dense");
+
+    StepArgs& a = x->base;
+    memset(&a, 0, sizeof a);
+    a.n_layers = c.n_layers;
+    a.hidden = c.hidden;
+    a.n_q_heads = c.n_q_heads;
+    a.n_kv_heads = c.n_kv_heads;
+    a.head_dim = c.head_dim;
+    a.ffn = c.ffn;
+    a.vocab = c.vocab;
+    a.n_experts = c.n_experts;
+    a.top_k = c.top_k;
+    a.n_shared = c.n_shared;
+    a.moe_ffn = c.moe_ffn;
+    a.rms_eps = c.rms_eps;
+    a.attn_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+    a.page_size = c.page_size;
+    a.max_pos = c.max_pos;
+
+    // kernels, LDS, occupancy -> grid
+    int wg_per_cu = 1;
+    if (const char* e = getenv("MBG_WG_PER_CU")) wg_per_cu = atoi(e) > 0 ? atoi(e) : 1;
+    for (int k = 1; k <= c.k_max; ++k) {
+        x->fn[k] = step_kernel_for(v, k, &x->lds[k]);
+        if (!x->fn[k]) {
+            delete x;
+            return fail(MBG_E_UNSUPPORTED, "no kernel for %d columns", k);
+        }
+        hipError_t e = hipFuncSetAttribute(x->fn[k], hipFuncAttributeMaxDynamicSharedMemorySize, x->lds[k]);
+        if (e != hipSuccess) {
+            delete x;
+            return hip_fail(e, "hipFuncSetAttribute");
+        }
+        int nb = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, x->fn[k], kBlock, x->lds[k]);
+        if (e != hipSuccess) {
+            delete x;
+            return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+        }
+        if (nb < 1) {
+            delete x;
+            return fail(MBG_E_UNSUPPORTED, "step kernel (%d columns) cannot be resident", k);
+        }
+        if (nb < wg_per_cu) wg_per_cu = nb;
+    }
+    int G = cus * wg_per_cu;
+    if (G > kMaxGrid) G = kMaxGrid;
+    x->grid = G;
+
+    auto cdiv = [](int64_t n, int64_t d) { return (n + d - 1) / d; };
+    auto tiles_for = [&](int64_t units) { return (uint32_t)std::min<int64_t>(G, cdiv(units, 4)); };
+    const int HALF = c.head_dim / 2;
+    const int64_t npairs = (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * HALF;
+    a.tiles_qkv = tiles_for(npairs);
+    if (2 * cdiv(npairs, (int64_t)a.tiles_qkv * 4) > 64) {
+        delete x;
+        return fail(MBG_E_UNSUPPORTED, "%lld Q/K/V rows exceed the per-wavefront buffer", (long long)(2 * npairs));
+    }
+    a.tiles_o = tiles_for(c.hidden);
+    a.tiles_gu = tiles_for(c.ffn);
+    a.tiles_down = tiles_for(c.hidden);
+    a.tiles_lm = tiles_for(c.vocab);
+    int S = G / c.n_kv_heads;
+    S = std::max(1, std::min(S, kMaxSplits));
+    S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 32)));
+    a.attn_splits = S;
+    const uint32_t tiles_attn = (uint32_t)(c.n_kv_heads * S);
+
+    // task lists
+    std::vector<uint32_t> off(G + 1, 0);
+    std::vector<Task> tasks;
+    auto ci = [](int l, int ph) { return (uint32_t)(l * PH_COUNT + ph); };
+    for (int wg = 0; wg < G; ++wg) {
+        off[wg] = (uint32_t)tasks.size();
+        const uint32_t t = (uint32_t)wg;
+        for (int l = 0; l < c.n_layers; ++l) {
+            const uint32_t L8 = (uint32_t)l << 8;
+            if (t < a.tiles_qkv)
+                tasks.push_back(Task{OP_QKV | L8, t, l == 0 ? kNoWait : ci(l - 1, PH_DOWN), l == 0 ? 0u : a.tiles_down});
+            if (t < tiles_attn) tasks.push_back(Task{OP_ATTN | L8, t, ci(l, PH_QKV), a.tiles_qkv});
+            if (t < a.tiles_o) tasks.push_back(Task{OP_OPROJ | L8, t, ci(l, PH_ATTN), (uint32_t)c.n_kv_heads});
+            if (t < a.tiles_gu) tasks.push_back(Task{OP_GATEUP | L8, t, ci(l, PH_OPROJ), a.tiles_o});
+            if (t < a.tiles_down) tasks.push_back(Task{OP_DOWN | L8, t, ci(l, PH_GATEUP), a.tiles_gu});
+        }
+        if (t < a.tiles_lm)
+            tasks.push_back(Task{OP_LMHEAD, t, ci(c.n_layers - 1, PH_DOWN), a.tiles_down});
+    }
+    off[G] = (uint32_t)tasks.size();
+    if (tasks.size() > plan.max_tasks) {
+        delete x;
+        return fail(MBG_E_WORKSPACE, "task list %zu exceeds plan %zu", tasks.size(), plan.max_tasks);
+    }
+    x->n_tasks = (int)tasks.size();
+
+    std::vector<LayerPtrs> lp(c.n_layers);
+    int64_t per_step = 0;
+    for (int l = 0; l < c.n_layers; ++l) {
+        const mbg_layer& L = w->layers[l];
+        LayerPtrs& p = lp[l];
+        memset(&p, 0, sizeof p);
+        p.attn_norm = (const uint16_t*)L.attn_norm.data;
+        p.ffn_norm = (const uint16_t*)L.ffn_norm.data;
+        p.wq = (const uint16_t*)L.wq.data;
+        p.wk = (const uint16_t*)L.wk.data;
+        p.wv = (const uint16_t*)L.wv.data;
+        p.wo = (const uint16_t*)L.wo.data;
+        p.w_gate = (const uint16_t*)L.w_gate.data;
+        p.w_up = (const uint16_t*)L.w_up.data;
+        p.w_down = (const uint16_t*)L.w_down.data;
+        per_step += 2 * ((int64_t)c.hidden * 2 + (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim * c.hidden +
+                         (int64_t)c.hidden * c.n_q_heads * c.head_dim + 3 * (int64_t)c.ffn * c.hidden);
+    }
+    per_step += 2 * (int64_t)c.hidden * 2;  // embedding row + final norm
+    per_step += (int64_t)c.vocab * c.hidden * (x->lm_dtype == MBG_FP8_E4M3 ? 1 : 2) +
+                (x->lm_dtype == MBG_FP8_E4M3 ? 4 * (int64_t)c.vocab : 0);
+    x->weight_bytes = per_step;
+
+    std::vector<double> inv(HALF);
+    for (int i = 0; i < HALF; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
+
+    char* base = static_cast<char*>(d_ws);
+    a.status = (uint32_t*)(base + plan.status);
+    a.lm_ctr = a.status + 1;
+    a.amax_keys = (unsigned long long*)(base + plan.keys);
+    a.ctr = (uint32_t*)(base + plan.ctr);
+    a.head_ctr = (uint32_t*)(base + plan.head_ctr);
+    a.task_off = (const uint32_t*)(base + plan.task_off);
+    a.tasks = (const Task*)(base + plan.tasks);
+    a.layers = (const LayerPtrs*)(base + plan.layers);
+    a.inv_freq = (const double*)(base + plan.inv_freq);
+    a.xres = (float*)(base + plan.xres);
+    a.qbuf = (float*)(base + plan.qbuf);
+    a.part = (float*)(base + plan.part);
+    a.attn = (float*)(base + plan.attn);
+    a.hbuf = (float*)(base + plan.hbuf);
+    a.route_w = (float*)(base + plan.route_w);
+    a.route_idx = (int32_t*)(base + plan.route_idx);
+    x->trace_buf = (unsigned long long*)(base + plan.trace);
+    x->trace_on = 0;
+    a.trace = nullptr;
+    a.embed = (const uint16_t*)w->embed.data;
+    a.final_norm = (const uint16_t*)w->final_norm.data;
+    a.lm_head = w->lm_head.data;
+    a.lm_scale = (const float*)w->lm_head.scale;
+    a.lm_dtype = w->lm_head.dtype == MBG_FP8_E4M3 ? 2 : 1;
+    a.kv_dtype = kv->dtype == MBG_FP8_E4M3 ? 2 : 1;
+    a.kv_pool = kv->pool;
+    a.page_table = kv->page_table;
+    a.kv_scales = kv->scales;
+    a.kv_layer_stride = (int64_t)kv->n_pages * 2 * c.n_kv_heads * c.page_size * c.head_dim;
+
+    hipError_t e = launch_fill_u32((uint32_t*)base, plan.zero_bytes / 4, 0u, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(base + plan.task_off, off.data(), 4 * off.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(base + plan.tasks, tasks.data(), sizeof(Task) * tasks.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(base + plan.layers, lp.data(), sizeof(LayerPtrs) * lp.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipMemcpyAsync(base + plan.inv_freq, inv.data(), 8 * inv.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+        delete x;
+        return hip_fail(e, "workspace upload");
+    }
+    *out = x;
+    return MBG_OK;
+}
+
+static int launch_step(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t pos, float* d_logits,
+                       int32_t* d_argmax) {
+    if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
+    if (!d_tokens || !d_argmax) return fail(MBG_E_INVALID_ARG, "tokens/argmax is NULL");
+    if (k < 1 || k > x->cfg.k_max) return fail(MBG_E_RANGE, "k %d outside [1, %d]", k, x->cfg.k_max);
+    if (pos < 0 || (int64_t)pos + k > x->cfg.max_pos)
+        return fail(MBG_E_RANGE, "positions %d..%d outside [0, %d)", pos, pos + k - 1, x->cfg.max_pos);
+    StepArgs a = x->base;
+    a.tokens = d_tokens;
+    a.logits = d_logits;
+    a.argmax = d_argmax;
+    a.pos = pos;
+    a.ncol = k;
+    a.epoch = ++x->epoch;
+    a.deadline_ticks = (uint64_t)x->timeout_us * (uint64_t)x->wall_khz / 1000ull;
+    void* args[] = {&a};
+    hipError_t e = hipLaunchCooperativeKernel(x->fn[k], dim3(x->grid), dim3(kBlock), args, (unsigned)x->lds[k],
+                                              x->stream);
+    if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel");
+    return MBG_OK;
+}
+
+int mbg_decode_step(mbg_ctx* x, const int32_t* d_token, int32_t pos, float* d_logits, int32_t* d_argmax) {
+    return launch_step(x, d_token, 1, pos, d_logits, d_argmax);
+}
+
+int mbg_decode_verify(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t pos, float* d_logits,
+                      int32_t* d_argmax) {
+    return launch_step(x, d_tokens, k, pos, d_logits, d_argmax);
+}
+
+int mbg_get_status(mbg_ctx* x) {
+    if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
+    HIP_TRY(hipStreamSynchronize(x->stream));
+    uint32_t st = 0;
+    HIP_TRY(hipMemcpy(&st, x->base.status, 4, hipMemcpyDeviceToHost));
+    if (st != 0) {
+        HIP_TRY(launch_fill_u32(x->base.status, 1, 0u, x->stream));
+        HIP_TRY(hipStreamSynchronize(x->stream));
+        if (st == kStatusTimeout) return fail(MBG_E_TIMEOUT, "a device wait exceeded its deadline");
+        if (st == kStatusRange) return fail(MBG_E_RANGE, "a token id was outside [0, vocab)");
+        return fail(MBG_E_HIP, "device status %u", st);
+    }
+    return MBG_OK;
+}
+
+int mbg_query(const mbg_ctx* x, mbg_info* info) {
+    if (!x || !info) return fail(MBG_E_INVALID_ARG, "ctx/info is NULL");
+    memset(info, 0, sizeof *info);
+    info->grid = x->grid;
+    info->block = kBlock;
+    info->n_tasks = x->n_tasks;
+    info->launches_per_step = 1;
+    info->lm_dtype = x->lm_dtype;
+    info->kv_dtype = x->kv_dtype;
+    info->expert_dtype = x->cfg.n_experts ? MBG_MXFP4 : 0;
+    info->attn_dtype = MBG_BF16;
+    info->attn_splits = x->base.attn_splits;
+    info->trace = x->trace_on;
+    info->clock_khz = x->wall_khz;
+    info->weight_bytes_per_step = x->weight_bytes;
+    info->workspace_bytes = (int64_t)x->ws_bytes;
+    snprintf(info->variant, sizeof info->variant, "%s", x->variant);
+    return MBG_OK;
+}
+
+int mbg_set_timeout_us(mbg_ctx* x, int64_t us) {
+    if (!x || us <= 0) return fail(MBG_E_INVALID_ARG, "ctx is NULL or timeout <= 0");
+    x->timeout_us = us;
+    return MBG_OK;
+}
+
+int mbg_set_trace(mbg_ctx* x, int on) {
+    if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
+    x->trace_on = on ? 1 : 0;
+    x->base.trace = on ? x->trace_buf : nullptr;
+    return MBG_OK;
+}
+
+int mbg_read_trace(mbg_ctx* x, uint64_t* host, size_t max_records, size_t* n_out) {
+    if (!x || !host || !n_out) return fail(MBG_E_INVALID_ARG, "NULL pointer");
+    if (!x->trace_on) return fail(MBG_E_INVALID_ARG, "tracing is off");
+    const size_t n = std::min<size_t>(max_records, (size_t)x->n_tasks);
+    HIP_TRY(hipStreamSynchronize(x->stream));
+    HIP_TRY(hipMemcpy(host, x->trace_buf, 64 * n, hipMemcpyDeviceToHost));
+    *n_out = n;
+    return MBG_OK;
+}
+
+void mbg_destroy(mbg_ctx* x) { delete x; }
+
+// ------------------------------------------------------- standalone ops
+
+int mbg_lm_head_workspace_size(int32_t k, size_t* bytes) {
+    if (k < 1 || k > 4) return fail(MBG_E_RANGE, "k %d outside [1, 4]", k);
+    if (!bytes) return fail(MBG_E_INVALID_ARG, "bytes is NULL");
+    *bytes = 256;
+    return MBG_OK;
+}
+
+int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logits, int32_t* d_argmax,
+                void* d_ws, size_t ws_bytes, void* stream) {
+    if (!w || !d_x || !d_argmax) return fail(MBG_E_INVALID_ARG, "w/x/argmax is NULL");
+    if (k < 1 || k > 4) return fail(MBG_E_RANGE, "k %d outside [1, 4]", k);
+    if (w->dtype != MBG_BF16 && w->dtype != MBG_FP8_E4M3)
+        return fail(MBG_E_UNSUPPORTED, "lm head dtype %d (BF16 or FP8 E4M3)", w->dtype);
+    int rc = check_tensor(*w, "lm_head", w->dtype, 1, w->rows, w->cols);
+    if (rc) return rc;
+    if (w->rows <= 0 || w->rows > 0x7FFFFFFF || w->cols <= 0 || w->cols % 16 != 0)
+        return fail(MBG_E_UNSUPPORTED, "lm head shape [%lld][%lld]: cols must be a positive multiple of 16",
+                    (long long)w->rows, (long long)w->cols);
+    if (!lm_head_hidden_supported((int)w->cols))
+        return fail(MBG_E_UNSUPPORTED, "lm head hidden size %lld not compiled in", (long long)w->cols);
+    if ((size_t)k * w->cols * 4 + 256 > 160 * 1024)
+        return fail(MBG_E_UNSUPPORTED, "k * cols too large for on-chip activations");
+    if (!d_ws || ws_bytes < 256) return fail(MBG_E_WORKSPACE, "workspace %zu bytes, need 256", ws_bytes);
+    static int cus = 0;
+    if (cus == 0 && (rc = device_cus(&cus))) return rc;
+    LmHeadArgs a;
+    a.w = w->data;
+    a.wscale = (const float*)w->scale;
+    a.x = d_x;
+    a.logits = d_logits;
+    a.argmax = d_argmax;
+    a.keys = (unsigned long long*)d_ws;
+    a.counter = (uint32_t*)((char*)d_ws + 64);
+    a.V = (int32_t)w->rows;
+    a.H = (int32_t)w->cols;
+    int64_t grid = std::min<int64_t>((a.V + 3) / 4, 2 * (int64_t)cus);
+    hipError_t e = launch_lm_head(a, k, w->dtype == MBG_FP8_E4M3 ? 2 : 1, (int)grid, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "lm_head launch");
+    return MBG_OK;
+}
+
+int mbg_quantize_fp8_rows(const uint16_t* d_w, int64_t rows, int64_t cols, uint8_t* d_codes, float* d_scales,
+                          void* stream) {
+    if (!d_w || !d_codes || !d_scales) return fail(MBG_E_INVALID_ARG, "NULL pointer");
+    if (rows <= 0 || cols <= 0 || rows > 0x7FFFFFFF || cols % 16 != 0)
+        return fail(MBG_E_INVALID_ARG, "shape [%lld][%lld]: cols must be a positive multiple of 16",
+                    (long long)rows, (long long)cols);
+    hipError_t e = launch_quantize_fp8_rows(d_w, rows, cols, d_codes, d_scales, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "quantize launch");
+    return MBG_OK;
+}
+
+int mbg_kv_write(const mbg_config* cfg, const mbg_kv* kv, int32_t layer, int32_t pos0, int32_t n, const float* d_k,
+                 const float* d_v, void* stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!kv || !kv->pool || !kv->page_table || !d_k || !d_v) return fail(MBG_E_INVALID_ARG, "NULL pointer");
+    if (kv->dtype != MBG_BF16 && kv->dtype != MBG_FP8_E4M3) return fail(MBG_E_UNSUPPORTED, "kv dtype %d", kv->dtype);
+    if (kv->dtype == MBG_FP8_E4M3 && !kv->scales) return fail(MBG_E_DTYPE_MISMATCH, "FP8 cache without scales");
+    if (layer < 0 || layer >= cfg->n_layers) return fail(MBG_E_RANGE, "layer %d", layer);
+    if (n < 0 || pos0 < 0 || (int64_t)pos0 + n > cfg->max_pos)
+        return fail(MBG_E_RANGE, "positions %d..%d outside [0, %d)", pos0, pos0 + n - 1, cfg->max_pos);
+    if (n == 0) return MBG_OK;
+    {
+        const int lp0 = pos0 / cfg->page_size, lp1 = (pos0 + n - 1) / cfg->page_size;
+        std::vector<int32_t> pt(lp1 - lp0 + 1);
+        HIP_TRY(hipMemcpy(pt.data(), kv->page_table + lp0, 4 * pt.size(), hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < pt.size(); ++i)
+            if (pt[i] < 0 || pt[i] >= kv->n_pages)
+                return fail(MBG_E_RANGE, "page_table[%zu] = %d outside [0, %d)", lp0 + i, pt[i], kv->n_pages);
+    }
+    KvWriteArgs a;
+    a.pool = kv->pool;
+    a.page_table = kv->page_table;
+    a.scales = kv->scales;
+    a.k = d_k;
+    a.v = d_v;
+    a.layer_off = (int64_t)layer * kv->n_pages * 2 * cfg->n_kv_heads * cfg->page_size * cfg->head_dim;
+    a.dtype = kv->dtype == MBG_FP8_E4M3 ? 2 : 1;
+    a.layer = layer;
+    a.pos0 = pos0;
+    a.n = n;
+    a.n_kv_heads = cfg->n_kv_heads;
+    a.head_dim = cfg->head_dim;
+    a.page_size = cfg->page_size;
+    hipError_t e = launch_kv_write(a, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kv_write launch");
+    return MBG_OK;
+}
+
+}  // extern "C"

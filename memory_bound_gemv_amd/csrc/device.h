@@ -1,0 +1,160 @@
+// Device helpers for the gfx950 decode kernels: number-format decoding and
+// encoding, wavefront reductions, dependency counters and the wait watchdog.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mbg {
+
+constexpr int kWave = 64;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal: data read once per step).
+__device__ __forceinline__ uint4 ld_stream(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ------------------------------------------------------------------ BF16
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// binary32 -> BF16, nearest with ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// ------------------------------------------------------------- FP8 E4M3FN
+
+// Two E4M3FN codes (bytes 0,1 or 2,3 of w) to binary32 with the gfx950
+// conversion unit (OCP format on this target).
+__device__ __forceinline__ void fp8x4_to_f32(uint32_t w, float* o) {
+    auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+    auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true);
+    o[0] = a[0];
+    o[1] = a[1];
+    o[2] = b[0];
+    o[3] = b[1];
+}
+
+// binary32 -> E4M3FN, nearest with ties to even, saturating at +-448;
+// NaN -> 0x7F with the sign.  Integer rounding of the binary32 fields:
+// below 2^-6 the value is a multiple of 2^-9 (subnormal grid), above it the
+// 23-bit mantissa is rounded to 3 bits with carry into the exponent.
+__device__ __forceinline__ uint8_t f32_to_fp8e4m3(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const uint32_t a = u & 0x7FFFFFFFu;
+    if (a > 0x7F800000u) return (uint8_t)(sign | 0x7Fu);
+    if (a >= 0x43E00000u) return (uint8_t)(sign | 0x7Eu);         // >= 448 (and inf)
+    if (a < 0x3C800000u) {                                          // < 2^-6
+        const float q = __builtin_rintf(__uint_as_float(a) * 512.0f);  // exact scaling
+        return (uint8_t)(sign | (uint32_t)q);                       // 0..8 (8 = 2^-6)
+    }
+    int e = (int)(a >> 23) - 127;                                   // -6 .. 8
+    uint32_t m = (a >> 20) & 7u;
+    const uint32_t rem = a & 0xFFFFFu;
+    if (rem > 0x80000u || (rem == 0x80000u && (m & 1u))) ++m;
+    if (m == 8u) { m = 0u; ++e; }
+    if (e > 8 || (e == 8 && m > 6u)) { e = 8; m = 6u; }
+    return (uint8_t)(sign | ((uint32_t)(e + 7) << 3) | m);
+}
+
+// ------------------------------------------------------------------ MXFP4
+
+// E8M0 byte -> binary32 2^(e-127) (e = 0 gives the subnormal 2^-127,
+// e = 255 NaN).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+    if (e == 255u) return __uint_as_float(0x7FC00000u);
+    return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+}
+
+// Eight E2M1 codes of one 32-bit word (element 2i in the low nibble of byte
+// i) times `scale`, with the gfx950 scaled FP4 conversion.
+__device__ __forceinline__ void fp4x8_to_f32(uint32_t w, float scale, float* o) {
+    auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 0);
+    auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 1);
+    auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 2);
+    auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, scale, 3);
+    o[0] = p0[0]; o[1] = p0[1]; o[2] = p1[0]; o[3] = p1[1];
+    o[4] = p2[0]; o[5] = p2[1]; o[6] = p3[0]; o[7] = p3[1];
+}
+
+// ------------------------------------------------------------ reductions
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum within aligned groups of 4, 8 or 16 lanes; every lane of a group gets
+// the same, order-fixed result (each step adds a lane and its partner, and
+// a + b == b + a exactly).
+__device__ __forceinline__ float group4_sum(float v) {
+    v += dpp_f<0xB1>(v);  // quad_perm [1,0,3,2]
+    v += dpp_f<0x4E>(v);  // quad_perm [2,3,0,1]
+    return v;
+}
+__device__ __forceinline__ float group8_sum(float v) {
+    v = group4_sum(v);
+    v += dpp_f<0x141>(v);  // row_half_mirror: lane i <-> 7-i
+    return v;
+}
+__device__ __forceinline__ float group16_sum(float v) {
+    v = group8_sum(v);
+    v += dpp_f<0x140>(v);  // row_mirror: lane i <-> 15-i
+    return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 4 || N == 8 || N == 16, "group size");
+    if constexpr (N == 4) return group4_sum(v);
+    else if constexpr (N == 8) return group8_sum(v);
+    else return group16_sum(v);
+}
+
+// Whole-wavefront sum, identical in every lane.
+__device__ __forceinline__ float wave_sum(float v) {
+    v = group16_sum(v);
+    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+// ------------------------------------------------- counters and watchdog
+
+__device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fetch_add_release(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t fetch_add_acq_rel(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_acquire() {
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+}
+__device__ __forceinline__ void fence_release() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+}
+
+// Record the first error of a launch (later ones keep the first).
+__device__ __forceinline__ void latch_error(uint32_t* status, uint32_t code) {
+    uint32_t zero = 0;
+    __hip_atomic_compare_exchange_strong(status, &zero, code, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace mbg

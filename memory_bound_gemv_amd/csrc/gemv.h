@@ -1,0 +1,207 @@
+// Batch-1 (and k <= 4 column) GEMV core for gfx950.
+//
+// At batch 1 a decode step is a chain of matrix-vector products whose cost is
+// the bytes of weight they stream (Kog article "Real-time LLM inference on
+// standard GPUs: 3k tokens/s per request", section on memory bandwidth as the
+// bottleneck: about 1 FLOP per byte for FP16, 2 for FP8, 4 for FP4).  So the
+// core is built around the load stream, not around matrix units:
+//   * a wavefront owns whole rows; a row is NV 16-byte vectors and lane l
+//     reads vectors l, l + 64, ... (1 KiB per wave instruction, coalesced);
+//     NV is a compile-time constant, so the loads of a row are one scalar
+//     base plus immediate offsets;
+//   * rows are streamed in chunks of RPC rows; two chunk buffers live in
+//     registers and chunk c + 1 is issued before chunk c is multiplied; the
+//     first chunk is issued before the workgroup waits for its input vector
+//     (weights do not depend on it);
+//   * the activation columns sit in LDS as binary32; a lane reads its slice
+//     once per chunk and uses it for all RPC rows and, in a verify window,
+//     each weight vector for all k columns (each weight byte read once);
+//   * products accumulate in binary32 in a fixed order and a row's lane
+//     sums are combined by an order-fixed DPP/swizzle tree, so results are
+//     bitwise reproducible and independent of scheduling.
+#pragma once
+
+#include "device.h"
+
+#define MBG_GLOBAL __attribute__((address_space(1)))
+#define MBG_LDS __attribute__((address_space(3)))
+#define MBG_CONST __attribute__((address_space(4)))
+
+namespace mbg {
+
+enum : int { F_BF16 = 1, F_FP8 = 2, F_MXFP4 = 3 };
+
+template <int F>
+struct FmtInfo;
+template <>
+struct FmtInfo<F_BF16> { static constexpr int kEPV = 8; };
+template <>
+struct FmtInfo<F_FP8> { static constexpr int kEPV = 16; };
+template <>
+struct FmtInfo<F_MXFP4> { static constexpr int kEPV = 32; };
+
+template <class T>
+__device__ __forceinline__ MBG_GLOBAL T* gp(T* p) {
+    return (MBG_GLOBAL T*)p;
+}
+template <class T>
+__device__ __forceinline__ const MBG_GLOBAL T* gp(const T* p) {
+    return (const MBG_GLOBAL T*)p;
+}
+
+typedef MBG_LDS float lds_f32;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream_g(const MBG_GLOBAL uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const MBG_GLOBAL u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16-byte load through the cache hierarchy (data written earlier in the step).
+__device__ __forceinline__ uint4 ld_g(const MBG_GLOBAL uint4* p) {
+    const u32x4 v = *reinterpret_cast<const MBG_GLOBAL u32x4*>(p);
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Address of one weight row (scalar): 16-byte vectors plus, for MXFP4, one
+// E8M0 byte per vector.
+struct GRow {
+    const MBG_GLOBAL uint4* data;
+    const MBG_GLOBAL uint8_t* scale;
+};
+
+template <int F>
+__device__ __forceinline__ void decode16(const uint4 w, uint32_t sbyte, float* wf) {
+    if constexpr (F == F_BF16) {
+        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            wf[2 * q] = bf16_lo(ws[q]);
+            wf[2 * q + 1] = bf16_hi(ws[q]);
+        }
+    } else if constexpr (F == F_FP8) {
+        fp8x4_to_f32(w.x, wf + 0);
+        fp8x4_to_f32(w.y, wf + 4);
+        fp8x4_to_f32(w.z, wf + 8);
+        fp8x4_to_f32(w.w, wf + 12);
+    } else {
+        const float sc = e8m0_to_f32(sbyte);
+        fp4x8_to_f32(w.x, sc, wf + 0);
+        fp4x8_to_f32(w.y, sc, wf + 8);
+        fp4x8_to_f32(w.z, sc, wf + 16);
+        fp4x8_to_f32(w.w, sc, wf + 24);
+    }
+}
+
+// Rows per chunk: keep the two chunk buffers near 128 VGPRs.
+template <int F, int NC, int NV>
+struct ChunkRows {
+    static constexpr int NJ = (NV + kWave - 1) / kWave;
+    static constexpr int budget = (F == F_MXFP4) ? (NC <= 2 ? 8 : 4) : (NC <= 2 ? 16 : 8);
+    static constexpr int value = budget / NJ > 0 ? budget / NJ : 1;
+};
+
+// One wavefront streams `nrows` rows (its own numbering; `row(rr)` gives the
+// address) of NV vectors each against NC activation columns in LDS
+// (xs[c * ldx + k]).  out(rr, sums) is called by every lane with the
+// wave-uniform row results.
+template <int F, int NC, int NV, int RPC = ChunkRows<F, NC, NV>::value>
+struct RowStream {
+    static constexpr int NJ = (NV + kWave - 1) / kWave;
+    static constexpr int LASTN = NV - kWave * (NJ - 1);  // lanes active in the last vector column
+    static constexpr bool PART = LASTN != kWave;
+    static constexpr int E = FmtInfo<F>::kEPV;
+
+    struct Buf {
+        uint4 w[RPC][NJ];
+        uint32_t s[RPC][NJ];
+    };
+
+    int nrows, lane;
+
+    __device__ __forceinline__ RowStream(int nrows_, int lane_) : nrows(nrows_), lane(lane_) {}
+
+    __device__ __forceinline__ static bool active(int j, int lane) { return !PART || j < NJ - 1 || lane < LASTN; }
+
+    template <class RowFn>
+    __device__ __forceinline__ void issue(Buf& b, int c, RowFn& row) const {
+#pragma unroll
+        for (int r = 0; r < RPC; ++r) {
+            const int rr = c * RPC + r;
+            if (rr < nrows) {
+                const GRow g = row(rr);
+#pragma unroll
+                for (int j = 0; j < NJ; ++j) {
+                    if (active(j, lane)) {
+                        b.w[r][j] = ld_stream_g(g.data + lane + kWave * j);
+                        if constexpr (F == F_MXFP4) b.s[r][j] = g.scale[lane + kWave * j];
+                    }
+                }
+            }
+        }
+    }
+
+    template <class OutFn>
+    __device__ __forceinline__ void compute(const Buf& b, int c, const lds_f32* xs, int ldx, OutFn& out) const {
+        float acc[RPC][NC][2];
+#pragma unroll
+        for (int r = 0; r < RPC; ++r)
+#pragma unroll
+            for (int q = 0; q < NC; ++q) acc[r][q][0] = acc[r][q][1] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            if (!active(j, lane)) continue;
+            const int k = (lane + kWave * j) * E;
+            float xv[NC][E];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+#pragma unroll
+                for (int e = 0; e < E; e += 4) {
+                    const f32x4 t = *reinterpret_cast<const MBG_LDS f32x4*>(xs + q * ldx + k + e);
+                    xv[q][e] = t[0];
+                    xv[q][e + 1] = t[1];
+                    xv[q][e + 2] = t[2];
+                    xv[q][e + 3] = t[3];
+                }
+            }
+#pragma unroll
+            for (int r = 0; r < RPC; ++r) {
+                if (c * RPC + r >= nrows) continue;
+                float wf[E];
+                decode16<F>(b.w[r][j], b.s[r][j], wf);
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+#pragma unroll
+                    for (int e = 0; e < E; e += 2) {
+                        acc[r][q][0] = fmaf(wf[e], xv[q][e], acc[r][q][0]);
+                        acc[r][q][1] = fmaf(wf[e + 1], xv[q][e + 1], acc[r][q][1]);
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < RPC; ++r) {
+            const int rr = c * RPC + r;
+            if (rr >= nrows) continue;
+            float sums[NC];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) sums[q] = wave_sum(acc[r][q][0] + acc[r][q][1]);
+            out(rr, sums);
+        }
+    }
+
+    // `a` holds chunk 0, already issued.
+    template <class RowFn, class OutFn>
+    __device__ __forceinline__ void run(Buf& a, Buf& b, RowFn& row, const lds_f32* xs, int ldx, OutFn& out) const {
+        const int nch = (nrows + RPC - 1) / RPC;
+        for (int c = 0; c < nch; c += 2) {
+            if (c + 1 < nch) issue(b, c + 1, row);
+            compute(a, c, xs, ldx, out);
+            if (c + 1 >= nch) break;
+            if (c + 2 < nch) issue(a, c + 2, row);
+            compute(b, c + 1, xs, ldx, out);
+        }
+    }
+};
+
+}  // namespace mbg

@@ -1,0 +1,122 @@
+// Structures shared by the host runtime and the persistent decode kernel:
+// the task encoding, per-layer weight pointers and the kernel argument block.
+#pragma once
+
+#include <stdint.h>
+
+namespace mbg {
+
+// Operations of the per-step task list.  One task is one tile of one op of
+// one layer; a workgroup runs its tasks in list order, each after waiting
+// for the counter of the phase it reads.
+enum Op : uint32_t {
+    OP_QKV = 1,    // RMSNorm(x) -> rows of Wq/Wk/Wv -> RoPE -> q to workspace, k/v to cache
+    OP_ATTN = 2,   // one (KV head, split) of single-query attention; last split combines
+    OP_OPROJ = 3,  // rows of Wo . attn, residual add
+    OP_GATEUP = 4, // RMSNorm(x) -> rows of Wgate/Wup -> silu(g) * u
+    OP_DOWN = 5,   // rows of Wdown . h, residual add
+    OP_LMHEAD = 6, // final RMSNorm -> rows of the LM head -> logits, argmax
+    OP_ROUTER = 7, // MoE: RMSNorm(x) -> router logits (whole row set per task)
+    OP_EXPGU = 8,  // MoE: rows of a selected expert's gate/up
+    OP_EXPDOWN = 9 // MoE: rows of the experts' down, weighted sum, residual add
+};
+
+// Phases: the dependency counters of one layer.
+enum Phase : uint32_t {
+    PH_QKV = 0,
+    PH_ATTN = 1,  // counts finished combines (one per KV head)
+    PH_OPROJ = 2,
+    PH_GATEUP = 3,
+    PH_DOWN = 4,
+    PH_ROUTER = 5,
+    PH_COUNT = 6
+};
+
+// 16-byte task record.
+struct Task {
+    uint32_t op_layer;  // op | layer << 8
+    uint32_t tile;      // tile index within the op
+    uint32_t wait_ctr;  // counter to wait on, or kNoWait
+    uint32_t wait_need; // per-step count that counter reaches when the producer phase is done
+};
+constexpr uint32_t kNoWait = 0xFFFFFFFFu;
+
+struct LayerPtrs {
+    const uint16_t* attn_norm;
+    const uint16_t* ffn_norm;
+    const uint16_t* wq;
+    const uint16_t* wk;
+    const uint16_t* wv;
+    const uint16_t* wo;
+    const uint16_t* w_gate;
+    const uint16_t* w_up;
+    const uint16_t* w_down;
+    const uint16_t* w_router;
+    const uint8_t* eg_codes;   // experts gate/up MXFP4 codes [E][2M][H/2]
+    const uint8_t* eg_scales;  // [E][2M][H/32]
+    const uint8_t* ed_codes;   // experts down [E][H][M/2]
+    const uint8_t* ed_scales;  // [E][H][M/32]
+    const uint8_t* sg_codes;   // shared experts gate/up [S][2M][H/2]
+    const uint8_t* sg_scales;
+    const uint8_t* sd_codes;   // shared experts down [S][H][M/2]
+    const uint8_t* sd_scales;
+};
+
+// Everything the persistent kernel reads, by value.
+struct StepArgs {
+    // model shape
+    int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab;
+    int32_t n_experts, top_k, n_shared, moe_ffn;
+    float rms_eps;
+    float attn_scale_log2;  // log2(e) / sqrt(head_dim)
+    int32_t page_size, max_pos;
+    // tiling: tasks (workgroups) per phase; each wavefront of a phase owns
+    // the output rows u = wave_id + n_waves * i of that phase
+    uint32_t tiles_qkv, tiles_o, tiles_gu, tiles_down, tiles_lm;
+    uint32_t tiles_router, tiles_egu, tiles_edown;
+    int32_t attn_splits;
+    // weights
+    const LayerPtrs* layers;
+    const uint16_t* embed;
+    const uint16_t* final_norm;
+    const void* lm_head;
+    const float* lm_scale;
+    int32_t lm_dtype;
+    // KV cache
+    int32_t kv_dtype;
+    void* kv_pool;
+    const int32_t* page_table;
+    const float* kv_scales;
+    int64_t kv_layer_stride;  // elements per layer = n_pages * 2 * Hkv * page * d
+    // workspace
+    const Task* tasks;
+    const uint32_t* task_off;  // [grid + 1]
+    uint32_t* ctr;             // [n_layers * PH_COUNT + extra]
+    uint32_t* head_ctr;        // [n_layers * n_kv_heads] split arrivals
+    uint32_t* lm_ctr;          // LM-head tiles finished
+    uint32_t* status;          // first device error
+    float* xres;               // [k][H] residual stream
+    float* qbuf;               // [k][Hq][d]
+    float* part;               // [k][Hq][splits][d + 2] attention partials
+    float* attn;               // [k][Hq * d]
+    float* hbuf;               // [k][F] or MoE [k][slots][M]
+    float* route_w;            // [k][top_k] routing weights (MoE)
+    int32_t* route_idx;        // [k][top_k]
+    unsigned long long* amax_keys;  // [k]
+    const double* inv_freq;    // [d/2] theta^(-2i/d)
+    unsigned long long* trace; // optional stamps
+    // per call
+    const int32_t* tokens;
+    float* logits;
+    int32_t* argmax;
+    int32_t pos;
+    int32_t ncol;
+    uint32_t epoch;
+    uint64_t deadline_ticks;   // s_memrealtime ticks a wait may take
+};
+
+// Device status codes (positive on the device, negated at the boundary).
+constexpr uint32_t kStatusTimeout = 7;
+constexpr uint32_t kStatusRange = 4;
+
+}  // namespace mbg

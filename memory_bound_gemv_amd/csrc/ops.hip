@@ -1,0 +1,221 @@
+// Standalone kernels: LM-head GEMV fused with argmax, online FP8 row
+// quantisation, and the quantising K/V write into the paged cache.
+#include <hip/hip_runtime.h>
+
+#include "gemv.h"
+#include "ops.h"
+
+namespace mbg {
+
+// ---------------------------------------------------------------- argmax
+
+// Order-preserving map of a binary32 onto uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t ordered_f32(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+// Packed argmax key: value first, then the lower row index wins ties.
+__device__ __forceinline__ unsigned long long argmax_key(float f, uint32_t row) {
+    return ((unsigned long long)ordered_f32(f) << 32) | (unsigned long long)(0xFFFFFFFFu - row);
+}
+
+// ------------------------------------------------------------- LM head
+
+// Every wavefront of the grid owns rows gw, gw + n_waves, ... of the head
+// and streams them back to back; one argmax key per workgroup is merged with
+// a 64-bit atomic max, and the last workgroup turns the keys into indices.
+template <int F, int NC, int H>
+__global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
+    extern __shared__ __align__(16) float smem_raw[];
+    lds_f32* xs = (lds_f32*)smem_raw;                  // [NC][H]
+    __shared__ unsigned long long wbest[4 * 4];
+    __shared__ uint32_t last;
+    constexpr int E = FmtInfo<F>::kEPV;
+    constexpr int NV = H / E;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int nw = gridDim.x * 4;
+    const int gw = blockIdx.x * 4 + wave;
+    const int nrows = gw < a.V ? (a.V - 1 - gw) / nw + 1 : 0;
+    const MBG_GLOBAL uint4* W = gp(reinterpret_cast<const uint4*>(a.w));
+    auto rowf = [&](int rr) -> GRow { return GRow{W + ((size_t)gw + (size_t)nw * rr) * NV, nullptr}; };
+    using RS = RowStream<F, NC, NV>;
+    RS st(nrows, lane);
+    typename RS::Buf A, B;
+    st.issue(A, 0, rowf);  // weights do not depend on x: start streaming first
+
+    const MBG_GLOBAL float* x = gp(a.x);
+    for (int i = threadIdx.x; i < NC * H; i += blockDim.x) xs[i] = x[i];
+    __syncthreads();
+
+    unsigned long long best[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) best[c] = 0ull;
+    MBG_GLOBAL float* logits = a.logits ? gp(a.logits) : nullptr;
+    const MBG_GLOBAL float* wsc = gp(a.wscale);
+    auto out = [&](int rr, const float (&s)[NC]) {
+        const uint32_t r = (uint32_t)(gw + nw * rr);
+        const float sc = (F == F_FP8) ? wsc[r] : 1.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float v = s[c] * sc;
+            if (logits != nullptr && lane == c) logits[(size_t)c * a.V + r] = v;
+            const unsigned long long k = argmax_key(v, r);
+            best[c] = k > best[c] ? k : best[c];
+        }
+    };
+    st.run(A, B, rowf, xs, H, out);
+
+    if (lane == 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) wbest[wave * 4 + c] = best[c];
+    }
+    __syncthreads();
+    MBG_GLOBAL unsigned long long* keys = gp(a.keys);
+    if (threadIdx.x < NC) {
+        const int c = threadIdx.x;
+        unsigned long long b = wbest[c];
+        for (int w = 1; w < 4; ++w) b = wbest[w * 4 + c] > b ? wbest[w * 4 + c] : b;
+        __hip_atomic_fetch_max(keys + c, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        fence_release();
+        const uint32_t old = __hip_atomic_fetch_add(gp(a.counter), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = (old + 1u == gridDim.x);
+        if (last) fence_acquire();
+    }
+    __syncthreads();
+    if (last && threadIdx.x < NC) {
+        const unsigned long long k = __hip_atomic_load(keys + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gp(a.argmax)[threadIdx.x] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        __hip_atomic_store(keys + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (threadIdx.x == 0) __hip_atomic_store(gp(a.counter), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <int F, int NC, int H>
+static hipError_t launch_lm_head_h(const LmHeadArgs& a, int grid, hipStream_t s) {
+    const size_t shm = (size_t)NC * H * sizeof(float);
+    hipLaunchKernelGGL((lm_head_kernel<F, NC, H>), dim3(grid), dim3(256), shm, s, a);
+    return hipGetLastError();
+}
+
+template <int F, int NC>
+static hipError_t launch_lm_head_nc(const LmHeadArgs& a, int grid, hipStream_t s) {
+    switch (a.H) {
+        case 256: return launch_lm_head_h<F, NC, 256>(a, grid, s);
+        case 512: return launch_lm_head_h<F, NC, 512>(a, grid, s);
+        case 1024: return launch_lm_head_h<F, NC, 1024>(a, grid, s);
+        case 2048: return launch_lm_head_h<F, NC, 2048>(a, grid, s);
+        case 2560: return launch_lm_head_h<F, NC, 2560>(a, grid, s);
+        case 4096: return launch_lm_head_h<F, NC, 4096>(a, grid, s);
+        case 8192: return launch_lm_head_h<F, NC, 8192>(a, grid, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+bool lm_head_hidden_supported(int H) {
+    return H == 256 || H == 512 || H == 1024 || H == 2048 || H == 2560 || H == 4096 || H == 8192;
+}
+
+hipError_t launch_lm_head(const LmHeadArgs& a, int ncol, int fmt, int grid, hipStream_t s) {
+    if (fmt == F_BF16) {
+        switch (ncol) {
+            case 1: return launch_lm_head_nc<F_BF16, 1>(a, grid, s);
+            case 2: return launch_lm_head_nc<F_BF16, 2>(a, grid, s);
+            case 3: return launch_lm_head_nc<F_BF16, 3>(a, grid, s);
+            case 4: return launch_lm_head_nc<F_BF16, 4>(a, grid, s);
+        }
+    } else {
+        switch (ncol) {
+            case 1: return launch_lm_head_nc<F_FP8, 1>(a, grid, s);
+            case 2: return launch_lm_head_nc<F_FP8, 2>(a, grid, s);
+            case 3: return launch_lm_head_nc<F_FP8, 3>(a, grid, s);
+            case 4: return launch_lm_head_nc<F_FP8, 4>(a, grid, s);
+        }
+    }
+    return hipErrorInvalidValue;
+}
+
+// ------------------------------------------------- FP8 row quantisation
+
+// One workgroup per row: amax over the row (exact), scale = amax / 448 in
+// binary32 (1 for a zero row), codes = E4M3FN(w / scale).
+__global__ void __launch_bounds__(256) quantize_fp8_rows_kernel(const uint16_t* __restrict__ w, int64_t cols,
+                                                                uint8_t* __restrict__ codes,
+                                                                float* __restrict__ scales) {
+    __shared__ float red[4];
+    const int64_t r = blockIdx.x;
+    const uint16_t* row = w + r * cols;
+    float m = 0.f;
+    for (int64_t i = threadIdx.x; i < cols; i += blockDim.x) m = fmaxf(m, fabsf(bf16_to_f32(row[i])));
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
+    if (threadIdx.x == 0) scales[r] = scale;
+    uint8_t* crow = codes + r * cols;
+    for (int64_t i = threadIdx.x; i < cols; i += blockDim.x) crow[i] = f32_to_fp8e4m3(bf16_to_f32(row[i]) / scale);
+}
+
+hipError_t launch_quantize_fp8_rows(const uint16_t* w, int64_t rows, int64_t cols, uint8_t* codes, float* scales,
+                                    hipStream_t s) {
+    hipLaunchKernelGGL(quantize_fp8_rows_kernel, dim3((unsigned)rows), dim3(256), 0, s, w, cols, codes, scales);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- KV write
+
+__global__ void __launch_bounds__(256) kv_write_kernel(KvWriteArgs a) {
+    const int64_t per_pos = (int64_t)a.n_kv_heads * a.head_dim;
+    const int64_t total = (int64_t)a.n * per_pos * 2;
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < total;
+         idx += (int64_t)gridDim.x * blockDim.x) {
+        const int kv = (int)(idx / ((int64_t)a.n * per_pos));
+        const int64_t rem = idx - (int64_t)kv * a.n * per_pos;
+        const int t = (int)(rem / per_pos);
+        const int64_t hd = rem - (int64_t)t * per_pos;
+        const int g = (int)(hd / a.head_dim);
+        const int e = (int)(hd - (int64_t)g * a.head_dim);
+        const int pos = a.pos0 + t;
+        const int page = a.page_table[pos / a.page_size];
+        const int slot = pos % a.page_size;
+        const int64_t off = a.layer_off +
+                            ((((int64_t)page * 2 + kv) * a.n_kv_heads + g) * a.page_size + slot) * a.head_dim + e;
+        const float v = (kv == 0 ? a.k : a.v)[rem];
+        if (a.dtype == F_BF16) {
+            reinterpret_cast<uint16_t*>(a.pool)[off] = f32_to_bf16(v);
+        } else {
+            const float sc = a.scales[(a.layer * a.n_kv_heads + g) * 2 + kv];
+            reinterpret_cast<uint8_t*>(a.pool)[off] = f32_to_fp8e4m3(v / sc);
+        }
+    }
+}
+
+hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s) {
+    const int64_t total = (int64_t)a.n * a.n_kv_heads * a.head_dim * 2;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(kv_write_kernel, dim3((unsigned)blocks), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- fill
+
+__global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = v;
+}
+
+hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s) {
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(fill_u32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
+}  // namespace mbg

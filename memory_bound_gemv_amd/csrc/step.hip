@@ -1,0 +1,936 @@
+// The persistent decode-step kernel: one cooperative launch per token (or
+// per verify window) runs every operation of every layer.
+//
+// Why one launch: a launch plus clean-up costs microseconds, so ten kernels
+// per layer over 25 layers would spend over a millisecond per token before
+// any useful work (Kog article "Real-time LLM inference on standard GPUs:
+// 3k tokens/s per request", section on where standard stacks lose
+// microseconds); a resident program removes those boundaries (same article,
+// monokernel section; "Muse Spark Open: 1,109 tokens/s" article, sections on
+// the launch baseline and the kernel boundary).
+//
+// Structure:
+//   * every workgroup walks its own static task list (built at init); a task
+//     is one tile of one operation of one layer;
+//   * a task first issues the loads that do not depend on the current step
+//     (weight rows, KV history), then waits until the dependency counter of
+//     the phase it reads has reached epoch * need, then computes, then adds
+//     one to its own phase counter with release semantics.  Counters are
+//     never reset: the epoch (launch number) makes them monotonic;
+//   * attention history (positions < pos) is loaded before the projections
+//     of the same layer finish, because it was written by earlier steps (the
+//     Muse Spark Open article's boundary section makes the same observation);
+//   * every wait has a deadline on the constant-rate clock; a workgroup whose
+//     wait expires latches a timeout and leaves, and all others follow, so a
+//     launch always drains;
+//   * with tracing on, thread 0 of each workgroup stamps every task (start,
+//     wait satisfied, end) into a workspace array: an external profiler sees
+//     one long kernel, so the kernel times itself (the Muse Spark Open
+//     article describes the same self-profiling, section on where the step
+//     time goes).  Stamps do not change any result.
+#include <hip/hip_runtime.h>
+
+#include "gemv.h"
+#include "layout.h"
+#include "ops.h"
+
+namespace mbg {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+// Upper bound of Q/K/V rows one wavefront owns in a step (pairs * 2).
+constexpr int kQkvRowsPerWave = 64;
+
+typedef const MBG_CONST StepArgs CArgs;
+typedef const MBG_CONST LayerPtrs CLayer;
+
+// Compile-time shape of a model family: hidden, FFN width, query width
+// (heads * head_dim), head_dim, query heads per KV head, KV format, MoE.
+template <int H_, int F_, int QD_, int HD_, int GQ_, int KVF_, int MOE_, int MF_>
+struct Shape {
+    static constexpr int H = H_, F = F_, QD = QD_, HD = HD_, GQ = GQ_, KVF = KVF_, MOE = MOE_, MF = MF_;
+};
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+__device__ __forceinline__ int lane_id() { return (int)(threadIdx.x & 63); }
+__device__ __forceinline__ uint32_t ctr_index(uint32_t layer, uint32_t ph) { return layer * PH_COUNT + ph; }
+
+__shared__ uint64_t s_twait;  // trace: when the current task's wait was satisfied
+
+// Cross-workgroup data (residual stream, q, new K/V, attention partials and
+// output, FFN hidden) is written and read with device-coherent accesses
+// (agent-scope relaxed atomics: loads and stores with the device-scope cache
+// policy), so no L2 write-back or invalidate is needed between phases: a
+// producer waits until its stores have completed, then bumps the phase
+// counter; a consumer that has seen the counter reads the data coherently.
+// Built with MBG_COHERENT=0 the same data moves through plain cached
+// accesses, ordered by release/acquire fences on the counters instead.
+#ifndef MBG_COHERENT
+#define MBG_COHERENT 1
+#endif
+__device__ __forceinline__ float ldc(const MBG_GLOBAL float* p) {
+#if MBG_COHERENT
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    return *p;
+#endif
+}
+__device__ __forceinline__ void stc(MBG_GLOBAL float* p, float v) {
+#if MBG_COHERENT
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    *p = v;
+#endif
+}
+template <class T>
+__device__ __forceinline__ void stc_small(MBG_GLOBAL T* p, T v) {
+#if MBG_COHERENT
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#else
+    *p = v;
+#endif
+}
+__device__ __forceinline__ uint4 ldc16(const MBG_GLOBAL uint4* p) {
+#if MBG_COHERENT
+    const MBG_GLOBAL uint32_t* q = reinterpret_cast<const MBG_GLOBAL uint32_t*>(p);
+    return make_uint4(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                      __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                      __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
+                      __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#else
+    return ld_g(p);
+#endif
+}
+__device__ __forceinline__ void acquire_after_wait() {
+#if !MBG_COHERENT
+    fence_acquire();
+#endif
+}
+__device__ __forceinline__ void release_before_signal() {
+#if !MBG_COHERENT
+    fence_release();
+#endif
+}
+
+// Wait until counter `idx` reaches epoch * need (mod 2^32).  Thread 0 polls;
+// the others wait at the barrier.  Returns false when the launch is aborting.
+__device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
+    __shared__ int s_ok;
+    if (threadIdx.x == 0) {
+        int ok = 1;
+        if (idx != kNoWait) {
+            const uint32_t target = a->epoch * need;
+            const MBG_GLOBAL uint32_t* ctr = gp(a->ctr) + idx;
+            const MBG_GLOBAL uint32_t* st = gp(a->status);
+            const uint64_t t0 = wall_clock64();
+            while ((int32_t)(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
+                if (__hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = 0; break; }
+                if (wall_clock64() - t0 > a->deadline_ticks) {
+                    latch_error(a->status, kStatusTimeout);
+                    ok = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        if (ok) acquire_after_wait();
+        s_ok = ok;
+        s_twait = wall_clock64();
+    }
+    __syncthreads();
+    return s_ok != 0;
+}
+
+// Make this workgroup's stores visible at device scope, then count the task.
+__device__ __forceinline__ void release_counter(CArgs* a, uint32_t idx) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached L2
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        release_before_signal();
+        __hip_atomic_fetch_add(gp(a->ctr) + idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+__device__ __forceinline__ int token_of(CArgs* a, int c) {
+    int t = gp(a->tokens)[c];
+    if (t < 0 || t >= a->vocab) {
+        if (threadIdx.x == 0) latch_error(a->status, kStatusRange);
+        t = t < 0 ? 0 : a->vocab - 1;
+    }
+    return t;
+}
+
+// xs[c][i] = src(c, i) / sqrt(mean_i src(c, i)^2 + eps) * gain[i], c < NC,
+// i < H; sums of squares in a fixed order (per thread, then the wave tree,
+// then the four waves in order).
+template <int NC, int H, class Src>
+__device__ void load_normed(CArgs* a, Src src, const uint16_t* gain, lds_f32* xs) {
+    __shared__ float red[kWaves * 4];
+    static_assert(H % kThreads == 0, "hidden size");
+    constexpr int PER = H / kThreads;
+    const int tid = threadIdx.x;
+    const MBG_GLOBAL uint16_t* g = gp(gain);
+    float v[NC][PER];
+    float ss[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        ss[c] = 0.f;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            v[c][p] = src(c, tid + kThreads * p);
+            ss[c] = fmaf(v[c][p], v[c][p], ss[c]);
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const float w = wave_sum(ss[c]);
+        if ((tid & 63) == 0) red[(tid >> 6) * 4 + c] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const float tot = ((red[c] + red[4 + c]) + red[8 + c]) + red[12 + c];
+        const float r = 1.0f / sqrtf(tot / (float)H + a->rms_eps);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int i = tid + kThreads * p;
+            xs[c * H + i] = v[c][p] * r * bf16_to_f32(g[i]);
+        }
+    }
+    __syncthreads();
+}
+
+// xs[0 .. NC*K) = src[...]: all loads issued before any LDS write (one
+// round trip of latency, not one per element group).
+template <int NC, int K>
+__device__ void load_plain(const float* src, lds_f32* xs) {
+    constexpr int N = NC * K;
+    constexpr int PER = (N + kThreads - 1) / kThreads;
+    const MBG_GLOBAL float* sp = gp(src);
+    float v[PER];
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int i = threadIdx.x + kThreads * p;
+        if (N % kThreads == 0 || i < N) v[p] = ldc(sp + i);
+    }
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+        const int i = threadIdx.x + kThreads * p;
+        if (N % kThreads == 0 || i < N) xs[i] = v[p];
+    }
+    __syncthreads();
+}
+
+__shared__ uint64_t s_stamp[2];  // trace: input loaded, stream finished
+__device__ __forceinline__ void stamp(int k) {
+    if (threadIdx.x == 0) s_stamp[k] = wall_clock64();
+}
+
+// ------------------------------------------------------------------ QKV
+
+template <int NC, class S>
+__device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+                                    lds_f32* xs) {
+    constexpr int HD = S::HD, HALF = HD / 2, H = S::H;
+    const int lane = lane_id();
+    const int wave = wave_id();
+    CLayer* L = (CLayer*)a->layers + layer;
+    const int Hq = a->n_q_heads, Hkv = a->n_kv_heads;
+    const int npairs = (Hq + 2 * Hkv) * HALF;
+    const int nw = (int)a->tiles_qkv * kWaves;
+    const int gw = (int)tile * kWaves + wave;
+    const int nunits = gw < npairs ? (npairs - 1 - gw) / nw + 1 : 0;
+    const uint16_t* wq = L->wq;
+    const uint16_t* wk = L->wk;
+    const uint16_t* wv = L->wv;
+    auto rowf = [&](int rr) -> GRow {
+        const int u = gw + nw * (rr >> 1);
+        const int hh = u / HALF;
+        const int i = u - hh * HALF + (rr & 1) * HALF;
+        const uint16_t* m;
+        int r;
+        if (hh < Hq) { m = wq; r = hh * HD + i; }
+        else if (hh < Hq + Hkv) { m = wk; r = (hh - Hq) * HD + i; }
+        else { m = wv; r = (hh - Hq - Hkv) * HD + i; }
+        return GRow{gp(reinterpret_cast<const uint4*>(m + (size_t)r * H)), nullptr};
+    };
+    using RS = RowStream<F_BF16, NC, H / 8>;
+    RS st(2 * nunits, lane);
+    typename RS::Buf A, B;
+    st.issue(A, 0, rowf);
+    if (!wait_counter(a, wctr, wneed)) return false;
+    if (layer == 0) {
+        int tok[NC];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) tok[c] = token_of(a, c);
+        const MBG_GLOBAL uint16_t* emb = gp(a->embed);
+        load_normed<NC, H>(a, [&](int c, int i) { return bf16_to_f32(emb[(size_t)tok[c] * H + i]); }, L->attn_norm, xs);
+    } else {
+        const MBG_GLOBAL float* x = gp(a->xres);
+        load_normed<NC, H>(a, [&](int c, int i) { return ldc(x + c * H + i); }, L->attn_norm, xs);
+    }
+    stamp(0);
+    // row sums -> per-wave LDS slots; RoPE and the cache write run after the stream
+    lds_f32* res = xs + NC * H + wave * kQkvRowsPerWave * NC;  // [rows][NC]
+    auto out = [&](int rr, const float (&s)[NC]) {
+        if (lane == 0) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) res[rr * NC + c] = s[c];
+        }
+    };
+    st.run(A, B, rowf, xs, H, out);
+    stamp(1);
+    __syncthreads();
+    const MBG_GLOBAL double* invf = gp(a->inv_freq);
+    const MBG_GLOBAL int32_t* ptab = gp(a->page_table);
+    for (int idx = lane; idx < nunits * NC; idx += kWave) {
+        const int pu = idx / NC;
+        const int c = idx - pu * NC;
+        float x0 = res[(2 * pu) * NC + c];
+        float x1 = res[(2 * pu + 1) * NC + c];
+        const int u = gw + nw * pu;
+        const int hh = u / HALF;
+        const int i = u - hh * HALF;
+        const int p = a->pos + c;
+        if (hh < Hq + Hkv) {
+            double sd, cd;
+            sincos((double)p * invf[i], &sd, &cd);
+            const float cs = (float)cd, sn = (float)sd;
+            const float y0 = x0 * cs - x1 * sn;
+            const float y1 = x0 * sn + x1 * cs;
+            x0 = y0;
+            x1 = y1;
+        }
+        if (hh < Hq) {
+            MBG_GLOBAL float* q = gp(a->qbuf) + ((size_t)c * Hq + hh) * HD;
+            stc(q + i, x0);
+            stc(q + i + HALF, x1);
+            continue;
+        }
+        const int kv = hh < Hq + Hkv ? 0 : 1;
+        const int gh = kv == 0 ? hh - Hq : hh - Hq - Hkv;
+        const int lp = p / a->page_size;
+        const int page = ptab[lp];
+        const int slot = p - lp * a->page_size;
+        const size_t off = (size_t)layer * a->kv_layer_stride +
+                           ((((size_t)page * 2 + kv) * Hkv + gh) * a->page_size + slot) * HD + i;
+        if constexpr (S::KVF == F_BF16) {
+            MBG_GLOBAL uint16_t* pool = gp(reinterpret_cast<uint16_t*>(a->kv_pool));
+            stc_small<uint16_t>(pool + off, f32_to_bf16(x0));
+            stc_small<uint16_t>(pool + off + HALF, f32_to_bf16(x1));
+        } else {
+            MBG_GLOBAL uint8_t* pool = gp(reinterpret_cast<uint8_t*>(a->kv_pool));
+            const float sc = gp(a->kv_scales)[((size_t)layer * Hkv + gh) * 2 + kv];
+            stc_small<uint8_t>(pool + off, f32_to_fp8e4m3(x0 / sc));
+            stc_small<uint8_t>(pool + off + HALF, f32_to_fp8e4m3(x1 / sc));
+        }
+    }
+    release_counter(a, ctr_index(layer, PH_QKV));
+    return true;
+}
+
+// ------------------------------------------------------------ attention
+
+// Merge weights of two softmax states (log2 domain).  Callers combine with
+// products first and one commutative add, so merge(x, y) == merge(y, x)
+// bit for bit.
+__device__ __forceinline__ void merge_weights(float m1, float m2, float& mn, float& w1, float& w2) {
+    mn = fmaxf(m1, m2);
+    if (mn == -INFINITY) {
+        w1 = 0.f;
+        w2 = 0.f;
+        return;
+    }
+    w1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - mn);
+    w2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
+}
+
+template <int NC, class S>
+__device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+                                     lds_f32* smem) {
+    constexpr int HD = S::HD, GQ = S::GQ, KVF = S::KVF;
+    constexpr int EB = KVF == F_BF16 ? 2 : 1;
+    constexpr int LPT = HD * EB / 16;        // lanes per token row
+    constexpr int EPC = 16 / EB;             // elements per lane
+    constexpr int SW = kWave / LPT;          // token slots per wave
+    constexpr int NS = kWaves * SW;          // token slots per workgroup
+    constexpr int CT = 4;                    // tokens per lane per chunk
+    static_assert(LPT == 4 || LPT == 8 || LPT == 16, "row layout");
+    const int lane = lane_id();
+    const int wave = wave_id();
+    const int Hq = a->n_q_heads, Hkv = a->n_kv_heads;
+    const int S_ = a->attn_splits;
+    const int g = (int)tile / S_;
+    const int s = (int)tile - g * S_;
+    const int pos = a->pos, ncol = a->ncol, page_size = a->page_size;
+    const int n_tok = pos + ncol;
+    const int T = (n_tok + S_ - 1) / S_;
+    const int t0 = s * T;
+    const int t1 = min(t0 + T, n_tok);
+    const int slot = wave * SW + lane / LPT;
+    const int cidx = lane % LPT;
+    const size_t layer_off = (size_t)layer * a->kv_layer_stride;
+    const MBG_GLOBAL uint8_t* pool = gp(reinterpret_cast<const uint8_t*>(a->kv_pool));
+    const MBG_GLOBAL int32_t* ptab = gp(a->page_table);
+
+    auto kv_ptr = [&](int t, int kv) -> const MBG_GLOBAL uint4* {
+        const int lp = t / page_size;
+        const int page = ptab[lp];
+        const int sl = t - lp * page_size;
+        const size_t el = layer_off + ((((size_t)page * 2 + kv) * Hkv + g) * page_size + sl) * HD;
+        return reinterpret_cast<const MBG_GLOBAL uint4*>(pool + el * EB + (size_t)cidx * 16);
+    };
+
+    uint4 KA[CT], VA[CT], KB[CT], VB[CT];
+    // token of chunk element j of chunk ch: t0 + slot + NS * (ch * CT + j)
+    auto issue = [&](uint4 (&K)[CT], uint4 (&V)[CT], int ch, int te, int limit) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j) {
+            const int t = t0 + slot + NS * (ch * CT + j);
+            if (t < te && t < limit) {
+                K[j] = ld_stream_g(kv_ptr(t, 0));
+                V[j] = ld_stream_g(kv_ptr(t, 1));
+            } else {
+                K[j] = make_uint4(0, 0, 0, 0);
+                V[j] = make_uint4(0, 0, 0, 0);
+            }
+        }
+    };
+
+    const bool empty = t0 >= t1;
+    // history (positions < pos) does not depend on this step: load it first
+    if (!empty) issue(KA, VA, 0, min(t1, pos + 1), pos);
+    if (!wait_counter(a, wctr, wneed)) return false;
+
+    const float qscale = a->attn_scale_log2;
+    const float ksc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 0] : 1.f;
+    const float vsc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 1] : 1.f;
+    lds_f32* red = smem;  // [kWaves][GQ][HD + 2]
+    constexpr int stride = HD + 2;
+    for (int col = 0; col < ncol && !empty; ++col) {
+        const int te = min(t1, pos + col + 1);
+        const int nlane0 = te > t0 ? (te - t0 + NS - 1) / NS : 0;  // tokens of slot 0
+        const int nch = (nlane0 + CT - 1) / CT;
+        float q[GQ][EPC];
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            const MBG_GLOBAL float* qp = gp(a->qbuf) + ((size_t)col * Hq + g * GQ + h) * HD + cidx * EPC;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) q[h][e] = ldc(qp + e) * qscale;
+        }
+        if (col == 0) stamp(0);
+        float m[GQ], l[GQ], o[GQ][EPC];
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            m[h] = -INFINITY;
+            l[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) o[h][e] = 0.f;
+        }
+        if (col == 0) {
+            // complete chunk 0 with the positions >= pos written this step
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                const int t = t0 + slot + NS * j;
+                if (t >= pos && t < te) {
+                    KA[j] = ldc16(kv_ptr(t, 0));
+                    VA[j] = ldc16(kv_ptr(t, 1));
+                }
+            }
+        } else {
+            issue(KA, VA, 0, te, 0x7FFFFFFF);
+        }
+        auto compute = [&](const uint4 (&K)[CT], const uint4 (&V)[CT], int ch) {
+            float sc[CT][GQ];
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                float kf[EPC];
+                decode16<KVF>(K[j], 0u, kf);
+                const int t = t0 + slot + NS * (ch * CT + j);
+                const bool valid = t < te;
+#pragma unroll
+                for (int h = 0; h < GQ; ++h) {
+                    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+                    for (int e = 0; e < EPC; e += 2) {
+                        p0 = fmaf(q[h][e], kf[e], p0);
+                        p1 = fmaf(q[h][e + 1], kf[e + 1], p1);
+                    }
+                    const float sv = group_sum<LPT>(p0 + p1) * ksc;
+                    sc[j][h] = valid ? sv : -INFINITY;
+                }
+            }
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                float cm = -INFINITY;
+#pragma unroll
+                for (int j = 0; j < CT; ++j) cm = fmaxf(cm, sc[j][h]);
+                const float mn = fmaxf(m[h], cm);
+                if (mn == -INFINITY) {  // no valid token yet: weights are 0, state unchanged
+#pragma unroll
+                    for (int j = 0; j < CT; ++j) sc[j][h] = 0.f;
+                    continue;
+                }
+                const float al = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+                m[h] = mn;
+                l[h] *= al;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o[h][e] *= al;
+#pragma unroll
+                for (int j = 0; j < CT; ++j) {
+                    sc[j][h] = sc[j][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[j][h] - mn);
+                    l[h] += sc[j][h];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < CT; ++j) {
+                float vf[EPC];
+                decode16<KVF>(V[j], 0u, vf);
+#pragma unroll
+                for (int h = 0; h < GQ; ++h) {
+                    const float p = sc[j][h];
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
+                }
+            }
+        };
+        for (int ch = 0; ch < nch; ch += 2) {
+            if (ch + 1 < nch) issue(KB, VB, ch + 1, te, 0x7FFFFFFF);
+            compute(KA, VA, ch);
+            if (ch + 1 >= nch) break;
+            if (ch + 2 < nch) issue(KA, VA, ch + 2, te, 0x7FFFFFFF);
+            compute(KB, VB, ch + 1);
+        }
+        if constexpr (KVF == F_FP8) {
+#pragma unroll
+            for (int h = 0; h < GQ; ++h)
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o[h][e] *= vsc;
+        }
+        // merge the token slots of a wave (lanes with the same cidx)
+#pragma unroll
+        for (int msk = LPT; msk < kWave; msk <<= 1) {
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                const float m2 = shfl_xor_f(m[h], msk);
+                const float l2 = shfl_xor_f(l[h], msk);
+                float mn, w1, w2;
+                merge_weights(m[h], m2, mn, w1, w2);
+                l[h] = l[h] * w1 + l2 * w2;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) {
+                    const float o2 = shfl_xor_f(o[h][e], msk);
+                    o[h][e] = o[h][e] * w1 + o2 * w2;
+                }
+                m[h] = mn;
+            }
+        }
+        // then the waves, through LDS, in wave order
+        if (lane < LPT) {
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                lds_f32* r = red + ((size_t)wave * GQ + h) * stride;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) r[cidx * EPC + e] = o[h][e];
+                if (cidx == 0) {
+                    r[HD] = m[h];
+                    r[HD + 1] = l[h];
+                }
+            }
+        }
+        __syncthreads();
+        if (wave == 0 && lane < LPT) {
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                float M = red[h * stride + HD], Ls = red[h * stride + HD + 1];
+                float O[EPC];
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) O[e] = red[h * stride + cidx * EPC + e];
+                for (int w = 1; w < kWaves; ++w) {
+                    const lds_f32* r = red + ((size_t)w * GQ + h) * stride;
+                    float mn, w1, w2;
+                    merge_weights(M, r[HD], mn, w1, w2);
+                    Ls = Ls * w1 + r[HD + 1] * w2;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) O[e] = O[e] * w1 + r[cidx * EPC + e] * w2;
+                    M = mn;
+                }
+                MBG_GLOBAL float* dst = gp(a->part) + (((size_t)col * Hq + g * GQ + h) * S_ + s) * stride;
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) stc(dst + cidx * EPC + e, O[e]);
+                if (cidx == 0) {
+                    stc(dst + HD, M);
+                    stc(dst + HD + 1, Ls);
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    stamp(1);
+    // arrival; the last split of this KV head combines all of them
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        release_before_signal();
+        const uint32_t old = __hip_atomic_fetch_add(gp(a->head_ctr) + layer * Hkv + g, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old + 1u == a->epoch * (uint32_t)S_);
+        if (s_last) acquire_after_wait();
+    }
+    __syncthreads();
+    if (!s_last) return true;
+    // Combine: softmax over [0, pos + col] = weights exp2(m_s - M) on the
+    // split partials, normalised by their weighted sum.  All loads of a stage
+    // are issued before any is used.
+    const int nsv = min(S_, (n_tok + T - 1) / T);   // splits that wrote partials
+    const MBG_GLOBAL float* part = gp(a->part);
+    MBG_GLOBAL float* attn = gp(a->attn);
+    lds_f32* wts = smem;                               // [ncol][GQ][S]
+    lds_f32* inv = smem + 4 * GQ * 64;                 // [ncol][GQ]
+    const int nw_ = ncol * GQ * nsv;
+    for (int idx = threadIdx.x; idx < nw_; idx += kThreads) {
+        const int ch = idx / nsv, sp = idx - ch * nsv;  // ch = col * GQ + h
+        const int col = ch / GQ, h = ch - col * GQ;
+        wts[ch * 64 + sp] = ldc(part + (((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + HD);
+        inv[ch] = 0.f;
+    }
+    __syncthreads();
+    for (int ch = threadIdx.x; ch < ncol * GQ; ch += kThreads) {
+        const int col = ch / GQ, h = ch - col * GQ;
+        float M = -INFINITY;
+        for (int sp = 0; sp < nsv; ++sp) M = fmaxf(M, wts[ch * 64 + sp]);
+        float Lsum = 0.f;
+        for (int sp = 0; sp < nsv; ++sp) {
+            const float ms = wts[ch * 64 + sp];
+            const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
+            wts[ch * 64 + sp] = w;
+            Lsum += w * ldc(part + (((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + HD + 1);
+        }
+        inv[ch] = Lsum;
+    }
+    __syncthreads();
+    for (int idx = threadIdx.x; idx < ncol * GQ * HD; idx += kThreads) {
+        const int ch = idx / HD;
+        const int e = idx - ch * HD;
+        const int col = ch / GQ, h = ch - col * GQ;
+        const MBG_GLOBAL float* base = part + ((size_t)col * Hq + g * GQ + h) * S_ * stride + e;
+        float ov[64];
+#pragma unroll
+        for (int sp = 0; sp < 64; ++sp)
+            if (sp < nsv) ov[sp] = ldc(base + (size_t)sp * stride);
+        float O = 0.f;
+#pragma unroll
+        for (int sp = 0; sp < 64; ++sp)
+            if (sp < nsv) O = fmaf(wts[ch * 64 + sp], ov[sp], O);
+        stc(attn + (size_t)col * Hq * HD + (g * GQ + h) * HD + e, O / inv[ch]);
+    }
+    release_counter(a, ctr_index(layer, PH_ATTN));
+    return true;
+}
+
+// --------------------------------------------------- plain row GEMVs
+
+template <int NC, class S>
+__device__ __forceinline__ bool op_oproj(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+                                      lds_f32* xs) {
+    constexpr int H = S::H, K = S::QD;
+    const int lane = lane_id(), wave = wave_id();
+    CLayer* L = (CLayer*)a->layers + layer;
+    const int nw = (int)a->tiles_o * kWaves, gw = (int)tile * kWaves + wave;
+    const int nrows = gw < H ? (H - 1 - gw) / nw + 1 : 0;
+    const uint16_t* wo = L->wo;
+    auto rowf = [&](int rr) -> GRow {
+        return GRow{gp(reinterpret_cast<const uint4*>(wo + (size_t)(gw + nw * rr) * K)), nullptr};
+    };
+    using RS = RowStream<F_BF16, NC, K / 8>;
+    RS st(nrows, lane);
+    typename RS::Buf A, B;
+    st.issue(A, 0, rowf);
+    if (!wait_counter(a, wctr, wneed)) return false;
+    load_plain<NC, K>(a->attn, xs);
+    stamp(0);
+    int tok[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) tok[c] = layer == 0 ? token_of(a, c) : 0;
+    MBG_GLOBAL float* x = gp(a->xres);
+    const MBG_GLOBAL uint16_t* emb = gp(a->embed);
+    auto out = [&](int rr, const float (&s)[NC]) {
+        if (lane >= NC) return;
+        const int c = lane;
+        float v = 0.f;
+        int tk_ = 0;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+            if (cc == c) { v = s[cc]; tk_ = tok[cc]; }
+        const int r = gw + nw * rr;
+        const float res = layer == 0 ? bf16_to_f32(emb[(size_t)tk_ * H + r]) : ldc(x + c * H + r);
+        stc(x + c * H + r, res + v);
+    };
+    st.run(A, B, rowf, xs, K, out);
+    stamp(1);
+    release_counter(a, ctr_index(layer, PH_OPROJ));
+    return true;
+}
+
+template <int NC, class S>
+__device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+                                       lds_f32* xs) {
+    constexpr int H = S::H, F = S::F;
+    const int lane = lane_id(), wave = wave_id();
+    CLayer* L = (CLayer*)a->layers + layer;
+    const int nw = (int)a->tiles_gu * kWaves, gw = (int)tile * kWaves + wave;
+    const int nunits = gw < F ? (F - 1 - gw) / nw + 1 : 0;
+    const uint16_t* wg = L->w_gate;
+    const uint16_t* wu = L->w_up;
+    auto rowf = [&](int rr) -> GRow {
+        const int f = gw + nw * (rr >> 1);
+        const uint16_t* m = (rr & 1) ? wu : wg;
+        return GRow{gp(reinterpret_cast<const uint4*>(m + (size_t)f * H)), nullptr};
+    };
+    using RS = RowStream<F_BF16, NC, H / 8>;
+    RS st(2 * nunits, lane);
+    typename RS::Buf A, B;
+    st.issue(A, 0, rowf);
+    if (!wait_counter(a, wctr, wneed)) return false;
+    const MBG_GLOBAL float* x = gp(a->xres);
+    load_normed<NC, H>(a, [&](int c, int i) { return ldc(x + c * H + i); }, L->ffn_norm, xs);
+    stamp(0);
+    MBG_GLOBAL float* hb = gp(a->hbuf);
+    float gate[NC];
+    auto out = [&](int rr, const float (&s)[NC]) {
+        if ((rr & 1) == 0) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) gate[c] = s[c];
+            return;
+        }
+        if (lane >= NC) return;
+        const int c = lane;
+        float gv = 0.f, uv = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+            if (cc == c) { gv = gate[cc]; uv = s[cc]; }
+        const int f = gw + nw * (rr >> 1);
+        stc(hb + (size_t)c * F + f, gv / (1.0f + expf(-gv)) * uv);
+    };
+    st.run(A, B, rowf, xs, H, out);
+    stamp(1);
+    release_counter(a, ctr_index(layer, PH_GATEUP));
+    return true;
+}
+
+template <int NC, class S>
+__device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+                                     lds_f32* xs) {
+    constexpr int H = S::H, F = S::F;
+    const int lane = lane_id(), wave = wave_id();
+    CLayer* L = (CLayer*)a->layers + layer;
+    const int nw = (int)a->tiles_down * kWaves, gw = (int)tile * kWaves + wave;
+    const int nrows = gw < H ? (H - 1 - gw) / nw + 1 : 0;
+    const uint16_t* wd = L->w_down;
+    auto rowf = [&](int rr) -> GRow {
+        return GRow{gp(reinterpret_cast<const uint4*>(wd + (size_t)(gw + nw * rr) * F)), nullptr};
+    };
+    using RS = RowStream<F_BF16, NC, F / 8>;
+    RS st(nrows, lane);
+    typename RS::Buf A, B;
+    st.issue(A, 0, rowf);
+    if (!wait_counter(a, wctr, wneed)) return false;
+    load_plain<NC, F>(a->hbuf, xs);
+    stamp(0);
+    MBG_GLOBAL float* x = gp(a->xres);
+    auto out = [&](int rr, const float (&s)[NC]) {
+        if (lane >= NC) return;
+        const int c = lane;
+        float v = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+            if (cc == c) v = s[cc];
+        const int r = gw + nw * rr;
+        stc(x + c * H + r, ldc(x + c * H + r) + v);
+    };
+    st.run(A, B, rowf, xs, F, out);
+    stamp(1);
+    release_counter(a, ctr_index(layer, PH_DOWN));
+    return true;
+}
+
+// --------------------------------------------------------------- LM head
+
+__device__ __forceinline__ uint32_t ordered_key32(float f) {
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int NC, class S, int F>
+__device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr, uint32_t wneed, lds_f32* xs) {
+    constexpr int H = S::H;
+    constexpr int E = FmtInfo<F>::kEPV;
+    __shared__ unsigned long long wbest[kWaves * 4];
+    const int lane = lane_id(), wave = wave_id();
+    const int V = a->vocab;
+    const int nw = (int)a->tiles_lm * kWaves, gw = (int)tile * kWaves + wave;
+    const int nrows = gw < V ? (V - 1 - gw) / nw + 1 : 0;
+    const MBG_GLOBAL uint4* W = gp(reinterpret_cast<const uint4*>(a->lm_head));
+    auto rowf = [&](int rr) -> GRow { return GRow{W + (size_t)(gw + nw * rr) * (H / E), nullptr}; };
+    using RS = RowStream<F, NC, H / E>;
+    RS st(nrows, lane);
+    typename RS::Buf A, B;
+    st.issue(A, 0, rowf);
+    if (!wait_counter(a, wctr, wneed)) return false;
+    const MBG_GLOBAL float* x = gp(a->xres);
+    load_normed<NC, H>(a, [&](int c, int i) { return ldc(x + c * H + i); }, a->final_norm, xs);
+    stamp(0);
+    unsigned long long best[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) best[c] = 0ull;
+    MBG_GLOBAL float* logits = a->logits ? gp(a->logits) : nullptr;
+    const MBG_GLOBAL float* lsc = gp(a->lm_scale);
+    auto out = [&](int rr, const float (&s)[NC]) {
+        const uint32_t r = (uint32_t)(gw + nw * rr);
+        const float sc = F == F_FP8 ? lsc[r] : 1.0f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float v = s[c] * sc;
+            if (logits != nullptr && lane == c) logits[(size_t)c * V + r] = v;
+            const unsigned long long k = ((unsigned long long)ordered_key32(v) << 32) | (0xFFFFFFFFu - r);
+            best[c] = k > best[c] ? k : best[c];
+        }
+    };
+    st.run(A, B, rowf, xs, H, out);
+    stamp(1);
+    if (lane == 0) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) wbest[wave * 4 + c] = best[c];
+    }
+    __syncthreads();
+    MBG_GLOBAL unsigned long long* keys = gp(a->amax_keys);
+    if (threadIdx.x < NC) {
+        const int c = threadIdx.x;
+        unsigned long long b = wbest[c];
+        for (int w = 1; w < kWaves; ++w) b = wbest[w * 4 + c] > b ? wbest[w * 4 + c] : b;
+        __hip_atomic_fetch_max(keys + c, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __shared__ int s_last;
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        release_before_signal();
+        const uint32_t old = __hip_atomic_fetch_add(gp(a->lm_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (old + 1u == a->epoch * a->tiles_lm);
+        if (s_last) acquire_after_wait();
+    }
+    __syncthreads();
+    if (s_last && threadIdx.x < NC) {
+        const int c = threadIdx.x;
+        const unsigned long long k = __hip_atomic_load(keys + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        gp(a->argmax)[c] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        __hip_atomic_store(keys + c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    return true;
+}
+
+// ------------------------------------------------------------------ kernel
+
+template <int NC, class S>
+__global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
+    (void)args;
+    CArgs* a = (CArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    extern __shared__ __align__(16) float smem_raw[];
+    lds_f32* smem = (lds_f32*)smem_raw;
+    const uint32_t b = blockIdx.x;
+    const MBG_CONST uint32_t* off = (const MBG_CONST uint32_t*)a->task_off;
+    const MBG_CONST u32x4* tasks = (const MBG_CONST u32x4*)a->tasks;
+    const uint32_t end = off[b + 1];
+    MBG_GLOBAL unsigned long long* trace = a->trace ? gp(a->trace) : nullptr;
+    for (uint32_t ti = off[b]; ti < end; ++ti) {
+        const u32x4 tv = tasks[ti];
+        const Task tk{tv[0], tv[1], tv[2], tv[3]};
+        const uint32_t op = tk.op_layer & 0xFFu;
+        const uint32_t layer = tk.op_layer >> 8;
+        const uint64_t t_start = trace ? wall_clock64() : 0;
+        bool ok = true;
+        switch (op) {
+            case OP_QKV: ok = op_qkv<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
+            case OP_ATTN: ok = op_attn<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
+            case OP_OPROJ: ok = op_oproj<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
+            case OP_GATEUP: ok = op_gateup<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
+            case OP_DOWN: ok = op_down<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
+            case OP_LMHEAD:
+                ok = a->lm_dtype == F_FP8 ? op_lmhead<NC, S, F_FP8>(a, tk.tile, tk.wait_ctr, tk.wait_need, smem)
+                                          : op_lmhead<NC, S, F_BF16>(a, tk.tile, tk.wait_ctr, tk.wait_need, smem);
+                break;
+            default: break;
+        }
+        if (!ok) return;
+        __syncthreads();  // LDS is reused by the next task
+        if (trace && threadIdx.x == 0) {
+            MBG_GLOBAL unsigned long long* r = trace + (size_t)ti * 8;
+            r[0] = t_start;
+            r[1] = s_twait;
+            r[2] = s_stamp[0];
+            r[3] = s_stamp[1];
+            r[4] = wall_clock64();
+            r[5] = (unsigned long long)tk.op_layer | ((unsigned long long)tk.tile << 32);
+            r[6] = 0;
+            r[7] = 0;
+        }
+    }
+}
+
+// ----------------------------------------------------------- variants
+
+// Model families compiled in: Shape<hidden, ffn, q_heads * head_dim,
+// head_dim, q heads per KV head, KV format, MoE, moe_ffn>.
+using ShapeTiny = Shape<256, 1024, 256, 64, 2, F_BF16, 0, 0>;
+using ShapeDense2B = Shape<2048, 8192, 2048, 128, 2, F_BF16, 0, 0>;
+using ShapeDense2BFp8Kv = Shape<2048, 8192, 2048, 128, 2, F_FP8, 0, 0>;
+#define MBG_VARIANTS(X) X(ShapeTiny) X(ShapeDense2B) X(ShapeDense2BFp8Kv)
+
+template <class S>
+static bool matches(const StepVariant& v) {
+    return v.hidden == S::H && v.ffn == S::F && v.qdim == S::QD && v.head_dim == S::HD && v.group == S::GQ &&
+           v.kv_fmt == S::KVF && v.moe == S::MOE && v.moe_ffn == S::MF;
+}
+
+template <class S>
+static const void* pick(int ncol) {
+    switch (ncol) {
+        case 1: return reinterpret_cast<const void*>(&step_kernel<1, S>);
+        case 2: return reinterpret_cast<const void*>(&step_kernel<2, S>);
+        case 3: return reinterpret_cast<const void*>(&step_kernel<3, S>);
+        case 4: return reinterpret_cast<const void*>(&step_kernel<4, S>);
+    }
+    return nullptr;
+}
+
+bool step_variant_supported(const StepVariant& v) {
+#define X(SH) \
+    if (matches<SH>(v)) return true;
+    MBG_VARIANTS(X)
+#undef X
+    return false;
+}
+
+const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out) {
+    const void* fn = nullptr;
+#define X(SH) \
+    if (!fn && matches<SH>(v)) fn = pick<SH>(ncol);
+    MBG_VARIANTS(X)
+#undef X
+    if (fn && lds_bytes_out) {
+        int kmax = v.hidden;
+        if (v.ffn > kmax) kmax = v.ffn;
+        if (v.qdim > kmax) kmax = v.qdim;
+        if (v.moe_ffn > kmax) kmax = v.moe_ffn;
+        const int xs_bytes = ncol * kmax * 4 + kWaves * kQkvRowsPerWave * ncol * 4;
+        const int red_bytes = kWaves * v.group * (v.head_dim + 2) * 4;
+        const int comb_bytes = (4 * v.group * 64 + 4 * v.group) * 4;
+        int m = xs_bytes > red_bytes ? xs_bytes : red_bytes;
+        *lds_bytes_out = m > comb_bytes ? m : comb_bytes;
+    }
+    return fn;
+}
+
+}  // namespace mbg

@@ -1,0 +1,149 @@
+"""Device-side plumbing around the C-ABI: upload host arrays into torch
+device tensors, describe them to the library, own the KV pool and the
+workspace, and forward step/verify calls.  No decode arithmetic happens here
+(PyTorch provides device memory and the stream; the HIP library does the
+work)."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import _mbg as M
+
+
+def _dev(a: np.ndarray, device) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if t.dtype == torch.uint16:
+        t = t.view(torch.int16)
+    return t.to(device)
+
+
+class DeviceModel:
+    """One decoder on one GPU.
+
+    cfg: any object with the shape attributes of ``synth.configs.DecodeConfig``.
+    host: dict of host arrays named like ``embed``, ``final_norm``, ``lm_head``,
+    ``l{i}.{attn_norm,wq,wk,wv,wo,ffn_norm,w_gate,w_up,w_down}`` (BF16 bits as
+    uint16).  lm_fp8: optional (codes uint8 [V][H], scales f32 [V]) given as
+    device tensors, replacing the BF16 LM head.
+    page_table: host int32 [n_pages] logical -> physical page.
+    """
+
+    def __init__(self, cfg, host: dict, page_table: np.ndarray, kv_dtype: str = "bf16", kv_scales=None,
+                 lm_fp8=None, device="cuda", k_max: int | None = None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        self.k_max = k_max or cfg.k_max
+        self.t = {k: _dev(v, self.device) for k, v in host.items()}
+        H, d = cfg.hidden, cfg.head_dim
+        bf = "bf16"
+
+        def T(name, rows, cols):
+            return M.make_tensor(self.t[name], bf, rows, cols)
+
+        layers = []
+        for i in range(cfg.n_layers):
+            p = f"l{i}."
+            lay = dict(
+                attn_norm=T(p + "attn_norm", 1, H), ffn_norm=T(p + "ffn_norm", 1, H),
+                wq=T(p + "wq", cfg.n_q_heads * d, H), wk=T(p + "wk", cfg.n_kv_heads * d, H),
+                wv=T(p + "wv", cfg.n_kv_heads * d, H), wo=T(p + "wo", H, cfg.n_q_heads * d))
+            if not cfg.is_moe:
+                lay.update(w_gate=T(p + "w_gate", cfg.ffn, H), w_up=T(p + "w_up", cfg.ffn, H),
+                           w_down=T(p + "w_down", H, cfg.ffn))
+            layers.append(M.make_layer(**lay))
+        if lm_fp8 is not None:
+            self.lm_codes, self.lm_scales = lm_fp8
+            lm = M.make_tensor(self.lm_codes, "fp8", cfg.vocab, H, scale=self.lm_scales)
+        else:
+            lm = T("lm_head", cfg.vocab, H)
+        self.weights = M.WeightSet(layers, T("embed", cfg.vocab, H), T("final_norm", 1, H), lm)
+
+        # KV pool [L][P][2][Hkv][page][d]
+        self.n_pages = int(page_table.max()) + 1 if page_table.size else 1
+        self.n_pages = max(self.n_pages, cfg.n_pages)
+        el = torch.int16 if kv_dtype == "bf16" else torch.uint8
+        self.pool = torch.zeros((cfg.n_layers, self.n_pages, 2, cfg.n_kv_heads, cfg.page_size, d), dtype=el,
+                                device=self.device)
+        self.page_table_host = np.asarray(page_table, dtype=np.int32)
+        self.page_table = torch.from_numpy(self.page_table_host).to(self.device)
+        self.kv_scales = None
+        if kv_dtype == "fp8":
+            self.kv_scales = torch.as_tensor(np.asarray(kv_scales, dtype=np.float32)).to(self.device).contiguous()
+        self.kv = M.make_kv(kv_dtype, self.n_pages, self.pool, self.page_table, self.kv_scales)
+        self.kv_dtype = kv_dtype
+
+        self.mcfg = M.make_config(cfg.n_layers, H, cfg.n_q_heads, cfg.n_kv_heads, d, cfg.ffn, cfg.vocab,
+                                  cfg.n_experts, cfg.top_k, cfg.n_shared, cfg.moe_ffn, cfg.rope_theta,
+                                  cfg.rms_eps, cfg.page_size, cfg.max_pos, self.k_max)
+        self.ws_bytes = M.mbg_workspace_size(self.mcfg)
+        self.ws = torch.zeros(self.ws_bytes // 4 + 64, dtype=torch.int32, device=self.device)
+        self.stream = torch.cuda.current_stream(self.device)
+        self.ctx = None
+
+    # ------------------------------------------------------------------ KV prefill
+    def prefill_bf16(self, layer: int, k_bits: np.ndarray, v_bits: np.ndarray) -> None:
+        """Place logical BF16 K/V [T][Hkv][d] of positions [0, T) into the pages."""
+        cfg = self.cfg
+        T = k_bits.shape[0]
+        P = cfg.page_size
+        npg = -(-T // P)
+        for which, src in ((0, k_bits), (1, v_bits)):
+            full = np.zeros((npg * P, cfg.n_kv_heads, cfg.head_dim), dtype=np.uint16)
+            full[:T] = src
+            blk = torch.from_numpy(full.view(np.int16)).to(self.device)
+            blk = blk.view(npg, P, cfg.n_kv_heads, cfg.head_dim).permute(0, 2, 1, 3)
+            phys = self.page_table[:npg].long()
+            if T % P:  # keep slots of the last page beyond T untouched
+                last = phys[-1]
+                keep = self.pool[layer, last, which, :, T % P:, :].clone()
+            self.pool[layer, phys, which] = blk
+            if T % P:
+                self.pool[layer, last, which, :, T % P:, :] = keep
+
+    def kv_write(self, layer: int, pos0: int, k: torch.Tensor, v: torch.Tensor) -> None:
+        """Quantising write through the library (cache dtype rounding)."""
+        M.mbg_kv_write(self.mcfg, self.kv, layer, pos0, k.shape[0], k, v, self.stream.cuda_stream)
+
+    # ------------------------------------------------------------------ decode
+    def init(self) -> None:
+        self.ctx = M.mbg_decode_init(self.mcfg, self.weights, self.kv, self.ws, self.ws_bytes,
+                                     self.stream.cuda_stream)
+
+    def info(self):
+        return M.mbg_query(self.ctx)
+
+    def step(self, token: torch.Tensor, pos: int, logits: torch.Tensor | None, argmax: torch.Tensor) -> None:
+        M.mbg_decode_step(self.ctx, token, pos, logits, argmax)
+
+    def verify(self, tokens: torch.Tensor, pos: int, logits, argmax) -> None:
+        M.mbg_decode_verify(self.ctx, tokens, tokens.numel(), pos, logits, argmax)
+
+    def status(self) -> int:
+        return M.mbg_get_status(self.ctx)
+
+    def close(self) -> None:
+        if self.ctx is not None:
+            M.mbg_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    # ------------------------------------------------------------------ inspection
+    def cache_logical(self, layer: int, upto: int):
+        """K, V of positions [0, upto) gathered back from the pages (host arrays)."""
+        cfg = self.cfg
+        P = cfg.page_size
+        npg = -(-upto // P)
+        phys = self.page_table[:npg].long()
+        out = []
+        for which in (0, 1):
+            blk = self.pool[layer, phys, which]                  # [npg][Hkv][P][d]
+            blk = blk.permute(0, 2, 1, 3).reshape(npg * P, cfg.n_kv_heads, cfg.head_dim)[:upto]
+            a = blk.cpu().numpy()
+            out.append(a.view(np.uint16) if a.dtype == np.int16 else a)
+        return out[0], out[1]
