@@ -132,6 +132,11 @@ __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, kWave);
 }
 
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits [3:0] and [15:14],
+// expcnt [6:4], lgkmcnt [11:8]); unnamed counters are left at their maximum.
+constexpr int waitcnt_vm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8); }
+constexpr int waitcnt_lgkm0() { return 0xF | (0x3 << 14) | (0x7 << 4); }
+
 // ------------------------------------------------- counters and watchdog
 
 __device__ __forceinline__ uint32_t ld_relaxed(const uint32_t* p) {

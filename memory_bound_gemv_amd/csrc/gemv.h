@@ -63,6 +63,20 @@ __device__ __forceinline__ uint4 ld_g(const MBG_GLOBAL uint4* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l's data
+// lands at dst + 16 * l (dst is the same for the whole wave).  Written as
+// inline assembly so that the compiler does not order it against other LDS
+// traffic with whole-counter waits; callers wait for these loads
+// explicitly (vmcnt), which stays correct for the compiler's own waits
+// because vector memory operations complete in issue order.
+__device__ __forceinline__ void lds_dma16(const MBG_GLOBAL void* src, MBG_LDS void* dst) {
+    const uint32_t lds = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+                 : "memory");
+}
+
 // Address of one weight row (scalar): 16-byte vectors plus, for MXFP4, one
 // E8M0 byte per vector.
 struct GRow {

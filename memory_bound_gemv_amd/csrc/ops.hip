@@ -78,7 +78,7 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
         for (int w = 1; w < 4; ++w) b = wbest[w * 4 + c] > b ? wbest[w * 4 + c] : b;
         __hip_atomic_fetch_max(keys + c, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if (threadIdx.x == 0) {
         fence_release();

@@ -143,7 +143,7 @@ __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
 
 // Make this workgroup's stores visible at device scope, then count the task.
 __device__ __forceinline__ void release_counter(CArgs* a, uint32_t idx) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stores have reached L2
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // vmcnt(0): this wave's stores have reached L2
     __syncthreads();
     if (threadIdx.x == 0) {
         release_before_signal();
@@ -345,17 +345,104 @@ __device__ __forceinline__ void merge_weights(float m1, float m2, float& mn, flo
     w2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
 }
 
+// Online-softmax state of one lane: GQ query heads, EPC dims of the output.
+// Scores are in the log2 domain (q is pre-scaled by log2(e) / sqrt(d)).
+template <int GQ, int EPC, int LPT, int KVF>
+struct AttnLane {
+    float m[GQ], l[GQ], o[GQ][EPC];
+
+    __device__ __forceinline__ void init() {
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            m[h] = -INFINITY;
+            l[h] = 0.f;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) o[h][e] = 0.f;
+        }
+    }
+
+    // Fold NT tokens (this lane's slices of their K and V rows) into the
+    // state.  Every lane of the wave must call it (group reductions).
+    template <int NT>
+    __device__ __forceinline__ void fold(const float (&q)[GQ][EPC], const uint4 (&K)[NT], const uint4 (&V)[NT],
+                                         const bool (&valid)[NT], float ksc) {
+        float sc[NT][GQ];
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            float kf[EPC];
+            decode16<KVF>(K[j], 0u, kf);
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+                float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+                for (int e = 0; e < EPC; e += 2) {
+                    p0 = fmaf(q[h][e], kf[e], p0);
+                    p1 = fmaf(q[h][e + 1], kf[e + 1], p1);
+                }
+                const float sv = group_sum<LPT>(p0 + p1) * ksc;
+                sc[j][h] = valid[j] ? sv : -INFINITY;
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            float cm = -INFINITY;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) cm = fmaxf(cm, sc[j][h]);
+            const float mn = fmaxf(m[h], cm);
+            if (mn == -INFINITY) {  // no valid token yet: weights are 0, state unchanged
+#pragma unroll
+                for (int j = 0; j < NT; ++j) sc[j][h] = 0.f;
+                continue;
+            }
+            const float al = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
+            m[h] = mn;
+            l[h] *= al;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) o[h][e] *= al;
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                sc[j][h] = sc[j][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[j][h] - mn);
+                l[h] += sc[j][h];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            float vf[EPC];
+            decode16<KVF>(V[j], 0u, vf);
+#pragma unroll
+            for (int h = 0; h < GQ; ++h) {
+#pragma unroll
+                for (int e = 0; e < EPC; ++e) o[h][e] = fmaf(sc[j][h], vf[e], o[h][e]);
+            }
+        }
+    }
+};
+
+// Attention LDS use: per wavefront a ring of 2 buffers x kAttnUnits units;
+// a unit is one wave instruction's worth of K rows (1 KiB) plus the same for
+// V.  The cross-wave merge area follows the rings.
+constexpr int kAttnUnits = 8;
+constexpr int kUnitBytes = kWave * 16;
+constexpr int kAttnWaveBytes = 2 * kAttnUnits * 2 * kUnitBytes;
+constexpr int kAttnRingBytes = kWaves * kAttnWaveBytes;
+
+// One (KV head, split) task: split-KV attention for the GQ query heads that
+// share KV head g, over positions [t0, t1) of the split, for every column of
+// the window.  History (positions < pos) streams straight from HBM into the
+// wave's LDS ring (global_load_lds_dwordx4); the first two ring buffers are
+// requested before the task waits for this step's q and new K/V.
 template <int NC, class S>
 __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
-                                     lds_f32* smem) {
+                                        lds_f32* smem) {
     constexpr int HD = S::HD, GQ = S::GQ, KVF = S::KVF;
     constexpr int EB = KVF == F_BF16 ? 2 : 1;
     constexpr int LPT = HD * EB / 16;        // lanes per token row
     constexpr int EPC = 16 / EB;             // elements per lane
-    constexpr int SW = kWave / LPT;          // token slots per wave
-    constexpr int NS = kWaves * SW;          // token slots per workgroup
-    constexpr int CT = 4;                    // tokens per lane per chunk
+    constexpr int TPI = kWave / LPT;         // tokens per wave instruction
+    constexpr int NS = kWaves * TPI;         // token slots per workgroup
+    constexpr int NUB = kAttnUnits;
     static_assert(LPT == 4 || LPT == 8 || LPT == 16, "row layout");
+    using Lane = AttnLane<GQ, EPC, LPT, KVF>;
     const int lane = lane_id();
     const int wave = wave_id();
     const int Hq = a->n_q_heads, Hkv = a->n_kv_heads;
@@ -364,53 +451,65 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const int s = (int)tile - g * S_;
     const int pos = a->pos, ncol = a->ncol, page_size = a->page_size;
     const int n_tok = pos + ncol;
-    const int T = (n_tok + S_ - 1) / S_;
+    // split length: a whole number of workgroup token slots, so that every
+    // wave instruction's TPI positions start TPI-aligned and sit in one page
+    const int T = ((n_tok + S_ - 1) / S_ + NS - 1) / NS * NS;
     const int t0 = s * T;
     const int t1 = min(t0 + T, n_tok);
-    const int slot = wave * SW + lane / LPT;
-    const int cidx = lane % LPT;
+    const int th = min(t1, pos);                    // history: [t0, th)
+    const int tl = lane / LPT;                      // token of this lane within an instruction
+    const int cidx = lane % LPT;                    // 16-byte slice of the row
+    const int nu = th > t0 ? (th - t0 + NS - 1) / NS : 0;   // units per wave
+    const int nch = (nu + NUB - 1) / NUB;
+    const bool resident = nch <= 2;                 // whole history stays in LDS
     const size_t layer_off = (size_t)layer * a->kv_layer_stride;
     const MBG_GLOBAL uint8_t* pool = gp(reinterpret_cast<const uint8_t*>(a->kv_pool));
     const MBG_GLOBAL int32_t* ptab = gp(a->page_table);
+    MBG_LDS uint8_t* ring = reinterpret_cast<MBG_LDS uint8_t*>(smem) + wave * kAttnWaveBytes;
 
-    auto kv_ptr = [&](int t, int kv) -> const MBG_GLOBAL uint4* {
+    auto row_ptr = [&](int t, int kv) -> const MBG_GLOBAL uint8_t* {
         const int lp = t / page_size;
         const int page = ptab[lp];
         const int sl = t - lp * page_size;
         const size_t el = layer_off + ((((size_t)page * 2 + kv) * Hkv + g) * page_size + sl) * HD;
-        return reinterpret_cast<const MBG_GLOBAL uint4*>(pool + el * EB + (size_t)cidx * 16);
+        return pool + el * EB + (size_t)cidx * 16;
     };
-
-    uint4 KA[CT], VA[CT], KB[CT], VB[CT];
-    // token of chunk element j of chunk ch: t0 + slot + NS * (ch * CT + j)
-    auto issue = [&](uint4 (&K)[CT], uint4 (&V)[CT], int ch, int te, int limit) {
+    auto tok_of = [&](int i) { return t0 + (i * kWaves + wave) * TPI + tl; };
+    const MBG_CONST int32_t* ptab_s = (const MBG_CONST int32_t*)a->page_table;
+    const size_t lane_off = (size_t)tl * HD * EB + (size_t)cidx * 16;
+    // Request chunk c of history into ring buffer b: NUB units, each one K and
+    // one V instruction.  A unit's TPI positions share a page, so its page is
+    // one scalar load (counted apart from the vector loads the waits count).
+    // Units past the history re-read the split's first unit, so every chunk
+    // is the same number of loads.
+    auto issue_chunk = [&](int c, int b) {
 #pragma unroll
-        for (int j = 0; j < CT; ++j) {
-            const int t = t0 + slot + NS * (ch * CT + j);
-            if (t < te && t < limit) {
-                K[j] = ld_stream_g(kv_ptr(t, 0));
-                V[j] = ld_stream_g(kv_ptr(t, 1));
-            } else {
-                K[j] = make_uint4(0, 0, 0, 0);
-                V[j] = make_uint4(0, 0, 0, 0);
-            }
+        for (int u = 0; u < NUB; ++u) {
+            int tb = t0 + ((c * NUB + u) * kWaves + wave) * TPI;
+            tb = __builtin_amdgcn_readfirstlane(tb < th ? tb : t0);
+            const int lp = tb / page_size;
+            const int page = ptab_s[lp];
+            const size_t el = layer_off + ((((size_t)page * 2) * Hkv + g) * page_size + (tb - lp * page_size)) * HD;
+            const size_t vstep = (size_t)Hkv * page_size * HD * EB;   // K -> V of the same page
+            const MBG_GLOBAL uint8_t* kp = pool + el * EB + lane_off;
+            MBG_LDS uint8_t* dst = ring + (b * NUB + u) * 2 * kUnitBytes;
+            lds_dma16(kp, (MBG_LDS void*)dst);
+            lds_dma16(kp + vstep, (MBG_LDS void*)(dst + kUnitBytes));
         }
     };
 
-    const bool empty = t0 >= t1;
-    // history (positions < pos) does not depend on this step: load it first
-    if (!empty) issue(KA, VA, 0, min(t1, pos + 1), pos);
+    if (nch > 0) issue_chunk(0, 0);
+    if (nch > 1) issue_chunk(1, 1);
     if (!wait_counter(a, wctr, wneed)) return false;
 
     const float qscale = a->attn_scale_log2;
     const float ksc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 0] : 1.f;
     const float vsc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 1] : 1.f;
-    lds_f32* red = smem;  // [kWaves][GQ][HD + 2]
+    lds_f32* red = reinterpret_cast<lds_f32*>(reinterpret_cast<MBG_LDS uint8_t*>(smem) + kAttnRingBytes);
     constexpr int stride = HD + 2;
+    const bool empty = t0 >= t1;
     for (int col = 0; col < ncol && !empty; ++col) {
         const int te = min(t1, pos + col + 1);
-        const int nlane0 = te > t0 ? (te - t0 + NS - 1) / NS : 0;  // tokens of slot 0
-        const int nch = (nlane0 + CT - 1) / CT;
         float q[GQ][EPC];
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
@@ -419,110 +518,70 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             for (int e = 0; e < EPC; ++e) q[h][e] = ldc(qp + e) * qscale;
         }
         if (col == 0) stamp(0);
-        float m[GQ], l[GQ], o[GQ][EPC];
-#pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            m[h] = -INFINITY;
-            l[h] = 0.f;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) o[h][e] = 0.f;
+        Lane st;
+        st.init();
+        if (col > 0 && !resident) {  // stream the history again for this column
+            __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // lgkmcnt(0): earlier ring reads are done
+            issue_chunk(0, 0);
+            if (nch > 1) issue_chunk(1, 1);
         }
-        if (col == 0) {
-            // complete chunk 0 with the positions >= pos written this step
+        for (int c = 0; c < nch; ++c) {
+            const int b = c & 1;
+            if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NUB));  // chunk c has landed
+            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            uint4 K[NUB], V[NUB];
+            bool valid[NUB];
 #pragma unroll
-            for (int j = 0; j < CT; ++j) {
-                const int t = t0 + slot + NS * j;
-                if (t >= pos && t < te) {
-                    KA[j] = ldc16(kv_ptr(t, 0));
-                    VA[j] = ldc16(kv_ptr(t, 1));
-                }
+            for (int u = 0; u < NUB; ++u) {
+                const MBG_LDS uint8_t* src = ring + (b * NUB + u) * 2 * kUnitBytes + lane * 16;
+                const u32x4 kv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src);
+                const u32x4 vv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src + kUnitBytes);
+                K[u] = make_uint4(kv4.x, kv4.y, kv4.z, kv4.w);
+                V[u] = make_uint4(vv4.x, vv4.y, vv4.z, vv4.w);
+                valid[u] = tok_of(c * NUB + u) < th;
             }
-        } else {
-            issue(KA, VA, 0, te, 0x7FFFFFFF);
+            st.template fold<NUB>(q, K, V, valid, ksc);
+            if (c + 2 < nch && (!resident || col + 1 == ncol)) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // lgkmcnt(0): this buffer's reads are done
+                issue_chunk(c + 2, b);
+            }
         }
-        auto compute = [&](const uint4 (&K)[CT], const uint4 (&V)[CT], int ch) {
-            float sc[CT][GQ];
-#pragma unroll
-            for (int j = 0; j < CT; ++j) {
-                float kf[EPC];
-                decode16<KVF>(K[j], 0u, kf);
-                const int t = t0 + slot + NS * (ch * CT + j);
-                const bool valid = t < te;
-#pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-                    for (int e = 0; e < EPC; e += 2) {
-                        p0 = fmaf(q[h][e], kf[e], p0);
-                        p1 = fmaf(q[h][e + 1], kf[e + 1], p1);
-                    }
-                    const float sv = group_sum<LPT>(p0 + p1) * ksc;
-                    sc[j][h] = valid ? sv : -INFINITY;
-                }
+        // positions written this step (at most ncol of them): wave 0, read coherently
+        if (wave == 0 && t1 > pos) {
+            const int tn = max(t0, pos) + tl;
+            uint4 K[1], V[1];
+            bool valid[1] = {tl < ncol && tn < te};
+            if (valid[0]) {
+                K[0] = ldc16(reinterpret_cast<const MBG_GLOBAL uint4*>(row_ptr(tn, 0)));
+                V[0] = ldc16(reinterpret_cast<const MBG_GLOBAL uint4*>(row_ptr(tn, 1)));
+            } else {
+                K[0] = make_uint4(0, 0, 0, 0);
+                V[0] = make_uint4(0, 0, 0, 0);
             }
-#pragma unroll
-            for (int h = 0; h < GQ; ++h) {
-                float cm = -INFINITY;
-#pragma unroll
-                for (int j = 0; j < CT; ++j) cm = fmaxf(cm, sc[j][h]);
-                const float mn = fmaxf(m[h], cm);
-                if (mn == -INFINITY) {  // no valid token yet: weights are 0, state unchanged
-#pragma unroll
-                    for (int j = 0; j < CT; ++j) sc[j][h] = 0.f;
-                    continue;
-                }
-                const float al = m[h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[h] - mn);
-                m[h] = mn;
-                l[h] *= al;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) o[h][e] *= al;
-#pragma unroll
-                for (int j = 0; j < CT; ++j) {
-                    sc[j][h] = sc[j][h] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(sc[j][h] - mn);
-                    l[h] += sc[j][h];
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < CT; ++j) {
-                float vf[EPC];
-                decode16<KVF>(V[j], 0u, vf);
-#pragma unroll
-                for (int h = 0; h < GQ; ++h) {
-                    const float p = sc[j][h];
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) o[h][e] = fmaf(p, vf[e], o[h][e]);
-                }
-            }
-        };
-        for (int ch = 0; ch < nch; ch += 2) {
-            if (ch + 1 < nch) issue(KB, VB, ch + 1, te, 0x7FFFFFFF);
-            compute(KA, VA, ch);
-            if (ch + 1 >= nch) break;
-            if (ch + 2 < nch) issue(KA, VA, ch + 2, te, 0x7FFFFFFF);
-            compute(KB, VB, ch + 1);
+            st.template fold<1>(q, K, V, valid, ksc);
         }
         if constexpr (KVF == F_FP8) {
 #pragma unroll
             for (int h = 0; h < GQ; ++h)
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) o[h][e] *= vsc;
+                for (int e = 0; e < EPC; ++e) st.o[h][e] *= vsc;
         }
         // merge the token slots of a wave (lanes with the same cidx)
 #pragma unroll
         for (int msk = LPT; msk < kWave; msk <<= 1) {
 #pragma unroll
             for (int h = 0; h < GQ; ++h) {
-                const float m2 = shfl_xor_f(m[h], msk);
-                const float l2 = shfl_xor_f(l[h], msk);
+                const float m2 = shfl_xor_f(st.m[h], msk);
+                const float l2 = shfl_xor_f(st.l[h], msk);
                 float mn, w1, w2;
-                merge_weights(m[h], m2, mn, w1, w2);
-                l[h] = l[h] * w1 + l2 * w2;
+                merge_weights(st.m[h], m2, mn, w1, w2);
+                st.l[h] = st.l[h] * w1 + l2 * w2;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) {
-                    const float o2 = shfl_xor_f(o[h][e], msk);
-                    o[h][e] = o[h][e] * w1 + o2 * w2;
+                    const float o2 = shfl_xor_f(st.o[h][e], msk);
+                    st.o[h][e] = st.o[h][e] * w1 + o2 * w2;
                 }
-                m[h] = mn;
+                st.m[h] = mn;
             }
         }
         // then the waves, through LDS, in wave order
@@ -531,10 +590,10 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             for (int h = 0; h < GQ; ++h) {
                 lds_f32* r = red + ((size_t)wave * GQ + h) * stride;
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) r[cidx * EPC + e] = o[h][e];
+                for (int e = 0; e < EPC; ++e) r[cidx * EPC + e] = st.o[h][e];
                 if (cidx == 0) {
-                    r[HD] = m[h];
-                    r[HD + 1] = l[h];
+                    r[HD] = st.m[h];
+                    r[HD + 1] = st.l[h];
                 }
             }
         }
@@ -566,11 +625,12 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         }
         __syncthreads();
     }
-
+    // a split with no history still has requested nothing; one with history
+    // has drained its ring above
     stamp(1);
     // arrival; the last split of this KV head combines all of them
     __shared__ int s_last;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if (threadIdx.x == 0) {
         release_before_signal();
@@ -587,18 +647,19 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const int nsv = min(S_, (n_tok + T - 1) / T);   // splits that wrote partials
     const MBG_GLOBAL float* part = gp(a->part);
     MBG_GLOBAL float* attn = gp(a->attn);
-    lds_f32* wts = smem;                               // [ncol][GQ][S]
-    lds_f32* inv = smem + 4 * GQ * 64;                 // [ncol][GQ]
+    lds_f32* wts = smem;                               // [ncol * GQ][64]: m, then weights
+    lds_f32* lsm = smem + 4 * GQ * 64;                 // [ncol * GQ][64]: l
+    lds_f32* tot = smem + 8 * GQ * 64;                 // [ncol * GQ]: weighted sum of l
     const int nw_ = ncol * GQ * nsv;
     for (int idx = threadIdx.x; idx < nw_; idx += kThreads) {
         const int ch = idx / nsv, sp = idx - ch * nsv;  // ch = col * GQ + h
         const int col = ch / GQ, h = ch - col * GQ;
-        wts[ch * 64 + sp] = ldc(part + (((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + HD);
-        inv[ch] = 0.f;
+        const MBG_GLOBAL float* r = part + (((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + HD;
+        wts[ch * 64 + sp] = ldc(r);
+        lsm[ch * 64 + sp] = ldc(r + 1);
     }
     __syncthreads();
     for (int ch = threadIdx.x; ch < ncol * GQ; ch += kThreads) {
-        const int col = ch / GQ, h = ch - col * GQ;
         float M = -INFINITY;
         for (int sp = 0; sp < nsv; ++sp) M = fmaxf(M, wts[ch * 64 + sp]);
         float Lsum = 0.f;
@@ -606,9 +667,9 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             const float ms = wts[ch * 64 + sp];
             const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
             wts[ch * 64 + sp] = w;
-            Lsum += w * ldc(part + (((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + HD + 1);
+            Lsum = fmaf(w, lsm[ch * 64 + sp], Lsum);
         }
-        inv[ch] = Lsum;
+        tot[ch] = Lsum;
     }
     __syncthreads();
     for (int idx = threadIdx.x; idx < ncol * GQ * HD; idx += kThreads) {
@@ -624,7 +685,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
 #pragma unroll
         for (int sp = 0; sp < 64; ++sp)
             if (sp < nsv) O = fmaf(wts[ch * 64 + sp], ov[sp], O);
-        stc(attn + (size_t)col * Hq * HD + (g * GQ + h) * HD + e, O / inv[ch]);
+        stc(attn + (size_t)col * Hq * HD + (g * GQ + h) * HD + e, O / tot[ch]);
     }
     release_counter(a, ctr_index(layer, PH_ATTN));
     return true;
@@ -813,7 +874,7 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
         __hip_atomic_fetch_max(keys + c, b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
     __shared__ int s_last;
-    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if (threadIdx.x == 0) {
         release_before_signal();
@@ -925,8 +986,8 @@ const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out) 
         if (v.qdim > kmax) kmax = v.qdim;
         if (v.moe_ffn > kmax) kmax = v.moe_ffn;
         const int xs_bytes = ncol * kmax * 4 + kWaves * kQkvRowsPerWave * ncol * 4;
-        const int red_bytes = kWaves * v.group * (v.head_dim + 2) * 4;
-        const int comb_bytes = (4 * v.group * 64 + 4 * v.group) * 4;
+        const int red_bytes = kAttnRingBytes + kWaves * v.group * (v.head_dim + 2) * 4;
+        const int comb_bytes = (8 * v.group * 64 + 4 * v.group) * 4;
         int m = xs_bytes > red_bytes ? xs_bytes : red_bytes;
         *lds_bytes_out = m > comb_bytes ? m : comb_bytes;
     }
