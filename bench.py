@@ -22,6 +22,28 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak, GB/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_dense2b_traffic.txt")
+
+
+def stored_traffic():
+    """HBM bytes per launch of the decode-step kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or
+    None when the summary is missing or was taken on other kernel sources."""
+    from memory_bound_gemv_amd.build import source_digest
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    fields = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                fields[k.strip()] = v.strip()
+    if fields.get("source_digest") != source_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(cfg, pos: int) -> tuple[int, int]:
@@ -182,7 +204,7 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": stored_traffic(),
         },
         "bytes_per_step": {"weights": wbytes, "kv_avg": round(kv_avg), "total": round(step_bytes)},
         "bound_tokens_s": round(PEAK_HBM_GBS * 1e9 / step_bytes, 1),

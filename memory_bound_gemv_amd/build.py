@@ -1,6 +1,7 @@
 """Compile the HIP library libmbg.so for gfx950 in-tree with hipcc."""
 from __future__ import annotations
 
+import hashlib
 import os
 import subprocess
 import sys
@@ -19,6 +20,22 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
 SOURCES = ["step.hip", "ops.hip", "api.cpp"]
+
+
+def source_digest() -> str:
+    """SHA-256 over the library's sources, the public header and the flags:
+    names the kernel build that a stored counter measurement belongs to."""
+    h = hashlib.sha256()
+    names = sorted(os.listdir(CSRC))
+    for n in names:
+        if n.endswith((".hip", ".cpp", ".h")):
+            h.update(n.encode())
+            with open(os.path.join(CSRC, n), "rb") as f:
+                h.update(f.read())
+    with open(os.path.join(INCLUDE, "mbg.h"), "rb") as f:
+        h.update(f.read())
+    h.update(" ".join(f for f in FLAGS if f not in (INCLUDE, CSRC)).encode())
+    return h.hexdigest()[:16]
 
 
 def _compile(src: str, extra) -> str:
