@@ -67,8 +67,8 @@ Plan make_plan(const mbg_config& c) {
     p.status = take(16);
     p.keys = take(8 * 4);
     p.n_ctr = L * PH_COUNT;
-    p.ctr = take(4 * p.n_ctr);
-    p.head_ctr = take(4 * L * (size_t)c.n_kv_heads);
+    p.ctr = take(4 * kLineU32 * kCtrLines * p.n_ctr);
+    p.head_ctr = take(4 * kLineU32 * L * (size_t)c.n_kv_heads);   // one line per (layer, KV head)
     p.zero_bytes = off;  // everything above starts at zero
     p.task_off = take(4 * (kMaxGrid + 1));
     p.max_tasks = (size_t)kMaxGrid * (8 * L + 1);

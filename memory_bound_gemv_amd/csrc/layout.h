@@ -41,6 +41,14 @@ struct Task {
 };
 constexpr uint32_t kNoWait = 0xFFFFFFFFu;
 
+// A dependency counter is kCtrLines separate 128-byte lines: a producer adds
+// to line (workgroup % kCtrLines) and a waiter sums all lines.  Same-address
+// atomics from hundreds of workgroups serialise at the memory side; spreading
+// them over lines keeps an all-to-all dependency point near two memory round
+// trips.
+constexpr uint32_t kCtrLines = 16;
+constexpr uint32_t kLineU32 = 32;
+
 struct LayerPtrs {
     const uint16_t* attn_norm;
     const uint16_t* ffn_norm;

@@ -112,42 +112,56 @@ __device__ __forceinline__ void release_before_signal() {
 #endif
 }
 
-// Wait until counter `idx` reaches epoch * need (mod 2^32).  Thread 0 polls;
-// the others wait at the barrier.  Returns false when the launch is aborting.
+// Wait until counter `idx` (the sum of its kCtrLines lines) reaches
+// epoch * need (mod 2^32).  Wave 0 polls, one line per lane plus the status
+// word in one load instruction; the other waves wait at the barrier.  Returns
+// false when the launch is aborting.
 __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
     __shared__ int s_ok;
-    if (threadIdx.x == 0) {
+    if (threadIdx.x < kWave) {
+        const int lane = threadIdx.x;
         int ok = 1;
         if (idx != kNoWait) {
             const uint32_t target = a->epoch * need;
-            const MBG_GLOBAL uint32_t* ctr = gp(a->ctr) + idx;
-            const MBG_GLOBAL uint32_t* st = gp(a->status);
+            const MBG_GLOBAL uint32_t* line = gp(a->ctr) + ((size_t)idx * kCtrLines + (lane & (kCtrLines - 1))) * kLineU32;
+            const MBG_GLOBAL uint32_t* src = lane == (int)kCtrLines ? gp(a->status) : line;
             const uint64_t t0 = wall_clock64();
-            while ((int32_t)(__hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - target) < 0) {
-                if (__hip_atomic_load(st, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = 0; break; }
+            while (true) {
+                uint32_t v = lane <= (int)kCtrLines ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
+                const uint32_t st = __builtin_amdgcn_readlane(v, kCtrLines);
+                if (lane >= (int)kCtrLines) v = 0u;
+#pragma unroll
+                for (int m = kCtrLines / 2; m >= 1; m >>= 1) v += (uint32_t)__shfl_xor((int)v, m, kWave);
+                const uint32_t sum = __builtin_amdgcn_readfirstlane(v);
+                if ((int32_t)(sum - target) >= 0) break;
+                if (st != 0u) { ok = 0; break; }
                 if (wall_clock64() - t0 > a->deadline_ticks) {
-                    latch_error(a->status, kStatusTimeout);
+                    if (lane == 0) latch_error(a->status, kStatusTimeout);
                     ok = 0;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(1);
             }
         }
-        if (ok) acquire_after_wait();
-        s_ok = ok;
-        s_twait = wall_clock64();
+        if (lane == 0) {
+            if (ok) acquire_after_wait();
+            s_ok = ok;
+            s_twait = wall_clock64();
+        }
     }
     __syncthreads();
     return s_ok != 0;
 }
 
-// Make this workgroup's stores visible at device scope, then count the task.
+// Make this workgroup's stores visible at device scope, then count the task
+// on this workgroup's line of the counter.
 __device__ __forceinline__ void release_counter(CArgs* a, uint32_t idx) {
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // vmcnt(0): this wave's stores have reached L2
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // vmcnt(0): this wave's stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
         release_before_signal();
-        __hip_atomic_fetch_add(gp(a->ctr) + idx, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        MBG_GLOBAL uint32_t* line = gp(a->ctr) + ((size_t)idx * kCtrLines + (blockIdx.x & (kCtrLines - 1))) * kLineU32;
+        __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -221,7 +235,7 @@ __device__ void load_plain(const float* src, lds_f32* xs) {
     __syncthreads();
 }
 
-__shared__ uint64_t s_stamp[2];  // trace: input loaded, stream finished
+__shared__ uint64_t s_stamp[4];  // trace: input loaded, stream finished, two op-specific points
 __device__ __forceinline__ void stamp(int k) {
     if (threadIdx.x == 0) s_stamp[k] = wall_clock64();
 }
@@ -546,6 +560,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
                 issue_chunk(c + 2, b);
             }
         }
+        if (col == 0) stamp(2);
         // positions written this step (at most ncol of them): wave 0, read coherently
         if (wave == 0 && t1 > pos) {
             const int tn = max(t0, pos) + tl;
@@ -634,7 +649,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     __syncthreads();
     if (threadIdx.x == 0) {
         release_before_signal();
-        const uint32_t old = __hip_atomic_fetch_add(gp(a->head_ctr) + layer * Hkv + g, 1u, __ATOMIC_RELAXED,
+        const uint32_t old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv + g) * kLineU32, 1u, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old + 1u == a->epoch * (uint32_t)S_);
         if (s_last) acquire_after_wait();
@@ -672,6 +687,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         tot[ch] = Lsum;
     }
     __syncthreads();
+    stamp(3);
     for (int idx = threadIdx.x; idx < ncol * GQ * HD; idx += kThreads) {
         const int ch = idx / HD;
         const int e = idx - ch * HD;
@@ -905,6 +921,7 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
     const MBG_CONST u32x4* tasks = (const MBG_CONST u32x4*)a->tasks;
     const uint32_t end = off[b + 1];
     MBG_GLOBAL unsigned long long* trace = a->trace ? gp(a->trace) : nullptr;
+    if (threadIdx.x == 0) s_stamp[2] = s_stamp[3] = 0;
     for (uint32_t ti = off[b]; ti < end; ++ti) {
         const u32x4 tv = tasks[ti];
         const Task tk{tv[0], tv[1], tv[2], tv[3]};
@@ -934,8 +951,10 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
             r[3] = s_stamp[1];
             r[4] = wall_clock64();
             r[5] = (unsigned long long)tk.op_layer | ((unsigned long long)tk.tile << 32);
-            r[6] = 0;
-            r[7] = 0;
+            r[6] = s_stamp[2];
+            r[7] = s_stamp[3];
+            s_stamp[2] = 0;
+            s_stamp[3] = 0;
         }
     }
 }
