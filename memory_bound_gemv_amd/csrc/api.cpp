@@ -77,7 +77,7 @@ Plan make_plan(const mbg_config& c) {
     p.inv_freq = take(8 * (size_t)(c.head_dim / 2));
     p.xres = take(4 * k * c.hidden);
     p.qbuf = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
-    p.part = take(4 * k * (size_t)c.n_q_heads * kMaxSplits * (c.head_dim + 2));
+    p.part = take(4 * k * (size_t)c.n_q_heads * kMaxSplits * (c.head_dim + 4));   // rows: o, m, l, 2 pad
     p.attn = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
     size_t hw = (size_t)c.ffn;
     const size_t moe_w = (size_t)(c.top_k + c.n_shared) * c.moe_ffn;
@@ -355,7 +355,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.tiles_lm = tiles_for(c.vocab);
     int S = G / c.n_kv_heads;
     S = std::max(1, std::min(S, kMaxSplits));
-    S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 32)));
+    S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 128)));   // >= ~128 positions per split
     a.attn_splits = S;
     const uint32_t tiles_attn = (uint32_t)(c.n_kv_heads * S);
 

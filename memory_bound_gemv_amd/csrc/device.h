@@ -9,6 +9,7 @@ namespace mbg {
 
 constexpr int kWave = 64;
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte streaming load (non-temporal: data read once per step).

@@ -101,6 +101,21 @@ __device__ __forceinline__ uint4 ldc16(const MBG_GLOBAL uint4* p) {
     return ld_g(p);
 #endif
 }
+// 16-byte device-coherent accesses: buffer instructions with the sc1 cache
+// policy, which is what a relaxed agent-scope atomic access of 4 bytes
+// compiles to on gfx950, four times wider.  Offsets are in bytes.
+constexpr int kCohAux = MBG_COHERENT ? 16 : 0;
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ f32x4 ldc4(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, kCohAux));
+}
+__device__ __forceinline__ void stc4(rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCohAux);
+}
+
 __device__ __forceinline__ void acquire_after_wait() {
 #if !MBG_COHERENT
     fence_acquire();
@@ -175,24 +190,32 @@ __device__ __forceinline__ int token_of(CArgs* a, int c) {
 }
 
 // xs[c][i] = src(c, i) / sqrt(mean_i src(c, i)^2 + eps) * gain[i], c < NC,
-// i < H; sums of squares in a fixed order (per thread, then the wave tree,
+// i < H, where src4(c, j) returns elements 4j .. 4j+3 of column c.  Sums of
+// squares in a fixed order (per thread over its quads, then the wave tree,
 // then the four waves in order).
-template <int NC, int H, class Src>
-__device__ void load_normed(CArgs* a, Src src, const uint16_t* gain, lds_f32* xs) {
+template <int NC, int H, class Src4>
+__device__ void load_normed(CArgs* a, Src4 src4, const uint16_t* gain, lds_f32* xs) {
     __shared__ float red[kWaves * 4];
-    static_assert(H % kThreads == 0, "hidden size");
-    constexpr int PER = H / kThreads;
+    static_assert(H % 4 == 0, "hidden size");
+    constexpr int NV = H / 4;
+    constexpr int PER = (NV + kThreads - 1) / kThreads;
     const int tid = threadIdx.x;
-    const MBG_GLOBAL uint16_t* g = gp(gain);
-    float v[NC][PER];
+    const MBG_GLOBAL u32x2* g2 = gp(reinterpret_cast<const u32x2*>(gain));
+    f32x4 v[NC][PER];
     float ss[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         ss[c] = 0.f;
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            v[c][p] = src(c, tid + kThreads * p);
-            ss[c] = fmaf(v[c][p], v[c][p], ss[c]);
+            const int j = tid + kThreads * p;
+            if (NV % kThreads == 0 || j < NV) {
+                v[c][p] = src4(c, j);
+                ss[c] = fmaf(v[c][p][0], v[c][p][0], ss[c]);
+                ss[c] = fmaf(v[c][p][1], v[c][p][1], ss[c]);
+                ss[c] = fmaf(v[c][p][2], v[c][p][2], ss[c]);
+                ss[c] = fmaf(v[c][p][3], v[c][p][3], ss[c]);
+            }
         }
     }
 #pragma unroll
@@ -207,32 +230,52 @@ __device__ void load_normed(CArgs* a, Src src, const uint16_t* gain, lds_f32* xs
         const float r = 1.0f / sqrtf(tot / (float)H + a->rms_eps);
 #pragma unroll
         for (int p = 0; p < PER; ++p) {
-            const int i = tid + kThreads * p;
-            xs[c * H + i] = v[c][p] * r * bf16_to_f32(g[i]);
+            const int j = tid + kThreads * p;
+            if (NV % kThreads == 0 || j < NV) {
+                const u32x2 gg = g2[j];
+                f32x4 o;
+                o[0] = v[c][p][0] * r * bf16_lo(gg.x);
+                o[1] = v[c][p][1] * r * bf16_hi(gg.x);
+                o[2] = v[c][p][2] * r * bf16_lo(gg.y);
+                o[3] = v[c][p][3] * r * bf16_hi(gg.y);
+                *reinterpret_cast<MBG_LDS f32x4*>(xs + c * H + 4 * j) = o;
+            }
         }
     }
     __syncthreads();
 }
 
-// xs[0 .. NC*K) = src[...]: all loads issued before any LDS write (one
-// round trip of latency, not one per element group).
+// xs[0 .. NC*K) = src[...] (float32, written this step): all 16-byte
+// coherent loads issued before any LDS write.
 template <int NC, int K>
 __device__ void load_plain(const float* src, lds_f32* xs) {
-    constexpr int N = NC * K;
-    constexpr int PER = (N + kThreads - 1) / kThreads;
-    const MBG_GLOBAL float* sp = gp(src);
-    float v[PER];
+    static_assert(K % 4 == 0, "row length");
+    constexpr int NV = NC * K / 4;
+    constexpr int PER = (NV + kThreads - 1) / kThreads;
+    const rsrc_t r = make_rsrc(src);
+    f32x4 v[PER];
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-        const int i = threadIdx.x + kThreads * p;
-        if (N % kThreads == 0 || i < N) v[p] = ldc(sp + i);
+        const int j = threadIdx.x + kThreads * p;
+        if (NV % kThreads == 0 || j < NV) v[p] = ldc4(r, 16u * j);
     }
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-        const int i = threadIdx.x + kThreads * p;
-        if (N % kThreads == 0 || i < N) xs[i] = v[p];
+        const int j = threadIdx.x + kThreads * p;
+        if (NV % kThreads == 0 || j < NV) *reinterpret_cast<MBG_LDS f32x4*>(xs + 4 * j) = v[p];
     }
     __syncthreads();
+}
+
+// Four BF16 values (8 bytes) as float32.
+__device__ __forceinline__ f32x4 bf16x4(const MBG_GLOBAL u32x2* p) {
+    const u32x2 u = *p;
+    f32x4 o;
+    o[0] = bf16_lo(u.x);
+    o[1] = bf16_hi(u.x);
+    o[2] = bf16_lo(u.y);
+    o[3] = bf16_hi(u.y);
+    return o;
 }
 
 __shared__ uint64_t s_stamp[4];  // trace: input loaded, stream finished, two op-specific points
@@ -277,11 +320,12 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
         int tok[NC];
 #pragma unroll
         for (int c = 0; c < NC; ++c) tok[c] = token_of(a, c);
-        const MBG_GLOBAL uint16_t* emb = gp(a->embed);
-        load_normed<NC, H>(a, [&](int c, int i) { return bf16_to_f32(emb[(size_t)tok[c] * H + i]); }, L->attn_norm, xs);
+        const MBG_GLOBAL u32x2* emb = gp(reinterpret_cast<const u32x2*>(a->embed));
+        load_normed<NC, H>(a, [&](int c, int j) { return bf16x4(emb + (size_t)tok[c] * (H / 4) + j); }, L->attn_norm,
+                           xs);
     } else {
-        const MBG_GLOBAL float* x = gp(a->xres);
-        load_normed<NC, H>(a, [&](int c, int i) { return ldc(x + c * H + i); }, L->attn_norm, xs);
+        const rsrc_t x = make_rsrc(a->xres);
+        load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, L->attn_norm, xs);
     }
     stamp(0);
     // row sums -> per-wave LDS slots; RoPE and the cache write run after the stream
@@ -432,18 +476,30 @@ struct AttnLane {
     }
 };
 
-// Attention LDS use: per wavefront a ring of 2 buffers x kAttnUnits units;
-// a unit is one wave instruction's worth of K rows (1 KiB) plus the same for
-// V.  The cross-wave merge area follows the rings.
-constexpr int kAttnUnits = 8;
+// Attention LDS use: per wavefront a ring of kAttnBufs buffers of
+// kAttnUnits units; a unit is one wave instruction's worth of K rows (1 KiB)
+// plus the same for V.  The cross-wave merge area follows the rings.
+constexpr int kAttnUnits = 4;
+constexpr int kAttnBufs = 4;
 constexpr int kUnitBytes = kWave * 16;
-constexpr int kAttnWaveBytes = 2 * kAttnUnits * 2 * kUnitBytes;
+constexpr int kAttnWaveBytes = kAttnBufs * kAttnUnits * 2 * kUnitBytes;
 constexpr int kAttnRingBytes = kWaves * kAttnWaveBytes;
+// A split's partial result row: o[HD], m, l and two pad words (16-byte rows).
+constexpr int kPartPad = 4;
+
+// Wait until at most k ring chunks (2 * kAttnUnits loads each) are in flight.
+__device__ __forceinline__ void wait_chunks(int k) {
+    static_assert(6 * kAttnUnits < 64, "vmcnt range");
+    if (k <= 0) __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    else if (k == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kAttnUnits));
+    else if (k == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * kAttnUnits));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(6 * kAttnUnits));
+}
 
 // One (KV head, split) task: split-KV attention for the GQ query heads that
 // share KV head g, over positions [t0, t1) of the split, for every column of
 // the window.  History (positions < pos) streams straight from HBM into the
-// wave's LDS ring (global_load_lds_dwordx4); the first two ring buffers are
+// wave's LDS ring (global_load_lds_dwordx4); up to kAttnBufs chunks are
 // requested before the task waits for this step's q and new K/V.
 template <int NC, class S>
 __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
@@ -454,8 +510,10 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     constexpr int EPC = 16 / EB;             // elements per lane
     constexpr int TPI = kWave / LPT;         // tokens per wave instruction
     constexpr int NS = kWaves * TPI;         // token slots per workgroup
-    constexpr int NUB = kAttnUnits;
+    constexpr int NUB = kAttnUnits, NB = kAttnBufs;
+    constexpr int stride = HD + kPartPad;
     static_assert(LPT == 4 || LPT == 8 || LPT == 16, "row layout");
+    static_assert(EPC % 4 == 0, "lane slice");
     using Lane = AttnLane<GQ, EPC, LPT, KVF>;
     const int lane = lane_id();
     const int wave = wave_id();
@@ -475,7 +533,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const int cidx = lane % LPT;                    // 16-byte slice of the row
     const int nu = th > t0 ? (th - t0 + NS - 1) / NS : 0;   // units per wave
     const int nch = (nu + NUB - 1) / NUB;
-    const bool resident = nch <= 2;                 // whole history stays in LDS
+    const bool resident = nch <= NB;                // whole history stays in LDS
     const size_t layer_off = (size_t)layer * a->kv_layer_stride;
     const MBG_GLOBAL uint8_t* pool = gp(reinterpret_cast<const uint8_t*>(a->kv_pool));
     const MBG_GLOBAL int32_t* ptab = gp(a->page_table);
@@ -512,37 +570,40 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         }
     };
 
-    if (nch > 0) issue_chunk(0, 0);
-    if (nch > 1) issue_chunk(1, 1);
+    const int npre = min(nch, NB);
+    for (int c = 0; c < npre; ++c) issue_chunk(c, c);
     if (!wait_counter(a, wctr, wneed)) return false;
 
     const float qscale = a->attn_scale_log2;
     const float ksc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 0] : 1.f;
     const float vsc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 1] : 1.f;
     lds_f32* red = reinterpret_cast<lds_f32*>(reinterpret_cast<MBG_LDS uint8_t*>(smem) + kAttnRingBytes);
-    constexpr int stride = HD + 2;
+    const rsrc_t rq = make_rsrc(a->qbuf);
+    const rsrc_t rp = make_rsrc(a->part);
     const bool empty = t0 >= t1;
     for (int col = 0; col < ncol && !empty; ++col) {
         const int te = min(t1, pos + col + 1);
         float q[GQ][EPC];
 #pragma unroll
         for (int h = 0; h < GQ; ++h) {
-            const MBG_GLOBAL float* qp = gp(a->qbuf) + ((size_t)col * Hq + g * GQ + h) * HD + cidx * EPC;
+            const uint32_t qo = (uint32_t)((((size_t)col * Hq + g * GQ + h) * HD + cidx * EPC) * 4);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) q[h][e] = ldc(qp + e) * qscale;
+            for (int e = 0; e < EPC; e += 4) {
+                const f32x4 t = ldc4(rq, qo + 4u * e);
+#pragma unroll
+                for (int k = 0; k < 4; ++k) q[h][e + k] = t[k] * qscale;
+            }
         }
         if (col == 0) stamp(0);
         Lane st;
         st.init();
         if (col > 0 && !resident) {  // stream the history again for this column
-            __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // lgkmcnt(0): earlier ring reads are done
-            issue_chunk(0, 0);
-            if (nch > 1) issue_chunk(1, 1);
+            __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // earlier ring reads are done
+            for (int c = 0; c < npre; ++c) issue_chunk(c, c);
         }
         for (int c = 0; c < nch; ++c) {
-            const int b = c & 1;
-            if (c + 1 < nch) __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NUB));  // chunk c has landed
-            else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            const int b = c & (NB - 1);
+            wait_chunks(min(nch - 1 - c, NB - 1));        // chunk c has landed
             uint4 K[NUB], V[NUB];
             bool valid[NUB];
 #pragma unroll
@@ -555,9 +616,9 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
                 valid[u] = tok_of(c * NUB + u) < th;
             }
             st.template fold<NUB>(q, K, V, valid, ksc);
-            if (c + 2 < nch && (!resident || col + 1 == ncol)) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // lgkmcnt(0): this buffer's reads are done
-                issue_chunk(c + 2, b);
+            if (c + NB < nch) {
+                __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // this buffer's reads are done
+                issue_chunk(c + NB, b);
             }
         }
         if (col == 0) stamp(2);
@@ -629,19 +690,28 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
                     for (int e = 0; e < EPC; ++e) O[e] = O[e] * w1 + r[cidx * EPC + e] * w2;
                     M = mn;
                 }
-                MBG_GLOBAL float* dst = gp(a->part) + (((size_t)col * Hq + g * GQ + h) * S_ + s) * stride;
+                const uint32_t row = (uint32_t)((((size_t)col * Hq + g * GQ + h) * S_ + s) * stride * 4);
 #pragma unroll
-                for (int e = 0; e < EPC; ++e) stc(dst + cidx * EPC + e, O[e]);
+                for (int e = 0; e < EPC; e += 4) {
+                    f32x4 t;
+                    t[0] = O[e];
+                    t[1] = O[e + 1];
+                    t[2] = O[e + 2];
+                    t[3] = O[e + 3];
+                    stc4(rp, row + 4u * (cidx * EPC + e), t);
+                }
                 if (cidx == 0) {
-                    stc(dst + HD, M);
-                    stc(dst + HD + 1, Ls);
+                    f32x4 t;
+                    t[0] = M;
+                    t[1] = Ls;
+                    t[2] = 0.f;
+                    t[3] = 0.f;
+                    stc4(rp, row + 4u * HD, t);
                 }
             }
         }
         __syncthreads();
     }
-    // a split with no history still has requested nothing; one with history
-    // has drained its ring above
     stamp(1);
     // arrival; the last split of this KV head combines all of them
     __shared__ int s_last;
@@ -649,32 +719,45 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     __syncthreads();
     if (threadIdx.x == 0) {
         release_before_signal();
-        const uint32_t old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv + g) * kLineU32, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv + g) * kLineU32, 1u,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old + 1u == a->epoch * (uint32_t)S_);
         if (s_last) acquire_after_wait();
     }
     __syncthreads();
     if (!s_last) return true;
     // Combine: softmax over [0, pos + col] = weights exp2(m_s - M) on the
-    // split partials, normalised by their weighted sum.  All loads of a stage
-    // are issued before any is used.
+    // split partials, normalised by their weighted sum.
     const int nsv = min(S_, (n_tok + T - 1) / T);   // splits that wrote partials
-    const MBG_GLOBAL float* part = gp(a->part);
-    MBG_GLOBAL float* attn = gp(a->attn);
-    lds_f32* wts = smem;                               // [ncol * GQ][64]: m, then weights
-    lds_f32* lsm = smem + 4 * GQ * 64;                 // [ncol * GQ][64]: l
-    lds_f32* tot = smem + 8 * GQ * 64;                 // [ncol * GQ]: weighted sum of l
-    const int nw_ = ncol * GQ * nsv;
-    for (int idx = threadIdx.x; idx < nw_; idx += kThreads) {
-        const int ch = idx / nsv, sp = idx - ch * nsv;  // ch = col * GQ + h
-        const int col = ch / GQ, h = ch - col * GQ;
-        const MBG_GLOBAL float* r = part + (((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + HD;
-        wts[ch * 64 + sp] = ldc(r);
-        lsm[ch * 64 + sp] = ldc(r + 1);
+    const int nch_ = ncol * GQ;                      // (column, head) rows
+    lds_f32* wts = smem;                             // [4 * GQ][64]: m, then weights
+    lds_f32* lsm = smem + 4 * GQ * 64;               // [4 * GQ][64]: l
+    lds_f32* tot = smem + 8 * GQ * 64;               // [4 * GQ]: weighted sum of l
+    lds_f32* accl = tot + 4 * GQ;                    // [kThreads][4]: group partial sums
+    // stage 1: (m, l) of every (row, split), eight loads per thread in flight
+    const int nml = nch_ * nsv;
+    for (int i0 = 0; i0 < nml; i0 += 8 * kThreads) {
+        f32x4 t[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int idx = min(i0 + k * kThreads + (int)threadIdx.x, nml - 1);
+            const int ch = idx / nsv, sp = idx - ch * nsv;
+            const int col = ch / GQ, h = ch - col * GQ;
+            t[k] = ldc4(rp, (uint32_t)(((((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + HD) * 4));
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int idx = i0 + k * kThreads + (int)threadIdx.x;
+            if (idx < nml) {
+                const int ch = idx / nsv, sp = idx - ch * nsv;
+                wts[ch * 64 + sp] = t[k][0];
+                lsm[ch * 64 + sp] = t[k][1];
+            }
+        }
     }
     __syncthreads();
-    for (int ch = threadIdx.x; ch < ncol * GQ; ch += kThreads) {
+    // stage 2: per row, the merge weights in split order
+    for (int ch = threadIdx.x; ch < nch_; ch += kThreads) {
         float M = -INFINITY;
         for (int sp = 0; sp < nsv; ++sp) M = fmaxf(M, wts[ch * 64 + sp]);
         float Lsum = 0.f;
@@ -688,20 +771,55 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     }
     __syncthreads();
     stamp(3);
-    for (int idx = threadIdx.x; idx < ncol * GQ * HD; idx += kThreads) {
-        const int ch = idx / HD;
-        const int e = idx - ch * HD;
+    // stage 3: weighted sum of the partial o rows.  A thread owns one 16-byte
+    // slice of a row and every ng-th split; ng thread groups then add up in
+    // group order.
+    constexpr int HDV = HD / 4;
+    const int pairs = nch_ * HDV;
+    const int fit = kThreads / pairs;
+    const int ng = fit >= 8 ? 8 : fit >= 4 ? 4 : fit >= 2 ? 2 : 1;
+    const int tpg = kThreads / ng;
+    const int grp = (int)threadIdx.x / tpg, pl = (int)threadIdx.x - grp * tpg;
+    const rsrc_t ra = make_rsrc(a->attn);
+    for (int base = 0; base < pairs; base += tpg) {
+        const int pr = base + pl;
+        const int prc = min(pr, pairs - 1);
+        const int ch = prc / HDV, vec = prc - ch * HDV;
         const int col = ch / GQ, h = ch - col * GQ;
-        const MBG_GLOBAL float* base = part + ((size_t)col * Hq + g * GQ + h) * S_ * stride + e;
-        float ov[64];
+        const size_t row0 = ((size_t)col * Hq + g * GQ + h) * S_;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int i0 = grp; i0 < nsv; i0 += 8 * ng) {
+            f32x4 v[8];
 #pragma unroll
-        for (int sp = 0; sp < 64; ++sp)
-            if (sp < nsv) ov[sp] = ldc(base + (size_t)sp * stride);
-        float O = 0.f;
+            for (int k = 0; k < 8; ++k) {
+                const int sp = min(i0 + k * ng, nsv - 1);
+                v[k] = ldc4(rp, (uint32_t)(((row0 + sp) * stride + vec * 4) * 4));
+            }
 #pragma unroll
-        for (int sp = 0; sp < 64; ++sp)
-            if (sp < nsv) O = fmaf(wts[ch * 64 + sp], ov[sp], O);
-        stc(attn + (size_t)col * Hq * HD + (g * GQ + h) * HD + e, O / tot[ch]);
+            for (int k = 0; k < 8; ++k) {
+                const int sp = i0 + k * ng;
+                if (sp < nsv) {
+                    const float w = wts[ch * 64 + sp];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) acc[e] = fmaf(w, v[k][e], acc[e]);
+                }
+            }
+        }
+        *reinterpret_cast<MBG_LDS f32x4*>(accl + 4 * threadIdx.x) = acc;
+        __syncthreads();
+        if (grp == 0 && pr < pairs) {
+            f32x4 sum = *reinterpret_cast<const MBG_LDS f32x4*>(accl + 4 * pl);
+            for (int q = 1; q < ng; ++q) {
+                const f32x4 o = *reinterpret_cast<const MBG_LDS f32x4*>(accl + 4 * (q * tpg + pl));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) sum[e] += o[e];
+            }
+            const float tt = tot[ch];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) sum[e] = sum[e] / tt;
+            stc4(ra, (uint32_t)((((size_t)col * Hq + g * GQ + h) * HD + vec * 4) * 4), sum);
+        }
+        __syncthreads();
     }
     release_counter(a, ctr_index(layer, PH_ATTN));
     return true;
@@ -771,8 +889,8 @@ __device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t til
     typename RS::Buf A, B;
     st.issue(A, 0, rowf);
     if (!wait_counter(a, wctr, wneed)) return false;
-    const MBG_GLOBAL float* x = gp(a->xres);
-    load_normed<NC, H>(a, [&](int c, int i) { return ldc(x + c * H + i); }, L->ffn_norm, xs);
+    const rsrc_t x = make_rsrc(a->xres);
+    load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, L->ffn_norm, xs);
     stamp(0);
     MBG_GLOBAL float* hb = gp(a->hbuf);
     float gate[NC];
@@ -856,8 +974,8 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     typename RS::Buf A, B;
     st.issue(A, 0, rowf);
     if (!wait_counter(a, wctr, wneed)) return false;
-    const MBG_GLOBAL float* x = gp(a->xres);
-    load_normed<NC, H>(a, [&](int c, int i) { return ldc(x + c * H + i); }, a->final_norm, xs);
+    const rsrc_t x = make_rsrc(a->xres);
+    load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, a->final_norm, xs);
     stamp(0);
     unsigned long long best[NC];
 #pragma unroll
@@ -1005,8 +1123,8 @@ const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out) 
         if (v.qdim > kmax) kmax = v.qdim;
         if (v.moe_ffn > kmax) kmax = v.moe_ffn;
         const int xs_bytes = ncol * kmax * 4 + kWaves * kQkvRowsPerWave * ncol * 4;
-        const int red_bytes = kAttnRingBytes + kWaves * v.group * (v.head_dim + 2) * 4;
-        const int comb_bytes = (8 * v.group * 64 + 4 * v.group) * 4;
+        const int red_bytes = kAttnRingBytes + kWaves * v.group * (v.head_dim + kPartPad) * 4;
+        const int comb_bytes = (8 * v.group * 64 + 4 * v.group) * 4 + kThreads * 16;
         int m = xs_bytes > red_bytes ? xs_bytes : red_bytes;
         *lds_bytes_out = m > comb_bytes ? m : comb_bytes;
     }
