@@ -16,6 +16,8 @@ TEST INFRASTRUCTURE: see the package docstring.
 """
 from __future__ import annotations
 
+import os
+
 import numpy as np
 
 # --------------------------------------------------------------------------
@@ -115,6 +117,79 @@ def f32_to_fp8e4m3(x) -> np.ndarray:
     code = np.where(nan, 0x7F, code)
     code = code | np.where(sign, 0x80, 0)
     return code.astype(np.uint8)
+
+
+# Bulk forms of the two FP8 functions above, for caches of hundreds of
+# millions of values.  They compute exactly the same function:
+#   * decoding looks the code up in the 256 values fp8e4m3_to_f64 gives;
+#   * encoding looks up the code that f32_to_fp8e4m3 gives for a binary32
+#     with the same top 13 bits (sign, exponent, 3 mantissa bits, the next
+#     bit) and the same "any lower bit set" flag.  Those 14 bits decide the
+#     result: E4M3FN keeps at most 3 mantissa bits, so rounding to nearest
+#     even needs the kept bits, the next one and whether anything below is
+#     non-zero; at smaller exponents the rounding point only moves up into
+#     the top 13 bits; NaN and infinity differ in the mantissa, which the
+#     14 bits also tell apart.
+
+
+def _fp8_tables():
+    global _FP8_ENC, _FP8_DEC
+    if _FP8_ENC is None:
+        top = np.arange(1 << 13, dtype=np.uint32) << 19
+        enc = np.empty((1 << 13, 2), dtype=np.uint8)
+        enc[:, 0] = f32_to_fp8e4m3(top.view(np.float32))
+        enc[:, 1] = f32_to_fp8e4m3((top | np.uint32(1)).view(np.float32))
+        _FP8_ENC = enc.reshape(-1)
+        _FP8_DEC = fp8e4m3_to_f64(np.arange(256, dtype=np.uint8))
+    return _FP8_ENC, _FP8_DEC
+
+
+_FP8_ENC = None
+_FP8_DEC = None
+
+
+def _chunked(fn, x: np.ndarray, out_dtype, chunk: int = 1 << 22) -> np.ndarray:
+    flat = np.ascontiguousarray(x).reshape(-1)
+    out = np.empty(flat.shape, dtype=out_dtype)
+    if flat.size <= chunk:
+        out[:] = fn(flat)
+        return out.reshape(np.shape(x))
+    from concurrent.futures import ThreadPoolExecutor
+    starts = range(0, flat.size, chunk)
+
+    def run(i):
+        out[i:i + chunk] = fn(flat[i:i + chunk])
+
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        list(ex.map(run, starts))
+    return out.reshape(np.shape(x))
+
+
+def f32_to_fp8e4m3_bulk(x) -> np.ndarray:
+    """f32_to_fp8e4m3 by table, for large arrays."""
+    enc, _ = _fp8_tables()
+
+    def one(a):
+        b = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+        return enc[((b >> np.uint32(19)) << np.uint32(1)) | ((b & np.uint32(0x7FFFF)) != 0)]
+
+    return _chunked(one, np.asarray(x, dtype=np.float32), np.uint8)
+
+
+def fp8e4m3_to_f64_bulk(codes, scale=None) -> np.ndarray:
+    """fp8e4m3_to_f64 by table, for large arrays; optionally times `scale`
+    (broadcast against the codes' trailing axes)."""
+    _, dec = _fp8_tables()
+    c = np.asarray(codes, dtype=np.uint8)
+    if scale is None:
+        return _chunked(lambda a: dec[a], c, np.float64)
+    sc = np.broadcast_to(np.asarray(scale, dtype=np.float64), c.shape[-2:])
+
+    def one_row_block(a):
+        return (dec[a].reshape(-1, *c.shape[-2:]) * sc).reshape(-1)
+
+    per = int(np.prod(c.shape[-2:]))
+    return _chunked(one_row_block, c, np.float64, chunk=max(per, (1 << 22) // per * per))
 
 
 # --------------------------------------------------------------------------

@@ -192,17 +192,30 @@ class OracleCache:
                 y = (np.asarray(src, dtype=np.float64).astype(np.float32) / sc).astype(np.float32)
                 dst[pos] = codecs.f32_to_fp8e4m3(y)
 
+    def prefill_f32(self, layer: int, pos0: int, k: np.ndarray, v: np.ndarray) -> None:
+        """Store float32 K/V rows [n][Hkv][d] at positions pos0 .. pos0+n-1,
+        rounded to the cache format as `store` does (bulk form)."""
+        n = k.shape[0]
+        if self.kv_dtype == "bf16":
+            self.k[layer][pos0:pos0 + n] = codecs.f32_to_bf16(np.asarray(k, dtype=np.float32))
+            self.v[layer][pos0:pos0 + n] = codecs.f32_to_bf16(np.asarray(v, dtype=np.float32))
+            return
+        for which, src, dst in ((0, k, self.k[layer]), (1, v, self.v[layer])):
+            sc = self.scales[layer, :, which].astype(np.float32)[None, :, None]
+            y = (np.asarray(src, dtype=np.float32) / sc).astype(np.float32)
+            dst[pos0:pos0 + n] = codecs.f32_to_fp8e4m3_bulk(y)
+
     def read(self, layer: int, upto: int, dtype=np.float64):
         """Dequantised K, V for positions [0, upto), [T][Hkv][d]."""
         if self.kv_dtype == "bf16":
             k = codecs.bf16_to_f64(self.k[layer][:upto])
             v = codecs.bf16_to_f64(self.v[layer][:upto])
         else:
-            sk = self.scales[layer, :, 0].astype(np.float64)[None, :, None]
-            sv = self.scales[layer, :, 1].astype(np.float64)[None, :, None]
-            k = codecs.fp8e4m3_to_f64(self.k[layer][:upto]) * sk
-            v = codecs.fp8e4m3_to_f64(self.v[layer][:upto]) * sv
-        return k.astype(dtype), v.astype(dtype)
+            sk = self.scales[layer, :, 0].astype(np.float64)[:, None]
+            sv = self.scales[layer, :, 1].astype(np.float64)[:, None]
+            k = codecs.fp8e4m3_to_f64_bulk(self.k[layer][:upto], sk)
+            v = codecs.fp8e4m3_to_f64_bulk(self.v[layer][:upto], sv)
+        return k.astype(dtype, copy=False), v.astype(dtype, copy=False)
 
 
 # ---------------------------------------------------------------------------

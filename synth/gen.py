@@ -10,6 +10,9 @@ Seeds (root seed 0 for weights):
     (truncation: a way to draw BF16 numbers, not the decode path's rounding);
   * prompt token ids: seed 1, uniform over [0, vocab);
   * K/V prefill: seed 2, N(0, 1) per (layer, K or V), BF16 by truncation;
+    for a float32 prefill of hundreds of thousands of positions (the
+    long-context FP8 cache), N(0, 1) drawn on the GPU by torch's generator,
+    seeded per (seed 2, layer, K or V, block of KV_BLOCK positions);
   * page-table shuffle: seed 3, a uniform permutation of the physical pages;
   * LM-head input vectors: seed 4, float32 N(0, 1);
   * MXFP4 expert codes and scales: a counter-based integer hash (SplitMix64,
@@ -150,6 +153,37 @@ def kv_prefill_bf16(cfg: DecodeConfig, layer: int) -> tuple:
         x = _rng(KV_SEED, layer, kv).standard_normal(int(np.prod(shp)), dtype=np.float32)
         out.append(_f32_to_bf16_bits_trunc(x).reshape(shp))
     return out[0], out[1]
+
+
+KV_BLOCK = 8192
+
+
+def _block_seed(*words: int) -> int:
+    return int(np.random.SeedSequence(list(words)).generate_state(1, np.uint64)[0] & np.uint64(2**63 - 1))
+
+
+def kv_prefill_f32_device(cfg: DecodeConfig, layer: int, kv: int, start: int, n: int, device):
+    """float32 N(0, 1) rows [n][n_kv_heads][head_dim] of K (kv = 0) or V
+    (kv = 1) for positions [start, start + n) of `layer`, as a torch tensor
+    on `device`.
+
+    Positions are drawn in blocks of KV_BLOCK, each from torch's generator on
+    that device seeded with (KV_SEED, layer, kv, block), so any range can be
+    drawn without the ones before it and both sides of a comparison draw the
+    same numbers.
+    """
+    import torch
+    shp = (cfg.n_kv_heads, cfg.head_dim)
+    out = torch.empty((n, *shp), dtype=torch.float32, device=device)
+    if n == 0:
+        return out
+    for b in range(start // KV_BLOCK, (start + n - 1) // KV_BLOCK + 1):
+        g = torch.Generator(device=device)
+        g.manual_seed(_block_seed(KV_SEED, layer, kv, b))
+        blk = torch.randn((KV_BLOCK, *shp), generator=g, device=device, dtype=torch.float32)
+        lo, hi = max(start, b * KV_BLOCK), min(start + n, (b + 1) * KV_BLOCK)
+        out[lo - start:hi - start] = blk[lo - b * KV_BLOCK:hi - b * KV_BLOCK]
+    return out
 
 
 def page_table(cfg: DecodeConfig, shuffled: bool | None = None) -> np.ndarray:

@@ -50,12 +50,42 @@ def check_argmax(gpu_idx: int, gpu_logits: np.ndarray, ref: np.ndarray, what="")
     return False
 
 
-def build_dense(cfg, shuffled=None, kv_dtype="bf16", kv_scales=None, k_max=None, host=None):
-    """(DeviceModel, OracleModel, OracleCache) with identical weights and prefill."""
-    import torch  # noqa: F401
+FP8_MAX = 448.0
+
+
+def fp8_kv_scales(cfg, block: int = 1 << 16):
+    """Per (layer, KV head, K or V) power-of-two scale 2^ceil(log2(amax / 448))
+    over the float32 prefill samples (float32 [L][Hkv][2])."""
+    import torch
+    sc = np.ones((cfg.n_layers, cfg.n_kv_heads, 2), dtype=np.float32)
+    if not cfg.prefill:
+        return sc
+    for li in range(cfg.n_layers):
+        for kv in (0, 1):
+            am = torch.zeros(cfg.n_kv_heads, dtype=torch.float32, device="cuda")
+            for p0 in range(0, cfg.prefill, block):
+                n = min(block, cfg.prefill - p0)
+                x = gen.kv_prefill_f32_device(cfg, li, kv, p0, n, "cuda")
+                am = torch.maximum(am, x.abs().amax(dim=(0, 2)))
+            a = am.double().cpu().numpy()
+            sc[li, :, kv] = np.exp2(np.ceil(np.log2(a / FP8_MAX))).astype(np.float32)
+    return sc
+
+
+def build_dense(cfg, shuffled=None, kv_dtype=None, kv_scales=None, k_max=None, host=None, block=1 << 16):
+    """(DeviceModel, OracleModel, OracleCache) with identical weights and prefill.
+
+    BF16 caches take their prefill as BF16 draws placed directly in both
+    caches.  FP8 caches take float32 draws (made on the GPU) that each side
+    rounds into its own cache: the library through mbg_kv_write, the oracle
+    through its codec."""
+    import torch
     from memory_bound_gemv_amd.device_model import DeviceModel
+    kv_dtype = kv_dtype or cfg.kv_dtype
     host = host if host is not None else gen.dense_weights(cfg)
     pt = gen.page_table(cfg, shuffled)
+    if kv_dtype == "fp8" and kv_scales is None:
+        kv_scales = fp8_kv_scales(cfg, block)
     dm = DeviceModel(cfg, host, pt, kv_dtype=kv_dtype, kv_scales=kv_scales, k_max=k_max)
     om = OracleModel(cfg, host)
     oc = OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim, kv_dtype)
@@ -69,6 +99,12 @@ def build_dense(cfg, shuffled=None, kv_dtype="bf16", kv_scales=None, k_max=None,
                 oc.k[li][:cfg.prefill] = k
                 oc.v[li][:cfg.prefill] = v
             else:
-                raise NotImplementedError
+                for p0 in range(0, cfg.prefill, block):
+                    n = min(block, cfg.prefill - p0)
+                    k = gen.kv_prefill_f32_device(cfg, li, 0, p0, n, "cuda")
+                    v = gen.kv_prefill_f32_device(cfg, li, 1, p0, n, "cuda")
+                    dm.kv_write(li, p0, k, v)
+                    oc.prefill_f32(li, p0, k.cpu().numpy(), v.cpu().numpy())
+                torch.cuda.synchronize()
     dm.init()
     return dm, om, oc

@@ -187,3 +187,24 @@ def test_quantize_fp8_rows_zero_row():
     codes, scale = od.quantize_fp8_rows(bits)
     assert scale[0] == 1.0 and np.all(codes[0] == 0)
     assert codes[1, 3] == 0x7E
+
+
+def test_cache_bulk_prefill_equals_store():
+    """OracleCache.prefill_f32 stores what per-position store() stores."""
+    from oracle import OracleCache
+    rng = np.random.default_rng(9)
+    for kv_dtype in ("bf16", "fp8"):
+        a = OracleCache(2, 40, 2, 16, kv_dtype)
+        b = OracleCache(2, 40, 2, 16, kv_dtype)
+        if kv_dtype == "fp8":
+            a.scales = b.scales = np.array([[[2.0**-3, 0.5], [1.0, 0.75]]] * 2, dtype=np.float32)
+        k = rng.standard_normal((40, 2, 16)).astype(np.float32) * 7
+        v = rng.standard_normal((40, 2, 16)).astype(np.float32) * 7
+        for li in range(2):
+            a.prefill_f32(li, 0, k, v)
+            for p in range(40):
+                b.store(li, p, k[p], v[p])
+            assert np.array_equal(a.k[li], b.k[li]) and np.array_equal(a.v[li], b.v[li])
+            ka, va = a.read(li, 40)
+            kb, vb = b.read(li, 40)
+            assert np.array_equal(ka, kb) and np.array_equal(va, vb)

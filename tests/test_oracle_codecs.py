@@ -175,3 +175,25 @@ def test_mxfp4_all_products_and_layout():
         for j in range(16):
             assert out[e, 2 * j] == val(j) * math.ldexp(1.0, e - 127)
             assert out[e, 2 * j + 1] == val(15 - j) * math.ldexp(1.0, e - 127)
+
+
+def test_fp8_bulk_codec_equals_direct():
+    """The table forms used for large caches compute the same functions:
+    every (top 13 bits, sticky) class of binary32 with several low-bit
+    patterns, plus random values; decoding of all 256 codes with scales."""
+    rng = np.random.default_rng(5)
+    top = np.arange(1 << 13, dtype=np.uint32) << np.uint32(19)
+    lows = np.array([0, 1, 0x40000, 0x7FFFF, 0x12345, 0x00100], dtype=np.uint32)
+    bits = (top[:, None] | lows[None, :]).reshape(-1)
+    rnd = rng.integers(0, 2**32, 200_000, dtype=np.uint64).astype(np.uint32)
+    x = np.concatenate([bits, rnd]).view(np.float32)
+    with np.errstate(invalid="ignore"):
+        direct = codecs.f32_to_fp8e4m3(x)
+    assert np.array_equal(codecs.f32_to_fp8e4m3_bulk(x), direct)
+    big = (rng.standard_normal(5_000_000).astype(np.float32) * 64)   # takes the threaded path
+    assert np.array_equal(codecs.f32_to_fp8e4m3_bulk(big), codecs.f32_to_fp8e4m3(big))
+    c = rng.integers(0, 256, (300, 4, 16), dtype=np.uint8)
+    sc = np.array([[2.0**-6], [0.75], [3.0], [1.0]])
+    assert np.array_equal(codecs.fp8e4m3_to_f64_bulk(c, sc), codecs.fp8e4m3_to_f64(c) * sc[None],
+                          equal_nan=True)
+    assert np.array_equal(codecs.fp8e4m3_to_f64_bulk(c), codecs.fp8e4m3_to_f64(c), equal_nan=True)
