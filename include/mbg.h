@@ -206,7 +206,8 @@ int mbg_set_timeout_us(mbg_ctx *ctx, int64_t us);
  * of each workgroup record, for each task it runs, eight uint64 words: the
  * device clock at task start, when its dependency wait was satisfied, when
  * its input vector was loaded, when its weight/KV stream finished, and at
- * task end; then (op | layer << 8 | tile << 32) and two zero words.  An external profiler
+ * task end; then (op | layer << 8 | tile << 32) and two op-specific stamps
+ * (attention: history folded, split-KV combine weights ready; else 0).  An external profiler
  * sees one long kernel per step, so the kernel times itself (the "Muse Spark
  * Open: 1,109 tokens/s" article describes the same in-kernel stamps, section
  * on where the step time goes).  Stamps do not change any result. */
@@ -216,6 +217,16 @@ int mbg_set_trace(mbg_ctx *ctx, int on);
  * records of 8 uint64, in task-list order) into host memory; *n_out is the
  * record count.  Fails with MBG_E_INVALID_ARG if tracing is off. */
 int mbg_read_trace(mbg_ctx *ctx, uint64_t *host_records, size_t max_records, size_t *n_out);
+
+/* MoE models: wait for the init stream and copy the routing the last
+ * step/verify call used in `layer` into host memory: for each of its *ncol
+ * columns, the top_k selected expert ids (int32, by decreasing router
+ * logit, lower id first on ties) and their renormalised softmax weights
+ * (float32), column-major [ncol][top_k].  Both arrays must hold
+ * k_max * top_k entries.  The selection rule is the 163.com Ling-3.0-flash
+ * article's routed top-8 of 512 experts (model and baseline configuration).
+ * MBG_E_INVALID_ARG for a dense model or before the first call. */
+int mbg_read_routing(mbg_ctx *ctx, int32_t layer, int32_t *idx, float *weights, int32_t *ncol);
 
 /* Text of the last error on this thread ("" if none). */
 const char *mbg_last_error(void);
@@ -229,8 +240,9 @@ void mbg_destroy(mbg_ctx *ctx);
 int mbg_lm_head_workspace_size(int32_t k, size_t *bytes);
 
 /* LM head GEMV fused with argmax: logits[j][v] = sum_i W[v][i] * x[j][i]
- * for j < k (1..4), W BF16 or FP8 (scale applied after accumulation), x
- * device float [k][H].  Writes logits (device float [k][V], may be NULL)
+ * for j < k (1..4), W BF16, FP8 (row scale applied after accumulation) or
+ * MXFP4 (E8M0 scale per 32 elements, applied on decode; cols a multiple of
+ * 32), x device float [k][H].  Writes logits (device float [k][V], may be NULL)
  * and argmax (device int32 [k]).  d_workspace (>= the size above) must be
  * zero-filled before its first use; every call leaves it zeroed again.
  * Calls sharing one workspace must not overlap.  The 163.com Ling-3.0-flash

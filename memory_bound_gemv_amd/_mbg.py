@@ -94,6 +94,7 @@ def _load():
         "mbg_set_timeout_us": (C.c_int, [CTX_P, C.c_int64]),
         "mbg_set_trace": (C.c_int, [CTX_P, C.c_int]),
         "mbg_read_trace": (C.c_int, [CTX_P, C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t)]),
+        "mbg_read_routing": (C.c_int, [CTX_P, C.c_int32, C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
         "mbg_last_error": (C.c_char_p, []),
         "mbg_destroy": (None, [CTX_P]),
         "mbg_lm_head_workspace_size": (C.c_int, [C.c_int32, C.POINTER(C.c_size_t)]),
@@ -114,7 +115,7 @@ def _load():
 _lib = _load()
 EXPORTED = ("mbg_workspace_size", "mbg_validate", "mbg_decode_init", "mbg_decode_step", "mbg_decode_verify",
             "mbg_get_status", "mbg_query", "mbg_set_timeout_us", "mbg_set_trace", "mbg_read_trace",
-            "mbg_last_error", "mbg_destroy",
+            "mbg_read_routing", "mbg_last_error", "mbg_destroy",
             "mbg_lm_head_workspace_size", "mbg_lm_head", "mbg_quantize_fp8_rows", "mbg_kv_write")
 
 
@@ -229,6 +230,17 @@ def mbg_read_trace(ctx, n_tasks: int):
     n = C.c_size_t(0)
     _check(_lib.mbg_read_trace(ctx, buf.ctypes.data, n_tasks, C.byref(n)))
     return buf[: n.value]
+
+
+def mbg_read_routing(ctx, layer: int, k_max: int, top_k: int):
+    """(expert ids int32 [ncol][top_k], weights float32 [ncol][top_k]) of the
+    last call's routing in `layer`."""
+    import numpy as np
+    idx = np.zeros(k_max * top_k, dtype=np.int32)
+    w = np.zeros(k_max * top_k, dtype=np.float32)
+    n = C.c_int32(0)
+    _check(_lib.mbg_read_routing(ctx, layer, idx.ctypes.data, w.ctypes.data, C.byref(n)))
+    return idx[: n.value * top_k].reshape(n.value, top_k), w[: n.value * top_k].reshape(n.value, top_k)
 
 
 def mbg_destroy(ctx) -> None:

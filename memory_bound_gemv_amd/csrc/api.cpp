@@ -50,7 +50,8 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 // Workspace sections, in bytes from the base.
 struct Plan {
     size_t status, keys, ctr, head_ctr, task_off, tasks, layers, inv_freq;
-    size_t xres, qbuf, part, attn, hbuf, route_w, route_idx, trace, total;
+    size_t xres, qbuf, part, attn, hbuf, rlogits, route_w, route_idx, trace, total;
+    int64_t hb_ld;
     size_t n_ctr, max_tasks, zero_bytes;
 };
 
@@ -79,12 +80,13 @@ Plan make_plan(const mbg_config& c) {
     p.qbuf = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
     p.part = take(4 * k * (size_t)c.n_q_heads * kMaxSplits * (c.head_dim + 4));   // rows: o, m, l, 2 pad
     p.attn = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
-    size_t hw = (size_t)c.ffn;
-    const size_t moe_w = (size_t)(c.top_k + c.n_shared) * c.moe_ffn;
-    if (moe_w > hw) hw = moe_w;
-    p.hbuf = take(4 * k * hw);
-    p.route_w = take(4 * k * (size_t)(c.top_k > 0 ? c.top_k : 1));
-    p.route_idx = take(4 * k * (size_t)(c.top_k > 0 ? c.top_k : 1));
+    // MoE: a window of k tokens uses at most k * top_k routed experts plus the shared ones
+    p.hb_ld = c.n_experts > 0 ? (int64_t)(k * c.top_k + c.n_shared) * c.moe_ffn : c.ffn;
+    p.hbuf = take(4 * k * (size_t)p.hb_ld);
+    p.rlogits = take(4 * k * (size_t)(c.n_experts > 0 ? c.n_experts : 1));
+    const size_t nroute = L * k * (size_t)(c.top_k > 0 ? c.top_k : 1);
+    p.route_w = take(4 * nroute);
+    p.route_idx = take(4 * nroute);
     p.trace = take(64 * p.max_tasks);
     p.total = off;
     return p;
@@ -123,8 +125,16 @@ int check_config(const mbg_config* c) {
         if (c->ffn <= 0 || c->ffn % 8 != 0)
             return fail(MBG_E_UNSUPPORTED, "config: ffn %d must be a positive multiple of 8", c->ffn);
     } else {
-        if (c->top_k < 1 || c->top_k > 8 || c->top_k > c->n_experts)
-            return fail(MBG_E_UNSUPPORTED, "config: top_k %d (1..8, <= n_experts)", c->top_k);
+        if (c->top_k < 1 || c->top_k > kMaxTopK || c->top_k > c->n_experts)
+            return fail(MBG_E_UNSUPPORTED, "config: top_k %d (1..%d, <= n_experts)", c->top_k, kMaxTopK);
+        if (c->n_experts > kMaxExperts || c->n_experts % 8 != 0)
+            return fail(MBG_E_UNSUPPORTED, "config: n_experts %d (a multiple of 8, <= %d)", c->n_experts,
+                        kMaxExperts);
+        if (c->n_shared > kMaxShared)
+            return fail(MBG_E_UNSUPPORTED, "config: n_shared %d (<= %d)", c->n_shared, kMaxShared);
+        if (c->k_max * c->top_k + c->n_shared > kMaxSlots)
+            return fail(MBG_E_UNSUPPORTED, "config: k_max %d x top_k %d + shared %d experts per window > %d",
+                        c->k_max, c->top_k, c->n_shared, kMaxSlots);
         if (c->moe_ffn <= 0 || c->moe_ffn % 32 != 0)
             return fail(MBG_E_UNSUPPORTED, "config: moe_ffn %d must be a positive multiple of 32", c->moe_ffn);
     }
@@ -171,6 +181,7 @@ struct mbg_ctx {
     int lm_dtype, kv_dtype;
     int n_tasks;
     int trace_on;
+    int last_ncol;   // columns of the last step/verify call (0: none yet)
     unsigned long long* trace_buf;
     char variant[64];
 };
@@ -252,7 +263,6 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     int rc = mbg_validate(cfg, w, kv);
     if (rc) return rc;
     const mbg_config& c = *cfg;
-    if (c.n_experts > 0) return fail(MBG_E_UNSUPPORTED, "MoE layers are not compiled into this build");
     const Plan plan = make_plan(c);
     if (!d_ws || ws_bytes < plan.total)
         return fail(MBG_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, plan.total);
@@ -353,6 +363,18 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.tiles_gu = tiles_for(c.ffn);
     a.tiles_down = tiles_for(c.hidden);
     a.tiles_lm = tiles_for(c.vocab);
+    const bool moe = c.n_experts > 0;
+    if (moe) {
+        a.tiles_router = tiles_for(c.n_experts);
+        a.tiles_egu = (uint32_t)G;
+        a.tiles_edown = tiles_for(c.hidden);
+        if (cdiv(c.hidden, (int64_t)a.tiles_edown * 4) > kMaxDownRows) {
+            delete x;
+            return fail(MBG_E_UNSUPPORTED, "hidden %d: more than %d expert-down rows per wavefront", c.hidden,
+                        kMaxDownRows);
+        }
+    }
+    const uint32_t tiles_last = moe ? a.tiles_edown : a.tiles_down;   // producers of the residual update
     int S = G / c.n_kv_heads;
     S = std::max(1, std::min(S, kMaxSplits));
     S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 128)));   // >= ~128 positions per split
@@ -369,14 +391,20 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
         for (int l = 0; l < c.n_layers; ++l) {
             const uint32_t L8 = (uint32_t)l << 8;
             if (t < a.tiles_qkv)
-                tasks.push_back(Task{OP_QKV | L8, t, l == 0 ? kNoWait : ci(l - 1, PH_DOWN), l == 0 ? 0u : a.tiles_down});
+                tasks.push_back(Task{OP_QKV | L8, t, l == 0 ? kNoWait : ci(l - 1, PH_DOWN), l == 0 ? 0u : tiles_last});
             if (t < tiles_attn) tasks.push_back(Task{OP_ATTN | L8, t, ci(l, PH_QKV), a.tiles_qkv});
             if (t < a.tiles_o) tasks.push_back(Task{OP_OPROJ | L8, t, ci(l, PH_ATTN), (uint32_t)c.n_kv_heads});
-            if (t < a.tiles_gu) tasks.push_back(Task{OP_GATEUP | L8, t, ci(l, PH_OPROJ), a.tiles_o});
-            if (t < a.tiles_down) tasks.push_back(Task{OP_DOWN | L8, t, ci(l, PH_GATEUP), a.tiles_gu});
+            if (!moe) {
+                if (t < a.tiles_gu) tasks.push_back(Task{OP_GATEUP | L8, t, ci(l, PH_OPROJ), a.tiles_o});
+                if (t < a.tiles_down) tasks.push_back(Task{OP_DOWN | L8, t, ci(l, PH_GATEUP), a.tiles_gu});
+            } else {
+                if (t < a.tiles_router) tasks.push_back(Task{OP_ROUTER | L8, t, ci(l, PH_OPROJ), a.tiles_o});
+                if (t < a.tiles_egu) tasks.push_back(Task{OP_EXPGU | L8, t, ci(l, PH_ROUTER), a.tiles_router});
+                if (t < a.tiles_edown) tasks.push_back(Task{OP_EXPDOWN | L8, t, ci(l, PH_GATEUP), a.tiles_egu});
+            }
         }
         if (t < a.tiles_lm)
-            tasks.push_back(Task{OP_LMHEAD, t, ci(c.n_layers - 1, PH_DOWN), a.tiles_down});
+            tasks.push_back(Task{OP_LMHEAD, t, ci(c.n_layers - 1, PH_DOWN), tiles_last});
     }
     off[G] = (uint32_t)tasks.size();
     if (tasks.size() > plan.max_tasks) {
@@ -400,8 +428,21 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
         p.w_gate = (const uint16_t*)L.w_gate.data;
         p.w_up = (const uint16_t*)L.w_up.data;
         p.w_down = (const uint16_t*)L.w_down.data;
+        p.w_router = (const uint16_t*)L.w_router.data;
+        p.eg_codes = (const uint8_t*)L.exp_gate_up.data;
+        p.eg_scales = (const uint8_t*)L.exp_gate_up.scale;
+        p.ed_codes = (const uint8_t*)L.exp_down.data;
+        p.ed_scales = (const uint8_t*)L.exp_down.scale;
+        p.sg_codes = (const uint8_t*)L.sh_gate_up.data;
+        p.sg_scales = (const uint8_t*)L.sh_gate_up.scale;
+        p.sd_codes = (const uint8_t*)L.sh_down.data;
+        p.sd_scales = (const uint8_t*)L.sh_down.scale;
         per_step += 2 * ((int64_t)c.hidden * 2 + (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim * c.hidden +
                          (int64_t)c.hidden * c.n_q_heads * c.head_dim + 3 * (int64_t)c.ffn * c.hidden);
+        if (moe) {  // router plus the top_k + shared experts a single token reads (codes and E8M0 scales)
+            const int64_t expert = 3 * (int64_t)c.moe_ffn * c.hidden * 17 / 32;
+            per_step += 2 * (int64_t)c.n_experts * c.hidden + (int64_t)(c.top_k + c.n_shared) * expert;
+        }
     }
     per_step += 2 * (int64_t)c.hidden * 2;  // embedding row + final norm
     per_step += (int64_t)c.vocab * c.hidden * (x->lm_dtype == MBG_FP8_E4M3 ? 1 : 2) +
@@ -426,6 +467,8 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.part = (float*)(base + plan.part);
     a.attn = (float*)(base + plan.attn);
     a.hbuf = (float*)(base + plan.hbuf);
+    a.hb_ld = (int32_t)plan.hb_ld;
+    a.rlogits = (float*)(base + plan.rlogits);
     a.route_w = (float*)(base + plan.route_w);
     a.route_idx = (int32_t*)(base + plan.route_idx);
     x->trace_buf = (unsigned long long*)(base + plan.trace);
@@ -477,6 +520,7 @@ static int launch_step(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t p
     hipError_t e = hipLaunchCooperativeKernel(x->fn[k], dim3(x->grid), dim3(kBlock), args, (unsigned)x->lds[k],
                                               x->stream);
     if (e != hipSuccess) return hip_fail(e, "hipLaunchCooperativeKernel");
+    x->last_ncol = k;
     return MBG_OK;
 }
 
@@ -547,6 +591,20 @@ int mbg_read_trace(mbg_ctx* x, uint64_t* host, size_t max_records, size_t* n_out
     return MBG_OK;
 }
 
+int mbg_read_routing(mbg_ctx* x, int32_t layer, int32_t* idx, float* weights, int32_t* ncol) {
+    if (!x || !idx || !weights || !ncol) return fail(MBG_E_INVALID_ARG, "NULL pointer");
+    if (x->cfg.n_experts == 0) return fail(MBG_E_INVALID_ARG, "dense model: no routing");
+    if (layer < 0 || layer >= x->cfg.n_layers) return fail(MBG_E_RANGE, "layer %d", layer);
+    if (x->last_ncol == 0) return fail(MBG_E_INVALID_ARG, "no step has run");
+    const size_t n = (size_t)x->last_ncol * x->cfg.top_k;
+    const size_t off = (size_t)layer * n;
+    HIP_TRY(hipStreamSynchronize(x->stream));
+    HIP_TRY(hipMemcpy(idx, x->base.route_idx + off, 4 * n, hipMemcpyDeviceToHost));
+    HIP_TRY(hipMemcpy(weights, x->base.route_w + off, 4 * n, hipMemcpyDeviceToHost));
+    *ncol = x->last_ncol;
+    return MBG_OK;
+}
+
 void mbg_destroy(mbg_ctx* x) { delete x; }
 
 // ------------------------------------------------------- standalone ops
@@ -562,13 +620,14 @@ int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logit
                 void* d_ws, size_t ws_bytes, void* stream) {
     if (!w || !d_x || !d_argmax) return fail(MBG_E_INVALID_ARG, "w/x/argmax is NULL");
     if (k < 1 || k > 4) return fail(MBG_E_RANGE, "k %d outside [1, 4]", k);
-    if (w->dtype != MBG_BF16 && w->dtype != MBG_FP8_E4M3)
-        return fail(MBG_E_UNSUPPORTED, "lm head dtype %d (BF16 or FP8 E4M3)", w->dtype);
+    if (w->dtype != MBG_BF16 && w->dtype != MBG_FP8_E4M3 && w->dtype != MBG_MXFP4)
+        return fail(MBG_E_UNSUPPORTED, "lm head dtype %d (BF16, FP8 E4M3 or MXFP4)", w->dtype);
     int rc = check_tensor(*w, "lm_head", w->dtype, 1, w->rows, w->cols);
     if (rc) return rc;
-    if (w->rows <= 0 || w->rows > 0x7FFFFFFF || w->cols <= 0 || w->cols % 16 != 0)
-        return fail(MBG_E_UNSUPPORTED, "lm head shape [%lld][%lld]: cols must be a positive multiple of 16",
-                    (long long)w->rows, (long long)w->cols);
+    const int align = w->dtype == MBG_MXFP4 ? 32 : 16;
+    if (w->rows <= 0 || w->rows > 0x7FFFFFFF || w->cols <= 0 || w->cols % align != 0)
+        return fail(MBG_E_UNSUPPORTED, "lm head shape [%lld][%lld]: cols must be a positive multiple of %d",
+                    (long long)w->rows, (long long)w->cols, align);
     if (!lm_head_hidden_supported((int)w->cols))
         return fail(MBG_E_UNSUPPORTED, "lm head hidden size %lld not compiled in", (long long)w->cols);
     if ((size_t)k * w->cols * 4 + 256 > 160 * 1024)
@@ -578,7 +637,7 @@ int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logit
     if (cus == 0 && (rc = device_cus(&cus))) return rc;
     LmHeadArgs a;
     a.w = w->data;
-    a.wscale = (const float*)w->scale;
+    a.wscale = w->scale;
     a.x = d_x;
     a.logits = d_logits;
     a.argmax = d_argmax;
@@ -587,7 +646,8 @@ int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logit
     a.V = (int32_t)w->rows;
     a.H = (int32_t)w->cols;
     int64_t grid = std::min<int64_t>((a.V + 3) / 4, 2 * (int64_t)cus);
-    hipError_t e = launch_lm_head(a, k, w->dtype == MBG_FP8_E4M3 ? 2 : 1, (int)grid, (hipStream_t)stream);
+    const int fmt = w->dtype == MBG_FP8_E4M3 ? 2 : w->dtype == MBG_MXFP4 ? 3 : 1;   // kernel format codes (gemv.h)
+    hipError_t e = launch_lm_head(a, k, fmt, (int)grid, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lm_head launch");
     return MBG_OK;
 }

@@ -49,6 +49,14 @@ constexpr uint32_t kNoWait = 0xFFFFFFFFu;
 constexpr uint32_t kCtrLines = 16;
 constexpr uint32_t kLineU32 = 32;
 
+// MoE limits of the compiled kernels.
+constexpr int kMaxExperts = 512;                 // routed experts (a multiple of 8)
+constexpr int kMaxTopK = 8;
+constexpr int kMaxShared = 2;
+constexpr int kMaxSlots = 4 * kMaxTopK + kMaxShared;   // union over a 4-token window plus shared experts
+constexpr int kSlotsPerPass = 9;                 // expert-down slots whose h sits in LDS at once
+constexpr int kMaxDownRows = 4;                  // output rows one wavefront owns in the expert down
+
 struct LayerPtrs {
     const uint16_t* attn_norm;
     const uint16_t* ffn_norm;
@@ -107,9 +115,11 @@ struct StepArgs {
     float* qbuf;               // [k][Hq][d]
     float* part;               // [k][Hq][splits][d + 2] attention partials
     float* attn;               // [k][Hq * d]
-    float* hbuf;               // [k][F] or MoE [k][slots][M]
-    float* route_w;            // [k][top_k] routing weights (MoE)
-    int32_t* route_idx;        // [k][top_k]
+    float* hbuf;               // [k][F] or MoE [k][hb_ld]: column c, slot s, row f at c * hb_ld + s * M + f
+    int32_t hb_ld;             // floats per column of hbuf
+    float* rlogits;            // [k][n_experts] router logits (MoE)
+    float* route_w;            // [L][k][top_k] routing weights of the last step (MoE)
+    int32_t* route_idx;        // [L][k][top_k] routed expert ids of the last step
     unsigned long long* amax_keys;  // [k]
     const double* inv_freq;    // [d/2] theta^(-2i/d)
     unsigned long long* trace; // optional stamps

@@ -10,7 +10,7 @@ namespace mbg {
 
 struct LmHeadArgs {
     const void* w;            // [V][H] BF16 or FP8 codes
-    const float* wscale;      // FP8 row scales [V]
+    const void* wscale;       // FP8: float row scales [V]; MXFP4: E8M0 bytes [V][H/32]
     const float* x;           // [k][H]
     float* logits;            // [k][V] or null
     int32_t* argmax;          // [k]

@@ -38,7 +38,11 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
     const int gw = blockIdx.x * 4 + wave;
     const int nrows = gw < a.V ? (a.V - 1 - gw) / nw + 1 : 0;
     const MBG_GLOBAL uint4* W = gp(reinterpret_cast<const uint4*>(a.w));
-    auto rowf = [&](int rr) -> GRow { return GRow{W + ((size_t)gw + (size_t)nw * rr) * NV, nullptr}; };
+    const MBG_GLOBAL uint8_t* Ws = gp(reinterpret_cast<const uint8_t*>(a.wscale));   // MXFP4: E8M0 [V][H/32]
+    auto rowf = [&](int rr) -> GRow {
+        const size_t row = (size_t)gw + (size_t)nw * rr;
+        return GRow{W + row * NV, F == F_MXFP4 ? Ws + row * NV : nullptr};
+    };
     using RS = RowStream<F, NC, NV>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
@@ -52,7 +56,7 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) best[c] = 0ull;
     MBG_GLOBAL float* logits = a.logits ? gp(a.logits) : nullptr;
-    const MBG_GLOBAL float* wsc = gp(a.wscale);
+    const MBG_GLOBAL float* wsc = gp(reinterpret_cast<const float*>(a.wscale));
     auto out = [&](int rr, const float (&s)[NC]) {
         const uint32_t r = (uint32_t)(gw + nw * rr);
         const float sc = (F == F_FP8) ? wsc[r] : 1.0f;
@@ -128,12 +132,19 @@ hipError_t launch_lm_head(const LmHeadArgs& a, int ncol, int fmt, int grid, hipS
             case 3: return launch_lm_head_nc<F_BF16, 3>(a, grid, s);
             case 4: return launch_lm_head_nc<F_BF16, 4>(a, grid, s);
         }
-    } else {
+    } else if (fmt == F_FP8) {
         switch (ncol) {
             case 1: return launch_lm_head_nc<F_FP8, 1>(a, grid, s);
             case 2: return launch_lm_head_nc<F_FP8, 2>(a, grid, s);
             case 3: return launch_lm_head_nc<F_FP8, 3>(a, grid, s);
             case 4: return launch_lm_head_nc<F_FP8, 4>(a, grid, s);
+        }
+    } else if (fmt == F_MXFP4) {
+        switch (ncol) {
+            case 1: return launch_lm_head_nc<F_MXFP4, 1>(a, grid, s);
+            case 2: return launch_lm_head_nc<F_MXFP4, 2>(a, grid, s);
+            case 3: return launch_lm_head_nc<F_MXFP4, 3>(a, grid, s);
+            case 4: return launch_lm_head_nc<F_MXFP4, 4>(a, grid, s);
         }
     }
     return hipErrorInvalidValue;

@@ -951,12 +951,346 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
     return true;
 }
 
-// --------------------------------------------------------------- LM head
+// ------------------------------------------------------------------- MoE
+//
+// A routed layer (163.com Ling-3.0-flash article, model and baseline
+// configuration: 512 experts, top-8 plus one shared expert; MXFP4 experts
+// per its optimisation 1) runs three phases after the output projection:
+//   ROUTER  r = W_router rmsnorm(x): BF16 rows, like any GEMV;
+//   EXPGU   every workgroup reads the router logits, picks each column's
+//           top-k (lower index on ties) and their renormalised softmax
+//           weights, and lays the union of the picked experts (by id) and
+//           the shared experts out as "slots"; it then streams the MXFP4
+//           gate/up rows of the slots and stores h = w * silu(g) * u per
+//           column, so only selected experts are read and each is read once
+//           for all columns of a verify window (the article's observation
+//           that expert activation is the verify cost);
+//   EXPDOWN x += sum over slots of D_slot h_slot: an output row is the
+//           gather of the slots' row segments, streamed in passes of
+//           kSlotsPerPass slots whose h fits in LDS.
 
+struct RouteLds {
+    uint32_t mask[kMaxExperts / 32];
+    int nslots, nrouted;
+    int slot_exp[kMaxSlots];     // expert id; ids >= n_experts are shared experts
+    float wt[kMaxSlots][4];      // weight of a slot in each column (0: not selected)
+    int sel[4][kMaxTopK];
+    float selw[4][kMaxTopK];
+};
+__shared__ RouteLds s_route;
+
+__device__ __forceinline__ float from_ordered_key32(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Float -> unsigned key with the same order (negative values reversed).
 __device__ __forceinline__ uint32_t ordered_key32(float f) {
     const uint32_t u = __float_as_uint(f);
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+// Routing of this step, from the router logits (float32 [k][E]), into
+// s_route.  Wave c < NC picks column c's top-k: lane l holds experts
+// 8l .. 8l+7 as 64-bit keys (value order, then lower index), and k rounds of
+// a wave-wide maximum take them out one by one.  Weights are
+// exp(r_j - r_max) / sum over the picked j, which equals the picked softmax
+// probabilities renormalised to sum to one.
+template <int NC>
+__device__ void route_slots(CArgs* a) {
+    RouteLds& R = s_route;
+    const int E = a->n_experts, K = a->top_k;
+    const int lane = lane_id(), wave = wave_id();
+    for (int i = threadIdx.x; i < kMaxExperts / 32; i += kThreads) R.mask[i] = 0u;
+    for (int i = threadIdx.x; i < kMaxSlots * 4; i += kThreads) (&R.wt[0][0])[i] = 0.f;
+    __syncthreads();
+    if (wave < NC) {
+        const int c = wave;
+        const rsrc_t rl = make_rsrc(a->rlogits);
+        unsigned long long key[8];
+        const bool has = 8 * lane < E;
+        f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
+        if (has) {
+            v0 = ldc4(rl, (uint32_t)((c * E + 8 * lane) * 4));
+            v1 = ldc4(rl, (uint32_t)((c * E + 8 * lane + 4) * 4));
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float v = i < 4 ? v0[i] : v1[i - 4];
+            const uint32_t e = 8u * lane + i;
+            key[i] = has ? ((unsigned long long)ordered_key32(v) << 32) | (0xFFFFFFFFu - e) : 0ull;
+        }
+        float top_v = 0.f, wsum = 0.f;
+#pragma unroll
+        for (int k = 0; k < kMaxTopK; ++k) {
+            if (k >= K) break;
+            unsigned long long m = key[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) m = key[i] > m ? key[i] : m;
+#pragma unroll
+            for (int o = 32; o >= 1; o >>= 1) {
+                const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)m, o, kWave);
+                const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(m >> 32), o, kWave);
+                const unsigned long long om = ((unsigned long long)hi << 32) | lo;
+                m = om > m ? om : m;
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if (key[i] == m) key[i] = 0ull;
+            const int esel = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
+            const float vsel = from_ordered_key32((uint32_t)(m >> 32));
+            if (k == 0) top_v = vsel;
+            const float ex = expf(vsel - top_v);
+            wsum += ex;
+            if (lane == 0) {
+                R.sel[c][k] = esel;
+                R.selw[c][k] = ex;
+                atomicOr(&R.mask[esel >> 5], 1u << (esel & 31));
+            }
+        }
+        if (lane < K) R.selw[c][lane] = R.selw[c][lane] / wsum;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int n = 0;
+        for (int w = 0; w < kMaxExperts / 32; ++w) {
+            uint32_t m = R.mask[w];
+            while (m) {
+                const int b = __builtin_ctz(m);
+                R.slot_exp[n++] = w * 32 + b;
+                m &= m - 1u;
+            }
+        }
+        R.nrouted = n;
+        for (int sh = 0; sh < a->n_shared; ++sh) R.slot_exp[n + sh] = E + sh;
+        R.nslots = n + a->n_shared;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < NC * K) {
+        const int c = threadIdx.x / K, k = threadIdx.x - c * K;
+        const int e = R.sel[c][k];
+        int slot = 0;
+        while (R.slot_exp[slot] != e) ++slot;
+        R.wt[slot][c] = R.selw[c][k];
+    }
+    if ((int)threadIdx.x < NC * a->n_shared) {
+        const int c = threadIdx.x / a->n_shared, sh = threadIdx.x - c * a->n_shared;
+        R.wt[R.nrouted + sh][c] = 1.f;
+    }
+    __syncthreads();
+}
+
+template <int NC, class S>
+__device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+                                       lds_f32* xs) {
+    constexpr int H = S::H;
+    const int lane = lane_id(), wave = wave_id();
+    CLayer* L = (CLayer*)a->layers + layer;
+    const int E = a->n_experts;
+    const int nw = (int)a->tiles_router * kWaves, gw = (int)tile * kWaves + wave;
+    const int nrows = gw < E ? (E - 1 - gw) / nw + 1 : 0;
+    const uint16_t* wr = L->w_router;
+    auto rowf = [&](int rr) -> GRow {
+        return GRow{gp(reinterpret_cast<const uint4*>(wr + (size_t)(gw + nw * rr) * H)), nullptr};
+    };
+    using RS = RowStream<F_BF16, NC, H / 8>;
+    RS st(nrows, lane);
+    typename RS::Buf A, B;
+    st.issue(A, 0, rowf);
+    if (!wait_counter(a, wctr, wneed)) return false;
+    const rsrc_t x = make_rsrc(a->xres);
+    load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, L->ffn_norm, xs);
+    stamp(0);
+    MBG_GLOBAL float* rl = gp(a->rlogits);
+    auto out = [&](int rr, const float (&s)[NC]) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            if (lane == c) stc(rl + (size_t)c * E + gw + nw * rr, s[c]);
+    };
+    st.run(A, B, rowf, xs, H, out);
+    stamp(1);
+    release_counter(a, ctr_index(layer, PH_ROUTER));
+    return true;
+}
+
+template <int NC, class S>
+__device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+                                      lds_f32* xs) {
+    constexpr int H = S::H, MF = S::MF;
+    const int lane = lane_id(), wave = wave_id();
+    CLayer* L = (CLayer*)a->layers + layer;
+    if (!wait_counter(a, wctr, wneed)) return false;
+    route_slots<NC>(a);
+    const RouteLds& R = s_route;
+    const rsrc_t x = make_rsrc(a->xres);
+    load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, L->ffn_norm, xs);
+    stamp(0);
+    const int E = a->n_experts;
+    const int U = R.nslots;
+    const int nw = (int)a->tiles_egu * kWaves, gw = (int)tile * kWaves + wave;
+    const int total = U * MF;
+    const int nunits = gw < total ? (total - 1 - gw) / nw + 1 : 0;
+    const uint8_t* egc = L->eg_codes;
+    const uint8_t* egs = L->eg_scales;
+    const uint8_t* sgc = L->sg_codes;
+    const uint8_t* sgs = L->sg_scales;
+    constexpr size_t kMatCodes = (size_t)2 * MF * (H / 2), kMatScales = (size_t)2 * MF * (H / 32);
+    auto rowf = [&](int rr) -> GRow {
+        const int u = gw + nw * (rr >> 1);
+        const int slot = u / MF;
+        const int f = u - slot * MF;
+        const int e = R.slot_exp[slot];
+        const size_t row = (size_t)f + (size_t)(rr & 1) * MF;
+        const uint8_t* cb = e < E ? egc + (size_t)e * kMatCodes : sgc + (size_t)(e - E) * kMatCodes;
+        const uint8_t* sb = e < E ? egs + (size_t)e * kMatScales : sgs + (size_t)(e - E) * kMatScales;
+        return GRow{gp(reinterpret_cast<const uint4*>(cb + row * (H / 2))), gp(sb + row * (H / 32))};
+    };
+    using RS = RowStream<F_MXFP4, NC, H / 32>;
+    RS st(2 * nunits, lane);
+    typename RS::Buf A, B;
+    st.issue(A, 0, rowf);
+    MBG_GLOBAL float* hb = gp(a->hbuf);
+    const int ld = a->hb_ld;
+    float gate[NC];
+    auto out = [&](int rr, const float (&s)[NC]) {
+        if ((rr & 1) == 0) {
+#pragma unroll
+            for (int c = 0; c < NC; ++c) gate[c] = s[c];
+            return;
+        }
+        if (lane >= NC) return;
+        const int c = lane;
+        float gv = 0.f, uv = 0.f;
+#pragma unroll
+        for (int cc = 0; cc < NC; ++cc)
+            if (cc == c) { gv = gate[cc]; uv = s[cc]; }
+        const int u = gw + nw * (rr >> 1);
+        const int slot = u / MF;
+        const float w = R.wt[slot][c];
+        stc(hb + (size_t)c * ld + u, w * (gv / (1.0f + expf(-gv)) * uv));
+    };
+    st.run(A, B, rowf, xs, H, out);
+    stamp(1);
+    if (tile == 0 && (int)threadIdx.x < NC * a->top_k) {  // routing record of this step
+        const int c = threadIdx.x / a->top_k, k = threadIdx.x - c * a->top_k;
+        const size_t o = ((size_t)layer * a->ncol + c) * a->top_k + k;
+        gp(a->route_idx)[o] = R.sel[c][k];
+        gp(a->route_w)[o] = R.selw[c][k];
+    }
+    release_counter(a, ctr_index(layer, PH_GATEUP));
+    return true;
+}
+
+template <int NC, class S>
+__device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+                                        lds_f32* xs) {
+    constexpr int H = S::H, MF = S::MF;
+    constexpr int VPS = MF / 32;                     // 16-byte vectors per slot segment of a row
+    constexpr int NV = kSlotsPerPass * VPS;          // vectors per pass
+    constexpr int NJ = (NV + kWave - 1) / kWave;
+    constexpr int XLD = kSlotsPerPass * MF;          // LDS floats per column
+    const int lane = lane_id(), wave = wave_id();
+    CLayer* L = (CLayer*)a->layers + layer;
+    if (!wait_counter(a, wctr, wneed)) return false;
+    route_slots<NC>(a);
+    const RouteLds& R = s_route;
+    stamp(0);
+    const int E = a->n_experts;
+    const int U = R.nslots;
+    const int nw = (int)a->tiles_edown * kWaves, gw = (int)tile * kWaves + wave;
+    const int nrows = gw < H ? min((H - 1 - gw) / nw + 1, kMaxDownRows) : 0;
+    const uint8_t* edc = L->ed_codes;
+    const uint8_t* eds = L->ed_scales;
+    const uint8_t* sdc = L->sd_codes;
+    const uint8_t* sds = L->sd_scales;
+    constexpr size_t kMatCodes = (size_t)H * (MF / 2), kMatScales = (size_t)H * (MF / 32);
+    const rsrc_t hr = make_rsrc(a->hbuf);
+    const int ld = a->hb_ld;
+    float acc[kMaxDownRows][NC];
+#pragma unroll
+    for (int i = 0; i < kMaxDownRows; ++i)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[i][c] = 0.f;
+    for (int s0 = 0; s0 < U; s0 += kSlotsPerPass) {
+        const int ns = min(kSlotsPerPass, U - s0);
+        // h of this pass's slots -> LDS [c][slot][MF]
+        __syncthreads();
+        const int nvec = ns * MF / 4;
+        for (int c = 0; c < NC; ++c)
+            for (int j = threadIdx.x; j < nvec; j += kThreads)
+                *reinterpret_cast<MBG_LDS f32x4*>(xs + c * XLD + 4 * j) =
+                    ldc4(hr, (uint32_t)(((size_t)c * ld + (size_t)s0 * MF + 4 * j) * 4));
+        __syncthreads();
+        // every row's gathered vectors, all in flight at once
+        uint4 w[kMaxDownRows][NJ];
+        uint32_t sb[kMaxDownRows][NJ];
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int v = lane + kWave * j;
+            const bool act = v < ns * VPS;
+            const int slot = s0 + (act ? v / VPS : 0);
+            const int vv = v - (v / VPS) * VPS;
+            const int e = R.slot_exp[slot];
+            const uint8_t* cb = e < E ? edc + (size_t)e * kMatCodes : sdc + (size_t)(e - E) * kMatCodes;
+            const uint8_t* scb = e < E ? eds + (size_t)e * kMatScales : sds + (size_t)(e - E) * kMatScales;
+#pragma unroll
+            for (int i = 0; i < kMaxDownRows; ++i) {
+                if (i < nrows && act) {
+                    const size_t r = (size_t)(gw + nw * i);
+                    w[i][j] = ld_stream_g(gp(reinterpret_cast<const uint4*>(cb + r * (MF / 2))) + vv);
+                    sb[i][j] = gp(scb)[r * (MF / 32) + vv];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j) {
+            const int v = lane + kWave * j;
+            if (v >= ns * VPS) continue;
+            float xv[NC][32];
+#pragma unroll
+            for (int c = 0; c < NC; ++c)
+#pragma unroll
+                for (int e4 = 0; e4 < 32; e4 += 4) {
+                    const f32x4 t = *reinterpret_cast<const MBG_LDS f32x4*>(xs + c * XLD + v * 32 + e4);
+                    xv[c][e4] = t[0];
+                    xv[c][e4 + 1] = t[1];
+                    xv[c][e4 + 2] = t[2];
+                    xv[c][e4 + 3] = t[3];
+                }
+#pragma unroll
+            for (int i = 0; i < kMaxDownRows; ++i) {
+                if (i >= nrows) continue;
+                float wf[32];
+                decode16<F_MXFP4>(w[i][j], sb[i][j], wf);
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+                    for (int e2 = 0; e2 < 32; e2 += 2) {
+                        p0 = fmaf(wf[e2], xv[c][e2], p0);
+                        p1 = fmaf(wf[e2 + 1], xv[c][e2 + 1], p1);
+                    }
+                    acc[i][c] += p0 + p1;
+                }
+            }
+        }
+    }
+    stamp(1);
+    MBG_GLOBAL float* x = gp(a->xres);
+#pragma unroll
+    for (int i = 0; i < kMaxDownRows; ++i) {
+        if (i >= nrows) continue;
+        const int r = gw + nw * i;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+            const float sum = wave_sum(acc[i][c]);
+            if (lane == c) stc(x + c * H + r, ldc(x + c * H + r) + sum);
+        }
+    }
+    release_counter(a, ctr_index(layer, PH_DOWN));
+    return true;
+}
+
+// --------------------------------------------------------------- LM head
 
 template <int NC, class S, int F>
 __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr, uint32_t wneed, lds_f32* xs) {
@@ -1051,8 +1385,21 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
             case OP_QKV: ok = op_qkv<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
             case OP_ATTN: ok = op_attn<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
             case OP_OPROJ: ok = op_oproj<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
-            case OP_GATEUP: ok = op_gateup<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
-            case OP_DOWN: ok = op_down<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem); break;
+            case OP_GATEUP:
+                if constexpr (!S::MOE) ok = op_gateup<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem);
+                break;
+            case OP_DOWN:
+                if constexpr (!S::MOE) ok = op_down<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem);
+                break;
+            case OP_ROUTER:
+                if constexpr (S::MOE) ok = op_router<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem);
+                break;
+            case OP_EXPGU:
+                if constexpr (S::MOE) ok = op_expgu<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem);
+                break;
+            case OP_EXPDOWN:
+                if constexpr (S::MOE) ok = op_expdown<NC, S>(a, layer, tk.tile, tk.wait_ctr, tk.wait_need, smem);
+                break;
             case OP_LMHEAD:
                 ok = a->lm_dtype == F_FP8 ? op_lmhead<NC, S, F_FP8>(a, tk.tile, tk.wait_ctr, tk.wait_need, smem)
                                           : op_lmhead<NC, S, F_BF16>(a, tk.tile, tk.wait_ctr, tk.wait_need, smem);
@@ -1084,7 +1431,8 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
 using ShapeTiny = Shape<256, 1024, 256, 64, 2, F_BF16, 0, 0>;
 using ShapeDense2B = Shape<2048, 8192, 2048, 128, 2, F_BF16, 0, 0>;
 using ShapeDense2BFp8Kv = Shape<2048, 8192, 2048, 128, 2, F_FP8, 0, 0>;
-#define MBG_VARIANTS(X) X(ShapeTiny) X(ShapeDense2B) X(ShapeDense2BFp8Kv)
+using ShapeMoE = Shape<2560, 0, 4096, 128, 8, F_BF16, 1, 768>;
+#define MBG_VARIANTS(X) X(ShapeTiny) X(ShapeDense2B) X(ShapeDense2BFp8Kv) X(ShapeMoE)
 
 template <class S>
 static bool matches(const StepVariant& v) {
@@ -1125,7 +1473,9 @@ const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out) 
         const int xs_bytes = ncol * kmax * 4 + kWaves * kQkvRowsPerWave * ncol * 4;
         const int red_bytes = kAttnRingBytes + kWaves * v.group * (v.head_dim + kPartPad) * 4;
         const int comb_bytes = (8 * v.group * 64 + 4 * v.group) * 4 + kThreads * 16;
+        const int moe_bytes = v.moe ? ncol * kSlotsPerPass * v.moe_ffn * 4 : 0;
         int m = xs_bytes > red_bytes ? xs_bytes : red_bytes;
+        m = m > moe_bytes ? m : moe_bytes;
         *lds_bytes_out = m > comb_bytes ? m : comb_bytes;
     }
     return fn;

@@ -27,10 +27,13 @@ class DeviceModel:
     uint16).  lm_fp8: optional (codes uint8 [V][H], scales f32 [V]) given as
     device tensors, replacing the BF16 LM head.
     page_table: host int32 [n_pages] logical -> physical page.
+    experts: MoE only, per layer a dict of device uint8 tensors: eg_codes
+    [E][2M][H/2], eg_scales [E][2M][H/32], ed_codes [E][H][M/2], ed_scales
+    [E][H][M/32] and the same for the shared experts (sg_*, sd_*, n = S).
     """
 
     def __init__(self, cfg, host: dict, page_table: np.ndarray, kv_dtype: str = "bf16", kv_scales=None,
-                 lm_fp8=None, device="cuda", k_max: int | None = None):
+                 lm_fp8=None, device="cuda", k_max: int | None = None, experts=None):
         self.cfg = cfg
         self.device = torch.device(device)
         self.k_max = k_max or cfg.k_max
@@ -51,6 +54,17 @@ class DeviceModel:
             if not cfg.is_moe:
                 lay.update(w_gate=T(p + "w_gate", cfg.ffn, H), w_up=T(p + "w_up", cfg.ffn, H),
                            w_down=T(p + "w_down", H, cfg.ffn))
+            else:
+                e = experts[i]
+                E, S, Mf = cfg.n_experts, cfg.n_shared, cfg.moe_ffn
+                lay.update(
+                    w_router=T(p + "w_router", E, H),
+                    exp_gate_up=M.make_tensor(e["eg_codes"], "mxfp4", 2 * Mf, H, n=E, scale=e["eg_scales"]),
+                    exp_down=M.make_tensor(e["ed_codes"], "mxfp4", H, Mf, n=E, scale=e["ed_scales"]))
+                if S:
+                    lay.update(
+                        sh_gate_up=M.make_tensor(e["sg_codes"], "mxfp4", 2 * Mf, H, n=S, scale=e["sg_scales"]),
+                        sh_down=M.make_tensor(e["sd_codes"], "mxfp4", H, Mf, n=S, scale=e["sd_scales"]))
             layers.append(M.make_layer(**lay))
         if lm_fp8 is not None:
             self.lm_codes, self.lm_scales = lm_fp8
@@ -121,6 +135,10 @@ class DeviceModel:
 
     def status(self) -> int:
         return M.mbg_get_status(self.ctx)
+
+    def routing(self, layer: int):
+        """(expert ids [ncol][top_k], weights [ncol][top_k]) of the last call."""
+        return M.mbg_read_routing(self.ctx, layer, self.k_max, self.cfg.top_k)
 
     def close(self) -> None:
         if self.ctx is not None:

@@ -221,3 +221,24 @@ def mxfp4_to_f64(codes, scales) -> np.ndarray:
     el[:, 1::2] = e2m1_to_f64(codes >> 4)
     sc = e8m0_to_f64(scales).reshape(rows, cols // 32)
     return (el.reshape(rows, cols // 32, 32) * sc[:, :, None]).reshape(rows, cols)
+
+
+# Bulk form of mxfp4_to_f64 for whole expert matrices: the same products,
+# looked up in the 16 x 256 table of E2M1 value times E8M0 scale that the
+# two functions above give.
+_MX_TAB = None
+
+
+def mxfp4_to_f64_bulk(codes, scales) -> np.ndarray:
+    global _MX_TAB
+    if _MX_TAB is None:
+        _MX_TAB = (e2m1_to_f64(np.arange(16))[None, :] * e8m0_to_f64(np.arange(256))[:, None]).reshape(-1)
+    codes = np.asarray(codes, dtype=np.uint8)
+    rows, half = codes.shape
+    cols = 2 * half
+    sc = np.asarray(scales, dtype=np.uint8).reshape(rows, cols // 32).astype(np.int32) << 4
+    nib = np.empty((rows, cols), dtype=np.int32)
+    nib[:, 0::2] = codes & 0xF
+    nib[:, 1::2] = codes >> 4
+    idx = (nib.reshape(rows, cols // 32, 32) + sc[:, :, None]).reshape(rows, cols)
+    return _MX_TAB[idx]

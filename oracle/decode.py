@@ -236,13 +236,14 @@ class OracleModel:
     """
 
     def __init__(self, cfg, tensors: dict, experts: Optional[Callable] = None,
-                 lm_fp8=None, dtype=np.float64, cache_weights: bool = True):
+                 lm_fp8=None, dtype=np.float64, cache_weights: bool = True, cache_experts: bool = True):
         self.cfg = cfg
         self.t = tensors
         self.experts = experts
         self.lm_fp8 = lm_fp8
         self.dtype = dtype
         self.cache_weights = cache_weights
+        self.cache_experts = cache_experts
         self._w = {}
         self.last_routing = []   # per layer: (indices, weights, router logits)
 
@@ -263,11 +264,11 @@ class OracleModel:
         key = f"l{layer}.expert{e}"
         if key in self._w:
             return self._w[key]
-        gu = codecs.mxfp4_to_f64(*self.experts(layer, e, "gate_up")).astype(self.dtype)
-        dn = codecs.mxfp4_to_f64(*self.experts(layer, e, "down")).astype(self.dtype)
+        gu = codecs.mxfp4_to_f64_bulk(*self.experts(layer, e, "gate_up")).astype(self.dtype, copy=False)
+        dn = codecs.mxfp4_to_f64_bulk(*self.experts(layer, e, "down")).astype(self.dtype, copy=False)
         mf = self.cfg.moe_ffn
         out = (gu[:mf], gu[mf:], dn)
-        if self.cache_weights:
+        if self.cache_weights and self.cache_experts:
             self._w[key] = out
         return out
 

@@ -255,3 +255,80 @@ def expert_mxfp4(cfg: DecodeConfig, layer: int, expert: int, which: str) -> tupl
     sb = hs.view(np.uint8)[:ns].astype(np.uint16)
     scales = (np.uint16(120) + (sb * np.uint16(3) >> np.uint16(8))).astype(np.uint8)
     return codes, scales.reshape(rows, cols // 32)
+
+
+# torch forms of the counter hash, so that experts of full-size models can be
+# drawn where they are used (on the GPU).  Same bits as the numpy functions:
+# int64 arithmetic wraps modulo 2^64 like uint64, and right shifts are made
+# logical with a mask.
+
+def _i64(u: int) -> int:
+    return u - (1 << 64) if u >= 1 << 63 else u
+
+
+def _lsr(z, k: int):
+    return (z >> k) & ((1 << (64 - k)) - 1)
+
+
+def splitmix64_torch(state):
+    z = state.clone()
+    z ^= _lsr(z, 30)
+    z *= _i64(0xBF58476D1CE4E5B9)
+    z ^= _lsr(z, 27)
+    z *= _i64(0x94D049BB133111EB)
+    z ^= _lsr(z, 31)
+    return z
+
+
+def hash_stream_torch(stream: int, start: int, n: int, device):
+    """hash_stream(stream, start .. start+n-1) as an int64 torch tensor."""
+    import torch
+    idx = torch.arange(start, start + n, dtype=torch.int64, device=device)
+    state = (idx + ((stream << 40) + 1)) * _i64(int(GOLDEN_GAMMA))
+    return splitmix64_torch(state)
+
+
+def expert_mxfp4_torch(cfg: DecodeConfig, layer: int, expert: int, which: str, codes_out, scales_out) -> None:
+    """expert_mxfp4 written into torch uint8 tensors (any device) of shapes
+    [rows][cols/2] and [rows][cols/32]."""
+    import torch
+    if which == "gate_up":
+        rows, cols, kind = 2 * cfg.moe_ffn, cfg.hidden, 0
+    else:
+        rows, cols, kind = cfg.hidden, cfg.moe_ffn, 1
+    stream = ((layer * (cfg.n_experts + 1) + expert) * 2 + kind) * 2
+    nb = rows * cols // 2
+    ns = rows * cols // 32
+    dev = codes_out.device
+    hc = hash_stream_torch(stream, 0, -(-nb // 8), dev)
+    codes_out.view(-1).copy_(hc.view(torch.uint8)[:nb])
+    hs = hash_stream_torch(stream + 1, 0, -(-ns // 8), dev)
+    sb = hs.view(torch.uint8)[:ns].to(torch.int32)
+    scales_out.view(-1).copy_((120 + ((sb * 3) >> 8)).to(torch.uint8))
+
+
+def experts_mxfp4_torch(cfg: DecodeConfig, layer: int, experts, which: str, codes_out, scales_out,
+                        chunk: int = 64) -> None:
+    """expert_mxfp4 of every expert id in `experts`, written into stacked
+    torch uint8 tensors codes_out [n][rows][cols/2], scales_out [n][rows][cols/32]."""
+    import torch
+    if which == "gate_up":
+        rows, cols, kind = 2 * cfg.moe_ffn, cfg.hidden, 0
+    else:
+        rows, cols, kind = cfg.hidden, cfg.moe_ffn, 1
+    nb = rows * cols // 2
+    ns = rows * cols // 32
+    dev = codes_out.device
+    ids = list(experts)
+    gamma = _i64(int(GOLDEN_GAMMA))
+    for i0 in range(0, len(ids), chunk):
+        part = ids[i0:i0 + chunk]
+        streams = torch.tensor([((layer * (cfg.n_experts + 1) + e) * 2 + kind) * 2 for e in part],
+                               dtype=torch.int64, device=dev)[:, None]
+        for off, n, out in ((0, nb, codes_out), (1, ns, scales_out)):
+            idx = torch.arange(-(-n // 8), dtype=torch.int64, device=dev)[None, :]
+            h = splitmix64_torch((((streams + off) << 40) + idx + 1) * gamma)
+            b = h.view(torch.uint8).view(len(part), -1)[:, :n]
+            if off == 1:
+                b = (120 + ((b.to(torch.int32) * 3) >> 8)).to(torch.uint8)
+            out[i0:i0 + len(part)].view(len(part), -1).copy_(b)

@@ -108,3 +108,58 @@ def build_dense(cfg, shuffled=None, kv_dtype=None, kv_scales=None, k_max=None, h
                 torch.cuda.synchronize()
     dm.init()
     return dm, om, oc
+
+
+def device_experts(cfg, device="cuda"):
+    """Every layer's MXFP4 experts, drawn on the device by the counter hash."""
+    import torch
+    E, S, H, Mf = cfg.n_experts, cfg.n_shared, cfg.hidden, cfg.moe_ffn
+    u8 = dict(dtype=torch.uint8, device=device)
+    out = []
+    for li in range(cfg.n_layers):
+        d = dict(eg_codes=torch.empty((E, 2 * Mf, H // 2), **u8), eg_scales=torch.empty((E, 2 * Mf, H // 32), **u8),
+                 ed_codes=torch.empty((E, H, Mf // 2), **u8), ed_scales=torch.empty((E, H, Mf // 32), **u8),
+                 sg_codes=torch.empty((max(S, 1), 2 * Mf, H // 2), **u8),
+                 sg_scales=torch.empty((max(S, 1), 2 * Mf, H // 32), **u8),
+                 sd_codes=torch.empty((max(S, 1), H, Mf // 2), **u8),
+                 sd_scales=torch.empty((max(S, 1), H, Mf // 32), **u8))
+        gen.experts_mxfp4_torch(cfg, li, range(E), "gate_up", d["eg_codes"], d["eg_scales"])
+        gen.experts_mxfp4_torch(cfg, li, range(E), "down", d["ed_codes"], d["ed_scales"])
+        if S:
+            gen.experts_mxfp4_torch(cfg, li, range(E, E + S), "gate_up", d["sg_codes"], d["sg_scales"])
+            gen.experts_mxfp4_torch(cfg, li, range(E, E + S), "down", d["sd_codes"], d["sd_scales"])
+        out.append(d)
+    torch.cuda.synchronize()
+    return out
+
+
+def build_moe(cfg, shuffled=None, k_max=None, host=None, cache_experts=True):
+    """(DeviceModel, OracleModel, OracleCache) of a routed model: BF16
+    attention/router weights, MXFP4 experts (drawn on the device for the
+    library, regenerated per expert on the host for the oracle), FP8 LM head
+    quantised from the same BF16 head by each side on its own (the library's
+    mbg_quantize_fp8_rows, the oracle's quantize_fp8_rows)."""
+    import torch
+    from memory_bound_gemv_amd import _mbg as M
+    from memory_bound_gemv_amd.device_model import DeviceModel
+    from oracle import quantize_fp8_rows
+    host = host if host is not None else gen.dense_weights(cfg)
+    pt = gen.page_table(cfg, shuffled)
+    V, H = cfg.vocab, cfg.hidden
+    lm_bf16 = torch.from_numpy(np.ascontiguousarray(host["lm_head"]).view(np.int16)).cuda()
+    lm_codes = torch.empty((V, H), dtype=torch.uint8, device="cuda")
+    lm_scales = torch.empty(V, dtype=torch.float32, device="cuda")
+    M.mbg_quantize_fp8_rows(lm_bf16, V, H, lm_codes, lm_scales, torch.cuda.current_stream().cuda_stream)
+    del lm_bf16
+    experts = device_experts(cfg)
+    dm = DeviceModel(cfg, host, pt, lm_fp8=(lm_codes, lm_scales), experts=experts, k_max=k_max)
+    om = OracleModel(cfg, host, experts=lambda l, e, w: gen.expert_mxfp4(cfg, l, e, w),
+                     lm_fp8=quantize_fp8_rows(host["lm_head"]), cache_experts=cache_experts)
+    oc = OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim, "bf16")
+    for li in range(cfg.n_layers if cfg.prefill else 0):
+        k, v = gen.kv_prefill_bf16(cfg, li)
+        dm.prefill_bf16(li, k, v)
+        oc.k[li][:cfg.prefill] = k
+        oc.v[li][:cfg.prefill] = v
+    dm.init()
+    return dm, om, oc

@@ -134,10 +134,11 @@ def test_standalone_argument_errors(M):
     with pytest.raises(M.MbgError) as e:
         M.mbg_lm_head_workspace_size(5)
     assert e.value.code == M.MBG_E_RANGE
-    w = M.make_tensor(FAKE, "mxfp4", 100, 256, scale=FAKE)
-    with pytest.raises(M.MbgError) as e:
-        M.mbg_lm_head(w, FAKE, 1, FAKE, FAKE, FAKE, 256, 0)
-    assert e.value.code == M.MBG_E_UNSUPPORTED
+    for w in (M.make_tensor(FAKE, "fp32", 100, 256),                 # no fp32 rows
+              M.make_tensor(FAKE, "mxfp4", 100, 48, scale=FAKE)):    # MXFP4 blocks are 32 wide
+        with pytest.raises(M.MbgError) as e:
+            M.mbg_lm_head(w, FAKE, 1, FAKE, FAKE, FAKE, 256, 0)
+        assert e.value.code == M.MBG_E_UNSUPPORTED
     with pytest.raises(M.MbgError) as e:
         M.mbg_quantize_fp8_rows(FAKE, 10, 20, FAKE, FAKE, 0)
     assert e.value.code == M.MBG_E_INVALID_ARG

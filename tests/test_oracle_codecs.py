@@ -197,3 +197,13 @@ def test_fp8_bulk_codec_equals_direct():
     assert np.array_equal(codecs.fp8e4m3_to_f64_bulk(c, sc), codecs.fp8e4m3_to_f64(c) * sc[None],
                           equal_nan=True)
     assert np.array_equal(codecs.fp8e4m3_to_f64_bulk(c), codecs.fp8e4m3_to_f64(c), equal_nan=True)
+
+
+def test_mxfp4_bulk_equals_direct():
+    rng = np.random.default_rng(8)
+    codes = rng.integers(0, 256, (40, 64), dtype=np.uint8)
+    scales = rng.integers(0, 256, (40, 4), dtype=np.uint8)
+    scales[0, :] = [0, 1, 254, 255]
+    a = codecs.mxfp4_to_f64(codes, scales)
+    b = codecs.mxfp4_to_f64_bulk(codes, scales)
+    assert np.array_equal(a, b, equal_nan=True)

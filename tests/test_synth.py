@@ -3,6 +3,7 @@ distributions and shapes (CPU only)."""
 import os
 
 import numpy as np
+import pytest
 
 from synth import CONFIGS, gen
 
@@ -60,3 +61,27 @@ def test_config_sizes():
     assert c.max_pos == 4352 and c.qkv_rows == 4096
     assert CONFIGS["tiny"].max_pos == 48
     assert CONFIGS["longctx"].max_pos == 200064
+
+
+def test_expert_hash_torch_matches_numpy():
+    """The torch form of the expert generator draws the same bytes."""
+    torch = pytest.importorskip("torch")
+    cfg = CONFIGS["moe"].with_(hidden=256, moe_ffn=64, n_experts=16)
+    for layer, e, which in ((0, 0, "gate_up"), (3, 15, "down"), (41, 16, "gate_up"), (7, 16, "down")):
+        c, s = gen.expert_mxfp4(cfg, layer, e, which)
+        ct = torch.empty(c.shape, dtype=torch.uint8)
+        st = torch.empty(s.shape, dtype=torch.uint8)
+        gen.expert_mxfp4_torch(cfg, layer, e, which, ct, st)
+        assert np.array_equal(ct.numpy(), c) and np.array_equal(st.numpy(), s)
+    # stacked form, several experts at once (shared expert id included)
+    ids = [2, 5, 16]
+    ct = torch.empty((3, 2 * cfg.moe_ffn, cfg.hidden // 2), dtype=torch.uint8)
+    st = torch.empty((3, 2 * cfg.moe_ffn, cfg.hidden // 32), dtype=torch.uint8)
+    gen.experts_mxfp4_torch(cfg, 9, ids, "gate_up", ct, st, chunk=2)
+    for i, e in enumerate(ids):
+        c, s = gen.expert_mxfp4(cfg, 9, e, "gate_up")
+        assert np.array_equal(ct[i].numpy(), c) and np.array_equal(st[i].numpy(), s)
+    # large stream ids and counters (the full model's last expert of its last layer)
+    big = gen.hash_stream(10**6, np.arange(2**20, 2**20 + 1000, dtype=np.uint64))
+    bt = gen.hash_stream_torch(10**6, 2**20, 1000, "cpu").numpy().view(np.uint64)
+    assert np.array_equal(big, bt)
