@@ -38,6 +38,9 @@ class DeviceModel:
         self.device = torch.device(device)
         self.k_max = k_max or cfg.k_max
         self.t = {k: _dev(v, self.device) for k, v in host.items()}
+        # The library keeps raw pointers into every tensor it is given: hold
+        # references for as long as the context lives.
+        self.experts = experts
         H, d = cfg.hidden, cfg.head_dim
         bf = "bf16"
 
