@@ -44,12 +44,13 @@ int hip_fail(hipError_t e, const char* what) {
 constexpr int kMaxGrid = 1024;   // workgroups of the persistent kernel (upper bound)
 constexpr int kMaxSplits = 64;   // split-KV partitions per KV head (upper bound)
 constexpr int kBlock = 256;
+constexpr int kAttnBufsHost = 4;   // attention ring chunks per wave (step.hip)
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace sections, in bytes from the base.
 struct Plan {
-    size_t status, keys, ctr, head_ctr, task_off, tasks, layers, inv_freq;
+    size_t status, keys, ctr, head_ctr, task_off, tasks, layers, inv_freq, rope_cs;
     size_t xres, qbuf, part, attn, hbuf, rlogits, route_w, route_idx, trace, total;
     int64_t hb_ld;
     size_t n_ctr, max_tasks, zero_bytes;
@@ -76,6 +77,7 @@ Plan make_plan(const mbg_config& c) {
     p.tasks = take(sizeof(Task) * p.max_tasks);
     p.layers = take(sizeof(LayerPtrs) * L);
     p.inv_freq = take(8 * (size_t)(c.head_dim / 2));
+    p.rope_cs = take(8 * (size_t)c.max_pos * (c.head_dim / 2));
     p.xres = take(4 * k * c.hidden);
     p.qbuf = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
     p.part = take(4 * k * (size_t)c.n_q_heads * kMaxSplits * (c.head_dim + 4));   // rows: o, m, l, 2 pad
@@ -379,6 +381,16 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     S = std::max(1, std::min(S, kMaxSplits));
     S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 128)));   // >= ~128 positions per split
     a.attn_splits = S;
+    // prefetch defaults chosen by measurement on the dense 2B step (the
+    // environment variables below override them for tuning runs)
+    a.gemv_pre = 1;
+    a.attn_pre = kAttnBufsHost;
+    a.poll_wave_prefetch = 1;
+    a.wave0_input = 1;
+    if (const char* e = getenv("MBG_GEMV_PREFETCH")) a.gemv_pre = std::max(1, std::min(2, atoi(e)));
+    if (const char* e = getenv("MBG_POLL_WAVE_PREFETCH")) a.poll_wave_prefetch = atoi(e) != 0;
+    if (const char* e = getenv("MBG_WAVE0_INPUT")) a.wave0_input = atoi(e) != 0;
+    if (const char* e = getenv("MBG_ATTN_PREFETCH")) a.attn_pre = std::max(0, std::min(kAttnBufsHost, atoi(e)));
     const uint32_t tiles_attn = (uint32_t)(c.n_kv_heads * S);
 
     // task lists
@@ -462,6 +474,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.tasks = (const Task*)(base + plan.tasks);
     a.layers = (const LayerPtrs*)(base + plan.layers);
     a.inv_freq = (const double*)(base + plan.inv_freq);
+    a.rope_cs = (const float2*)(base + plan.rope_cs);
     a.xres = (float*)(base + plan.xres);
     a.qbuf = (float*)(base + plan.qbuf);
     a.part = (float*)(base + plan.part);
@@ -492,6 +505,8 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     if (e == hipSuccess)
         e = hipMemcpyAsync(base + plan.layers, lp.data(), sizeof(LayerPtrs) * lp.size(), hipMemcpyHostToDevice, s);
     if (e == hipSuccess) e = hipMemcpyAsync(base + plan.inv_freq, inv.data(), 8 * inv.size(), hipMemcpyHostToDevice, s);
+    if (e == hipSuccess)
+        e = launch_rope_table((const double*)(base + plan.inv_freq), HALF, c.max_pos, (float2*)(base + plan.rope_cs), s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
         delete x;

@@ -77,6 +77,16 @@ __device__ __forceinline__ void lds_dma16(const MBG_GLOBAL void* src, MBG_LDS vo
                  : "memory");
 }
 
+// The same with the device-scope (sc1) cache policy: for data other
+// workgroups wrote earlier in the same launch.
+__device__ __forceinline__ void lds_dma16_coh(const MBG_GLOBAL void* src, MBG_LDS void* dst) {
+    const uint32_t lds = (uint32_t)(uintptr_t)dst;
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off sc1"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(src)
+                 : "memory");
+}
+
 // Address of one weight row (scalar): 16-byte vectors plus, for MXFP4, one
 // E8M0 byte per vector.
 struct GRow {
@@ -204,12 +214,28 @@ struct RowStream {
         }
     }
 
-    // `a` holds chunk 0, already issued.
+    __device__ __forceinline__ int chunks() const { return (nrows + RPC - 1) / RPC; }
+
+    // Issue chunk 0 into `a` and, if there is one, chunk 1 into `b`: the
+    // whole register double buffer is requested before the caller's wait.
+    // Returns whether chunk 1 was issued (pass it to run()).
+    template <class RowFn>
+    __device__ __forceinline__ bool prefetch(Buf& a, Buf& b, RowFn& row, int depth = 2) const {
+        issue(a, 0, row);
+        if (depth > 1 && chunks() > 1) {
+            issue(b, 1, row);
+            return true;
+        }
+        return false;
+    }
+
+    // `a` holds chunk 0, already issued; `b` holds chunk 1 when b_issued.
     template <class RowFn, class OutFn>
-    __device__ __forceinline__ void run(Buf& a, Buf& b, RowFn& row, const lds_f32* xs, int ldx, OutFn& out) const {
-        const int nch = (nrows + RPC - 1) / RPC;
+    __device__ __forceinline__ void run(Buf& a, Buf& b, RowFn& row, const lds_f32* xs, int ldx, OutFn& out,
+                                        bool b_issued = false) const {
+        const int nch = chunks();
         for (int c = 0; c < nch; c += 2) {
-            if (c + 1 < nch) issue(b, c + 1, row);
+            if (c + 1 < nch && !(c == 0 && b_issued)) issue(b, c + 1, row);
             compute(a, c, xs, ldx, out);
             if (c + 1 >= nch) break;
             if (c + 2 < nch) issue(a, c + 2, row);

@@ -91,6 +91,11 @@ struct StepArgs {
     uint32_t tiles_qkv, tiles_o, tiles_gu, tiles_down, tiles_lm;
     uint32_t tiles_router, tiles_egu, tiles_edown;
     int32_t attn_splits;
+    // prefetch depth before a dependency wait: register chunks per GEMV wave
+    // (1 or 2) and attention ring chunks per wave (0 .. kAttnBufs)
+    int32_t gemv_pre, attn_pre;
+    int32_t poll_wave_prefetch;  // 1: the polling wave (0) also prefetches before its wait
+    int32_t wave0_input;         // 1: inputs copied to LDS by wave 0 alone (coherent DMA); 0: all waves load
     // weights
     const LayerPtrs* layers;
     const uint16_t* embed;
@@ -122,6 +127,7 @@ struct StepArgs {
     int32_t* route_idx;        // [L][k][top_k] routed expert ids of the last step
     unsigned long long* amax_keys;  // [k]
     const double* inv_freq;    // [d/2] theta^(-2i/d)
+    const float2* rope_cs;     // [max_pos][d/2] (cos, sin) of p * inv_freq[i], from double angles
     unsigned long long* trace; // optional stamps
     // per call
     const int32_t* tokens;

@@ -36,6 +36,7 @@ hipError_t launch_quantize_fp8_rows(const uint16_t* w, int64_t rows, int64_t col
                                     hipStream_t s);
 hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* p, size_t n, uint32_t v, hipStream_t s);
+hipError_t launch_rope_table(const double* inv_freq, int half, int64_t max_pos, float2* cs, hipStream_t s);
 
 // Decode-step kernel family: the compile-time shape a kernel is built for.
 struct StepVariant {

@@ -215,6 +215,29 @@ hipError_t launch_kv_write(const KvWriteArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// ------------------------------------------------------------ RoPE table
+
+// cs[p][i] = (cos, sin)(p * inv_freq[i]) for every position p < max_pos:
+// the angle and its cosine and sine in double precision, rounded once to
+// binary32.  Built at init, so a step only loads the pair it needs.
+__global__ void rope_table_kernel(const double* __restrict__ inv_freq, int half, int64_t n, float2* __restrict__ cs) {
+    for (int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t p = idx / half;
+        const int i = (int)(idx - p * half);
+        double sd, cd;
+        sincos((double)p * inv_freq[i], &sd, &cd);
+        cs[idx] = make_float2((float)cd, (float)sd);
+    }
+}
+
+hipError_t launch_rope_table(const double* inv_freq, int half, int64_t max_pos, float2* cs, hipStream_t s) {
+    const int64_t n = max_pos * half;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s, inv_freq, half, n, cs);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- fill
 
 __global__ void fill_u32_kernel(uint32_t* p, size_t n, uint32_t v) {

@@ -267,6 +267,79 @@ __device__ void load_plain(const float* src, lds_f32* xs) {
     __syncthreads();
 }
 
+// xs[0 .. n) = src[0 .. n) (float32 written earlier in this launch, n a
+// multiple of 256), copied by wave 0 alone with device-coherent LDS DMA:
+// wave 0 is the polling wave and has no weight loads in flight, so the copy
+// does not queue behind the other waves' prefetch.  Ends with a barrier.
+__device__ __forceinline__ void dma_input(CArgs* a, const float* src, int n, lds_f32* xs) {
+    if (!a->wave0_input) {   // every wave copies its share through registers
+        const rsrc_t r = make_rsrc(src);
+        for (int j = threadIdx.x; j < n / 4; j += kThreads)
+            *reinterpret_cast<MBG_LDS f32x4*>(xs + 4 * j) = ldc4(r, 16u * j);
+        __syncthreads();
+        return;
+    }
+    if (wave_id() == 0) {
+        const MBG_GLOBAL float* s = gp(src) + lane_id() * 4;
+        for (int i = 0; i < n; i += kWave * 4) lds_dma16_coh(s + i, (MBG_LDS void*)(xs + i));
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    }
+    __syncthreads();
+}
+
+// xs[c][i] (already in LDS) *= 1 / sqrt(mean_i xs[c][i]^2 + eps) * gain[i]:
+// the same per-thread quads and reduction order as load_normed.
+template <int NC, int H>
+__device__ void norm_in_place(CArgs* a, const uint16_t* gain, lds_f32* xs) {
+    __shared__ float red[kWaves * 4];
+    constexpr int NV = H / 4;
+    constexpr int PER = (NV + kThreads - 1) / kThreads;
+    const int tid = threadIdx.x;
+    const MBG_GLOBAL u32x2* g2 = gp(reinterpret_cast<const u32x2*>(gain));
+    float ss[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        ss[c] = 0.f;
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int j = tid + kThreads * p;
+            if (NV % kThreads == 0 || j < NV) {
+                const f32x4 v = *reinterpret_cast<const MBG_LDS f32x4*>(xs + c * H + 4 * j);
+                ss[c] = fmaf(v[0], v[0], ss[c]);
+                ss[c] = fmaf(v[1], v[1], ss[c]);
+                ss[c] = fmaf(v[2], v[2], ss[c]);
+                ss[c] = fmaf(v[3], v[3], ss[c]);
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const float w = wave_sum(ss[c]);
+        if ((tid & 63) == 0) red[(tid >> 6) * 4 + c] = w;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const float tot = ((red[c] + red[4 + c]) + red[8 + c]) + red[12 + c];
+        const float r = 1.0f / sqrtf(tot / (float)H + a->rms_eps);
+#pragma unroll
+        for (int p = 0; p < PER; ++p) {
+            const int j = tid + kThreads * p;
+            if (NV % kThreads == 0 || j < NV) {
+                const u32x2 gg = g2[j];
+                MBG_LDS f32x4* q = reinterpret_cast<MBG_LDS f32x4*>(xs + c * H + 4 * j);
+                f32x4 o = *q;
+                o[0] = o[0] * r * bf16_lo(gg.x);
+                o[1] = o[1] * r * bf16_hi(gg.x);
+                o[2] = o[2] * r * bf16_lo(gg.y);
+                o[3] = o[3] * r * bf16_hi(gg.y);
+                *q = o;
+            }
+        }
+    }
+    __syncthreads();
+}
+
 // Four BF16 values (8 bytes) as float32.
 __device__ __forceinline__ f32x4 bf16x4(const MBG_GLOBAL u32x2* p) {
     const u32x2 u = *p;
@@ -314,7 +387,24 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
     using RS = RowStream<F_BF16, NC, H / 8>;
     RS st(2 * nunits, lane);
     typename RS::Buf A, B;
-    st.issue(A, 0, rowf);
+    bool b_issued = false;
+    const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
+    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
+    // RoPE (cos, sin) of this lane's epilogue items (at most two per lane:
+    // nunits * NC <= 2 * kWave), loaded before the wait: positions are known
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const MBG_GLOBAL f32x2* rcs = gp(reinterpret_cast<const f32x2*>(a->rope_cs));
+    f32x2 cs_pre[2] = {{1.f, 0.f}, {1.f, 0.f}};
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = lane + kWave * it;
+        if (idx < nunits * NC) {
+            const int pu = idx / NC, c = idx - pu * NC;
+            const int u = gw + nw * pu;
+            const int hh = u / HALF;
+            if (hh < Hq + Hkv) cs_pre[it] = rcs[(size_t)(a->pos + c) * HALF + (u - hh * HALF)];
+        }
+    }
     if (!wait_counter(a, wctr, wneed)) return false;
     if (layer == 0) {
         int tok[NC];
@@ -324,9 +414,10 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
         load_normed<NC, H>(a, [&](int c, int j) { return bf16x4(emb + (size_t)tok[c] * (H / 4) + j); }, L->attn_norm,
                            xs);
     } else {
-        const rsrc_t x = make_rsrc(a->xres);
-        load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, L->attn_norm, xs);
+        dma_input(a, a->xres, NC * H, xs);
+        norm_in_place<NC, H>(a, L->attn_norm, xs);
     }
+    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
     stamp(0);
     // row sums -> per-wave LDS slots; RoPE and the cache write run after the stream
     lds_f32* res = xs + NC * H + wave * kQkvRowsPerWave * NC;  // [rows][NC]
@@ -336,12 +427,14 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
             for (int c = 0; c < NC; ++c) res[rr * NC + c] = s[c];
         }
     };
-    st.run(A, B, rowf, xs, H, out);
+    st.run(A, B, rowf, xs, H, out, b_issued);
     stamp(1);
     __syncthreads();
-    const MBG_GLOBAL double* invf = gp(a->inv_freq);
     const MBG_GLOBAL int32_t* ptab = gp(a->page_table);
-    for (int idx = lane; idx < nunits * NC; idx += kWave) {
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+        const int idx = lane + kWave * it;
+        if (idx >= nunits * NC) break;
         const int pu = idx / NC;
         const int c = idx - pu * NC;
         float x0 = res[(2 * pu) * NC + c];
@@ -351,9 +444,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
         const int i = u - hh * HALF;
         const int p = a->pos + c;
         if (hh < Hq + Hkv) {
-            double sd, cd;
-            sincos((double)p * invf[i], &sd, &cd);
-            const float cs = (float)cd, sn = (float)sd;
+            const float cs = cs_pre[it][0], sn = cs_pre[it][1];
             const float y0 = x0 * cs - x1 * sn;
             const float y1 = x0 * sn + x1 * cs;
             x0 = y0;
@@ -571,8 +662,11 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     };
 
     const int npre = min(nch, NB);
-    for (int c = 0; c < npre; ++c) issue_chunk(c, c);
+    // the polling wave (0) may hold its loads back until its wait is over
+    const int early = (wave != 0 || a->poll_wave_prefetch) ? min(npre, a->attn_pre) : 0;
+    for (int c = 0; c < early; ++c) issue_chunk(c, c);
     if (!wait_counter(a, wctr, wneed)) return false;
+    for (int c = early; c < npre; ++c) issue_chunk(c, c);
 
     const float qscale = a->attn_scale_log2;
     const float ksc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 0] : 1.f;
@@ -842,9 +936,12 @@ __device__ __forceinline__ bool op_oproj(CArgs* a, uint32_t layer, uint32_t tile
     using RS = RowStream<F_BF16, NC, K / 8>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
-    st.issue(A, 0, rowf);
+    bool b_issued = false;
+    const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
+    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
     if (!wait_counter(a, wctr, wneed)) return false;
-    load_plain<NC, K>(a->attn, xs);
+    dma_input(a, a->attn, NC * K, xs);
+    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
     stamp(0);
     int tok[NC];
 #pragma unroll
@@ -863,7 +960,7 @@ __device__ __forceinline__ bool op_oproj(CArgs* a, uint32_t layer, uint32_t tile
         const float res = layer == 0 ? bf16_to_f32(emb[(size_t)tk_ * H + r]) : ldc(x + c * H + r);
         stc(x + c * H + r, res + v);
     };
-    st.run(A, B, rowf, xs, K, out);
+    st.run(A, B, rowf, xs, K, out, b_issued);
     stamp(1);
     release_counter(a, ctr_index(layer, PH_OPROJ));
     return true;
@@ -887,10 +984,13 @@ __device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t til
     using RS = RowStream<F_BF16, NC, H / 8>;
     RS st(2 * nunits, lane);
     typename RS::Buf A, B;
-    st.issue(A, 0, rowf);
+    bool b_issued = false;
+    const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
+    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
     if (!wait_counter(a, wctr, wneed)) return false;
-    const rsrc_t x = make_rsrc(a->xres);
-    load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, L->ffn_norm, xs);
+    dma_input(a, a->xres, NC * H, xs);
+    norm_in_place<NC, H>(a, L->ffn_norm, xs);
+    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
     stamp(0);
     MBG_GLOBAL float* hb = gp(a->hbuf);
     float gate[NC];
@@ -909,7 +1009,7 @@ __device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t til
         const int f = gw + nw * (rr >> 1);
         stc(hb + (size_t)c * F + f, gv / (1.0f + expf(-gv)) * uv);
     };
-    st.run(A, B, rowf, xs, H, out);
+    st.run(A, B, rowf, xs, H, out, b_issued);
     stamp(1);
     release_counter(a, ctr_index(layer, PH_GATEUP));
     return true;
@@ -930,9 +1030,12 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
     using RS = RowStream<F_BF16, NC, F / 8>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
-    st.issue(A, 0, rowf);
+    bool b_issued = false;
+    const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
+    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
     if (!wait_counter(a, wctr, wneed)) return false;
-    load_plain<NC, F>(a->hbuf, xs);
+    dma_input(a, a->hbuf, NC * F, xs);
+    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
     stamp(0);
     MBG_GLOBAL float* x = gp(a->xres);
     auto out = [&](int rr, const float (&s)[NC]) {
@@ -945,7 +1048,7 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
         const int r = gw + nw * rr;
         stc(x + c * H + r, ldc(x + c * H + r) + v);
     };
-    st.run(A, B, rowf, xs, F, out);
+    st.run(A, B, rowf, xs, F, out, b_issued);
     stamp(1);
     release_counter(a, ctr_index(layer, PH_DOWN));
     return true;
@@ -1095,10 +1198,13 @@ __device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t til
     using RS = RowStream<F_BF16, NC, H / 8>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
-    st.issue(A, 0, rowf);
+    bool b_issued = false;
+    const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
+    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
     if (!wait_counter(a, wctr, wneed)) return false;
-    const rsrc_t x = make_rsrc(a->xres);
-    load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, L->ffn_norm, xs);
+    dma_input(a, a->xres, NC * H, xs);
+    norm_in_place<NC, H>(a, L->ffn_norm, xs);
+    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
     stamp(0);
     MBG_GLOBAL float* rl = gp(a->rlogits);
     auto out = [&](int rr, const float (&s)[NC]) {
@@ -1106,7 +1212,7 @@ __device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t til
         for (int c = 0; c < NC; ++c)
             if (lane == c) stc(rl + (size_t)c * E + gw + nw * rr, s[c]);
     };
-    st.run(A, B, rowf, xs, H, out);
+    st.run(A, B, rowf, xs, H, out, b_issued);
     stamp(1);
     release_counter(a, ctr_index(layer, PH_ROUTER));
     return true;
@@ -1121,8 +1227,8 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
     if (!wait_counter(a, wctr, wneed)) return false;
     route_slots<NC>(a);
     const RouteLds& R = s_route;
-    const rsrc_t x = make_rsrc(a->xres);
-    load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, L->ffn_norm, xs);
+    dma_input(a, a->xres, NC * H, xs);
+    norm_in_place<NC, H>(a, L->ffn_norm, xs);
     stamp(0);
     const int E = a->n_experts;
     const int U = R.nslots;
@@ -1306,10 +1412,13 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     using RS = RowStream<F, NC, H / E>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
-    st.issue(A, 0, rowf);
+    bool b_issued = false;
+    const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
+    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
     if (!wait_counter(a, wctr, wneed)) return false;
-    const rsrc_t x = make_rsrc(a->xres);
-    load_normed<NC, H>(a, [&](int c, int j) { return ldc4(x, 16u * (c * (H / 4) + j)); }, a->final_norm, xs);
+    dma_input(a, a->xres, NC * H, xs);
+    norm_in_place<NC, H>(a, a->final_norm, xs);
+    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
     stamp(0);
     unsigned long long best[NC];
 #pragma unroll
@@ -1327,7 +1436,7 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
             best[c] = k > best[c] ? k : best[c];
         }
     };
-    st.run(A, B, rowf, xs, H, out);
+    st.run(A, B, rowf, xs, H, out, b_issued);
     stamp(1);
     if (lane == 0) {
 #pragma unroll
