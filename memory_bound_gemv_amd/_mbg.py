@@ -8,7 +8,8 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libmbg.so")
+# MBG_LIBRARY names another build of the same library (A/B measurements)
+LIB_PATH = os.environ.get("MBG_LIBRARY") or os.path.join(HERE, "libmbg.so")
 
 MBG_OK = 0
 MBG_E_INVALID_ARG = -1

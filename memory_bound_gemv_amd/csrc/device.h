@@ -129,6 +129,17 @@ __device__ __forceinline__ float wave_sum(float v) {
            __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
 }
 
+// Whole-wavefront maximum, identical in every lane.
+__device__ __forceinline__ float wave_max(float v) {
+    v = fmaxf(v, dpp_f<0xB1>(v));
+    v = fmaxf(v, dpp_f<0x4E>(v));
+    v = fmaxf(v, dpp_f<0x141>(v));
+    v = fmaxf(v, dpp_f<0x140>(v));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
+    return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
+                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int mask) {
     return __shfl_xor(v, mask, kWave);
 }

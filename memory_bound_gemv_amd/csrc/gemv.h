@@ -135,6 +135,8 @@ struct RowStream {
     static constexpr int LASTN = NV - kWave * (NJ - 1);  // lanes active in the last vector column
     static constexpr bool PART = LASTN != kWave;
     static constexpr int E = FmtInfo<F>::kEPV;
+    static constexpr int kRowBytes = NV * 16;   // weight bytes per row (scales aside)
+    static constexpr int kRpc = RPC;
 
     struct Buf {
         uint4 w[RPC][NJ];
@@ -147,12 +149,13 @@ struct RowStream {
 
     __device__ __forceinline__ static bool active(int j, int lane) { return !PART || j < NJ - 1 || lane < LASTN; }
 
+    // Issue rows [r0, r1) of chunk c into b.
     template <class RowFn>
-    __device__ __forceinline__ void issue(Buf& b, int c, RowFn& row) const {
+    __device__ __forceinline__ void issue_rows(Buf& b, int c, RowFn& row, int r0, int r1) const {
 #pragma unroll
         for (int r = 0; r < RPC; ++r) {
             const int rr = c * RPC + r;
-            if (rr < nrows) {
+            if (r >= r0 && r < r1 && rr < nrows) {
                 const GRow g = row(rr);
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
@@ -163,6 +166,10 @@ struct RowStream {
                 }
             }
         }
+    }
+    template <class RowFn>
+    __device__ __forceinline__ void issue(Buf& b, int c, RowFn& row) const {
+        issue_rows(b, c, row, 0, RPC);
     }
 
     template <class OutFn>
@@ -216,14 +223,24 @@ struct RowStream {
 
     __device__ __forceinline__ int chunks() const { return (nrows + RPC - 1) / RPC; }
 
-    // Issue chunk 0 into `a` and, if there is one, chunk 1 into `b`: the
-    // whole register double buffer is requested before the caller's wait.
-    // Returns whether chunk 1 was issued (pass it to run()).
+    // Before the caller's input wait: issue the first `pre` rows (at most
+    // two chunks) of the stream into `a` (chunk 0) and `b` (chunk 1).
+    // Returns how many were issued; pass it to finish_prefetch.
     template <class RowFn>
-    __device__ __forceinline__ bool prefetch(Buf& a, Buf& b, RowFn& row, int depth = 2) const {
-        issue(a, 0, row);
-        if (depth > 1 && chunks() > 1) {
-            issue(b, 1, row);
+    __device__ __forceinline__ int prefetch(Buf& a, Buf& b, RowFn& row, int pre) const {
+        pre = pre < 0 ? 0 : pre > 2 * RPC ? 2 * RPC : pre;
+        issue_rows(a, 0, row, 0, pre < RPC ? pre : RPC);
+        if (pre > RPC) issue_rows(b, 1, row, 0, pre - RPC);
+        return pre;
+    }
+
+    // After the wait: the rest of the prefetched chunks.  Returns whether
+    // chunk 1 is issued (pass it to run()).
+    template <class RowFn>
+    __device__ __forceinline__ bool finish_prefetch(Buf& a, Buf& b, RowFn& row, int pre) const {
+        if (pre < RPC) issue_rows(a, 0, row, pre, RPC);
+        if (pre > RPC) {
+            issue_rows(b, 1, row, pre - RPC, RPC);
             return true;
         }
         return false;

@@ -91,8 +91,9 @@ struct StepArgs {
     uint32_t tiles_qkv, tiles_o, tiles_gu, tiles_down, tiles_lm;
     uint32_t tiles_router, tiles_egu, tiles_edown;
     int32_t attn_splits;
-    // prefetch depth before a dependency wait: register chunks per GEMV wave
-    // (1 or 2) and attention ring chunks per wave (0 .. kAttnBufs)
+    // prefetch before a dependency wait: KiB of weight rows per GEMV
+    // wavefront (whole rows, at most two register chunks) and attention ring
+    // chunks per wavefront (0 .. kAttnBufs)
     int32_t gemv_pre, attn_pre;
     int32_t poll_wave_prefetch;  // 1: the polling wave (0) also prefetches before its wait
     int32_t wave0_input;         // 1: inputs copied to LDS by wave 0 alone (coherent DMA); 0: all waves load

@@ -141,6 +141,7 @@ __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
             const MBG_GLOBAL uint32_t* line = gp(a->ctr) + ((size_t)idx * kCtrLines + (lane & (kCtrLines - 1))) * kLineU32;
             const MBG_GLOBAL uint32_t* src = lane == (int)kCtrLines ? gp(a->status) : line;
             const uint64_t t0 = wall_clock64();
+            uint32_t rounds = 0;
             while (true) {
                 uint32_t v = lane <= (int)kCtrLines ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
                 const uint32_t st = __builtin_amdgcn_readlane(v, kCtrLines);
@@ -150,7 +151,8 @@ __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
                 const uint32_t sum = __builtin_amdgcn_readfirstlane(v);
                 if ((int32_t)(sum - target) >= 0) break;
                 if (st != 0u) { ok = 0; break; }
-                if (wall_clock64() - t0 > a->deadline_ticks) {
+                // the clock is a scalar memory read: consult it every 32nd round
+                if ((++rounds & 31u) == 0u && wall_clock64() - t0 > a->deadline_ticks) {
                     if (lane == 0) latch_error(a->status, kStatusTimeout);
                     ok = 0;
                     break;
@@ -351,6 +353,13 @@ __device__ __forceinline__ f32x4 bf16x4(const MBG_GLOBAL u32x2* p) {
     return o;
 }
 
+// Rows of its stream a wavefront issues before it waits for its input: the
+// prefetch budget (KiB per wavefront) rounded up to whole rows.
+template <class RS>
+__device__ __forceinline__ int gemv_pre_rows(CArgs* a) {
+    return (a->gemv_pre * 1024 + RS::kRowBytes - 1) / RS::kRowBytes;
+}
+
 __shared__ uint64_t s_stamp[4];  // trace: input loaded, stream finished, two op-specific points
 __device__ __forceinline__ void stamp(int k) {
     if (threadIdx.x == 0) s_stamp[k] = wall_clock64();
@@ -387,9 +396,9 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
     using RS = RowStream<F_BF16, NC, H / 8>;
     RS st(2 * nunits, lane);
     typename RS::Buf A, B;
-    bool b_issued = false;
+    int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
+    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
     // RoPE (cos, sin) of this lane's epilogue items (at most two per lane:
     // nunits * NC <= 2 * kWave), loaded before the wait: positions are known
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -417,7 +426,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
         dma_input(a, a->xres, NC * H, xs);
         norm_in_place<NC, H>(a, L->attn_norm, xs);
     }
-    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
+    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
     // row sums -> per-wave LDS slots; RoPE and the cache write run after the stream
     lds_f32* res = xs + NC * H + wave * kQkvRowsPerWave * NC;  // [rows][NC]
@@ -427,7 +436,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
             for (int c = 0; c < NC; ++c) res[rr * NC + c] = s[c];
         }
     };
-    st.run(A, B, rowf, xs, H, out, b_issued);
+    st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     __syncthreads();
     const MBG_GLOBAL int32_t* ptab = gp(a->page_table);
@@ -824,51 +833,52 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     // split partials, normalised by their weighted sum.
     const int nsv = min(S_, (n_tok + T - 1) / T);   // splits that wrote partials
     const int nch_ = ncol * GQ;                      // (column, head) rows
-    lds_f32* wts = smem;                             // [4 * GQ][64]: m, then weights
-    lds_f32* lsm = smem + 4 * GQ * 64;               // [4 * GQ][64]: l
-    lds_f32* tot = smem + 8 * GQ * 64;               // [4 * GQ]: weighted sum of l
-    lds_f32* accl = tot + 4 * GQ;                    // [kThreads][4]: group partial sums
-    // stage 1: (m, l) of every (row, split), eight loads per thread in flight
-    const int nml = nch_ * nsv;
-    for (int i0 = 0; i0 < nml; i0 += 8 * kThreads) {
+    constexpr int HDV = HD / 4;                      // 16-byte vectors of o
+    constexpr int RV = HDV + 1;                      // vectors of a partial row: o, then (m, l, pad)
+    // stage 1: in one batch of loads, the whole partial rows of the group when
+    // they fit in the (now idle) ring area, else their (m, l) only
+    const bool whole = (size_t)nch_ * nsv * RV * 16 + (size_t)nch_ * 65 * 4 <= (size_t)kAttnRingBytes;
+    const int vpr = whole ? RV : 1;                  // vectors held per (row, split)
+    lds_f32* prt = smem;                             // [nch_][nsv][vpr] vectors
+    lds_f32* wts = prt + (size_t)nch_ * nsv * vpr * 4;   // [nch_][64]: weights
+    lds_f32* tot = wts + nch_ * 64;                  // [nch_]: weighted sum of l
+    lds_f32* accl = smem + kAttnRingBytes / 4;       // [kThreads][4]: group partial sums (merge area)
+    const int nload = nch_ * nsv * vpr;
+    for (int i0 = 0; i0 < nload; i0 += 8 * kThreads) {
         f32x4 t[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-            const int idx = min(i0 + k * kThreads + (int)threadIdx.x, nml - 1);
-            const int ch = idx / nsv, sp = idx - ch * nsv;
+            const int idx = min(i0 + k * kThreads + (int)threadIdx.x, nload - 1);
+            const int rs = idx / vpr, v = idx - rs * vpr;
+            const int ch = rs / nsv, sp = rs - ch * nsv;
             const int col = ch / GQ, h = ch - col * GQ;
-            t[k] = ldc4(rp, (uint32_t)(((((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + HD) * 4));
+            const int vec = whole ? v : HDV;
+            t[k] = ldc4(rp, (uint32_t)(((((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + vec * 4) * 4));
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
             const int idx = i0 + k * kThreads + (int)threadIdx.x;
-            if (idx < nml) {
-                const int ch = idx / nsv, sp = idx - ch * nsv;
-                wts[ch * 64 + sp] = t[k][0];
-                lsm[ch * 64 + sp] = t[k][1];
-            }
+            if (idx < nload) *reinterpret_cast<MBG_LDS f32x4*>(prt + 4 * idx) = t[k];
         }
     }
     __syncthreads();
-    // stage 2: per row, the merge weights in split order
-    for (int ch = threadIdx.x; ch < nch_; ch += kThreads) {
-        float M = -INFINITY;
-        for (int sp = 0; sp < nsv; ++sp) M = fmaxf(M, wts[ch * 64 + sp]);
-        float Lsum = 0.f;
-        for (int sp = 0; sp < nsv; ++sp) {
-            const float ms = wts[ch * 64 + sp];
-            const float w = ms == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms - M);
-            wts[ch * 64 + sp] = w;
-            Lsum = fmaf(w, lsm[ch * 64 + sp], Lsum);
-        }
-        tot[ch] = Lsum;
+    // stage 2: one wavefront per row, one lane per split: the maximum, the
+    // weights and their l-weighted sum are wavefront reductions
+    for (int ch = wave; ch < nch_; ch += kWaves) {
+        const bool act = lane < nsv;
+        const lds_f32* ml = prt + ((size_t)(ch * nsv + (act ? lane : 0)) * vpr + (whole ? HDV : 0)) * 4;
+        const float m = act ? ml[0] : -INFINITY;
+        const float M = wave_max(m);
+        const float w = m == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m - M);
+        const float ls = wave_sum(act ? w * ml[1] : 0.f);
+        if (act) wts[ch * 64 + lane] = w;
+        if (lane == 0) tot[ch] = ls;
     }
     __syncthreads();
     stamp(3);
-    // stage 3: weighted sum of the partial o rows.  A thread owns one 16-byte
-    // slice of a row and every ng-th split; ng thread groups then add up in
-    // group order.
-    constexpr int HDV = HD / 4;
+    // stage 3: weighted sum of the partial o rows (from LDS, or loaded now).
+    // A thread owns one 16-byte slice of a row and every ng-th split; ng
+    // thread groups then add up in group order.
     const int pairs = nch_ * HDV;
     const int fit = kThreads / pairs;
     const int ng = fit >= 8 ? 8 : fit >= 4 ? 4 : fit >= 2 ? 2 : 1;
@@ -887,7 +897,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int sp = min(i0 + k * ng, nsv - 1);
-                v[k] = ldc4(rp, (uint32_t)(((row0 + sp) * stride + vec * 4) * 4));
+                v[k] = whole ? *reinterpret_cast<const MBG_LDS f32x4*>(prt + ((size_t)(ch * nsv + sp) * RV + vec) * 4)
+                             : ldc4(rp, (uint32_t)(((row0 + sp) * stride + vec * 4) * 4));
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -936,12 +947,12 @@ __device__ __forceinline__ bool op_oproj(CArgs* a, uint32_t layer, uint32_t tile
     using RS = RowStream<F_BF16, NC, K / 8>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
-    bool b_issued = false;
+    int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
+    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->attn, NC * K, xs);
-    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
+    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
     int tok[NC];
 #pragma unroll
@@ -960,7 +971,7 @@ __device__ __forceinline__ bool op_oproj(CArgs* a, uint32_t layer, uint32_t tile
         const float res = layer == 0 ? bf16_to_f32(emb[(size_t)tk_ * H + r]) : ldc(x + c * H + r);
         stc(x + c * H + r, res + v);
     };
-    st.run(A, B, rowf, xs, K, out, b_issued);
+    st.run(A, B, rowf, xs, K, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     release_counter(a, ctr_index(layer, PH_OPROJ));
     return true;
@@ -984,13 +995,13 @@ __device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t til
     using RS = RowStream<F_BF16, NC, H / 8>;
     RS st(2 * nunits, lane);
     typename RS::Buf A, B;
-    bool b_issued = false;
+    int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
+    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->xres, NC * H, xs);
     norm_in_place<NC, H>(a, L->ffn_norm, xs);
-    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
+    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
     MBG_GLOBAL float* hb = gp(a->hbuf);
     float gate[NC];
@@ -1009,7 +1020,7 @@ __device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t til
         const int f = gw + nw * (rr >> 1);
         stc(hb + (size_t)c * F + f, gv / (1.0f + expf(-gv)) * uv);
     };
-    st.run(A, B, rowf, xs, H, out, b_issued);
+    st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     release_counter(a, ctr_index(layer, PH_GATEUP));
     return true;
@@ -1030,12 +1041,12 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
     using RS = RowStream<F_BF16, NC, F / 8>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
-    bool b_issued = false;
+    int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
+    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->hbuf, NC * F, xs);
-    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
+    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
     MBG_GLOBAL float* x = gp(a->xres);
     auto out = [&](int rr, const float (&s)[NC]) {
@@ -1048,7 +1059,7 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
         const int r = gw + nw * rr;
         stc(x + c * H + r, ldc(x + c * H + r) + v);
     };
-    st.run(A, B, rowf, xs, F, out, b_issued);
+    st.run(A, B, rowf, xs, F, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     release_counter(a, ctr_index(layer, PH_DOWN));
     return true;
@@ -1198,13 +1209,13 @@ __device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t til
     using RS = RowStream<F_BF16, NC, H / 8>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
-    bool b_issued = false;
+    int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
+    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->xres, NC * H, xs);
     norm_in_place<NC, H>(a, L->ffn_norm, xs);
-    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
+    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
     MBG_GLOBAL float* rl = gp(a->rlogits);
     auto out = [&](int rr, const float (&s)[NC]) {
@@ -1212,7 +1223,7 @@ __device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t til
         for (int c = 0; c < NC; ++c)
             if (lane == c) stc(rl + (size_t)c * E + gw + nw * rr, s[c]);
     };
-    st.run(A, B, rowf, xs, H, out, b_issued);
+    st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     release_counter(a, ctr_index(layer, PH_ROUTER));
     return true;
@@ -1412,13 +1423,13 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     using RS = RowStream<F, NC, H / E>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
-    bool b_issued = false;
+    int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);
+    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->xres, NC * H, xs);
     norm_in_place<NC, H>(a, a->final_norm, xs);
-    if (!early) b_issued = st.prefetch(A, B, rowf, a->gemv_pre);   // after the input loads, not ahead of them
+    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
     unsigned long long best[NC];
 #pragma unroll
@@ -1436,7 +1447,7 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
             best[c] = k > best[c] ? k : best[c];
         }
     };
-    st.run(A, B, rowf, xs, H, out, b_issued);
+    st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     if (lane == 0) {
 #pragma unroll
@@ -1580,12 +1591,13 @@ const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out) 
         if (v.qdim > kmax) kmax = v.qdim;
         if (v.moe_ffn > kmax) kmax = v.moe_ffn;
         const int xs_bytes = ncol * kmax * 4 + kWaves * kQkvRowsPerWave * ncol * 4;
-        const int red_bytes = kAttnRingBytes + kWaves * v.group * (v.head_dim + kPartPad) * 4;
-        const int comb_bytes = (8 * v.group * 64 + 4 * v.group) * 4 + kThreads * 16;
+        // attention: rings (reused by the combine), then the cross-wave merge
+        // rows or the combine's group sums, whichever is larger
+        const int merge_bytes = kWaves * v.group * (v.head_dim + kPartPad) * 4;
+        const int red_bytes = kAttnRingBytes + (merge_bytes > kThreads * 16 ? merge_bytes : kThreads * 16);
         const int moe_bytes = v.moe ? ncol * kSlotsPerPass * v.moe_ffn * 4 : 0;
         int m = xs_bytes > red_bytes ? xs_bytes : red_bytes;
-        m = m > moe_bytes ? m : moe_bytes;
-        *lds_bytes_out = m > comb_bytes ? m : comb_bytes;
+        *lds_bytes_out = m > moe_bytes ? m : moe_bytes;
     }
     return fn;
 }
