@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -50,11 +51,16 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Workspace sections, in bytes from the base.
 struct Plan {
-    size_t status, keys, ctr, head_ctr, task_off, tasks, layers, inv_freq, rope_cs;
+    size_t keys, head_ctr, task_off, tasks, layers, inv_freq, rope_cs;
     size_t xres, qbuf, part, attn, hbuf, rlogits, route_w, route_idx, trace, total;
     int64_t hb_ld;
     size_t n_ctr, max_tasks, zero_bytes;
+    size_t uc_bytes;   // library-owned uncached block: status word, LM-head counter, dependency counters
 };
+
+// Bytes of the uncached block: one 128-byte line for the status word and the
+// LM-head counter, then the dependency counters.
+constexpr size_t kUcCtrOffset = 128;
 
 Plan make_plan(const mbg_config& c) {
     Plan p{};
@@ -66,11 +72,10 @@ Plan make_plan(const mbg_config& c) {
         off = align_up(off + bytes, 256);
         return o;
     };
-    p.status = take(16);
     p.keys = take(8 * 4);
     p.n_ctr = L * PH_COUNT;
-    p.ctr = take(4 * kLineU32 * kCtrLines * p.n_ctr);
-    p.head_ctr = take(4 * kLineU32 * L * (size_t)c.n_kv_heads);   // one line per (layer, KV head)
+    p.uc_bytes = kUcCtrOffset + 4 * kLineU32 * kCtrLines * p.n_ctr;
+    p.head_ctr = take(4 * kLineU32 * L * (size_t)c.n_q_heads);   // one line per (layer, KV head, head group)
     p.zero_bytes = off;  // everything above starts at zero
     p.task_off = take(4 * (kMaxGrid + 1));
     p.max_tasks = (size_t)kMaxGrid * (8 * L + 1);
@@ -95,6 +100,38 @@ Plan make_plan(const mbg_config& c) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Uncached device memory for the dependency counters and the status word
+// (the step kernel polls them with cache-bypassing scalar loads, which
+// return the memory-side value only for memory the L2 does not cache).
+// Uncached blocks are not handed back to the runtime once a kernel has read
+// them: a destroyed context returns its block to this process-wide pool and
+// later contexts on the same device reuse it.
+struct UcBlock {
+    int dev;
+    size_t bytes;
+    void* p;
+};
+std::mutex g_uc_mu;
+std::vector<UcBlock> g_uc_free;
+
+hipError_t uc_acquire(int dev, size_t bytes, void** out) {
+    std::lock_guard<std::mutex> lk(g_uc_mu);
+    for (size_t i = 0; i < g_uc_free.size(); ++i) {
+        if (g_uc_free[i].dev == dev && g_uc_free[i].bytes >= bytes) {
+            *out = g_uc_free[i].p;
+            g_uc_free.erase(g_uc_free.begin() + (long)i);
+            return hipSuccess;
+        }
+    }
+    return hipExtMallocWithFlags(out, bytes, hipDeviceMallocUncached);
+}
+
+void uc_release(int dev, size_t bytes, void* p) {
+    if (!p) return;
+    std::lock_guard<std::mutex> lk(g_uc_mu);
+    g_uc_free.push_back(UcBlock{dev, bytes, p});
+}
 
 int check_tensor(const mbg_tensor& t, const char* name, int dtype, int64_t n, int64_t rows, int64_t cols) {
     if (t.data == nullptr) return fail(MBG_E_INVALID_ARG, "%s: data is NULL", name);
@@ -184,6 +221,9 @@ struct mbg_ctx {
     int n_tasks;
     int trace_on;
     int last_ncol;   // columns of the last step/verify call (0: none yet)
+    void* uc;        // uncached block (counters, status), from the pool
+    size_t uc_bytes;
+    int dev;
     unsigned long long* trace_buf;
     char variant[64];
 };
@@ -377,7 +417,11 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
         }
     }
     const uint32_t tiles_last = moe ? a.tiles_edown : a.tiles_down;   // producers of the residual update
-    int S = G / c.n_kv_heads;
+    // attention tasks: (KV head, head group of at most kAttnHeadsPerTask
+    // query heads, split); the splits fill the grid
+    const int gq = c.n_q_heads / c.n_kv_heads;
+    const int head_groups = gq / std::min(gq, kAttnHeadsPerTask);
+    int S = G / (c.n_kv_heads * head_groups);
     S = std::max(1, std::min(S, kMaxSplits));
     S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 128)));   // >= ~128 positions per split
     a.attn_splits = S;
@@ -391,7 +435,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     if (const char* e = getenv("MBG_POLL_WAVE_PREFETCH")) a.poll_wave_prefetch = atoi(e) != 0;
     if (const char* e = getenv("MBG_WAVE0_INPUT")) a.wave0_input = atoi(e) != 0;
     if (const char* e = getenv("MBG_ATTN_PREFETCH")) a.attn_pre = std::max(0, std::min(kAttnBufsHost, atoi(e)));
-    const uint32_t tiles_attn = (uint32_t)(c.n_kv_heads * S);
+    const uint32_t tiles_attn = (uint32_t)(c.n_kv_heads * head_groups * S);
 
     // task lists
     std::vector<uint32_t> off(G + 1, 0);
@@ -405,7 +449,8 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
             if (t < a.tiles_qkv)
                 tasks.push_back(Task{OP_QKV | L8, t, l == 0 ? kNoWait : ci(l - 1, PH_DOWN), l == 0 ? 0u : tiles_last});
             if (t < tiles_attn) tasks.push_back(Task{OP_ATTN | L8, t, ci(l, PH_QKV), a.tiles_qkv});
-            if (t < a.tiles_o) tasks.push_back(Task{OP_OPROJ | L8, t, ci(l, PH_ATTN), (uint32_t)c.n_kv_heads});
+            if (t < a.tiles_o)
+                tasks.push_back(Task{OP_OPROJ | L8, t, ci(l, PH_ATTN), (uint32_t)(c.n_kv_heads * head_groups)});
             if (!moe) {
                 if (t < a.tiles_gu) tasks.push_back(Task{OP_GATEUP | L8, t, ci(l, PH_OPROJ), a.tiles_o});
                 if (t < a.tiles_down) tasks.push_back(Task{OP_DOWN | L8, t, ci(l, PH_GATEUP), a.tiles_gu});
@@ -465,10 +510,19 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     for (int i = 0; i < HALF; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
 
     char* base = static_cast<char*>(d_ws);
-    a.status = (uint32_t*)(base + plan.status);
+    void* uc = nullptr;
+    hipError_t eu = uc_acquire(dev, plan.uc_bytes, &uc);
+    if (eu != hipSuccess) {
+        delete x;
+        return hip_fail(eu, "uncached counter block");
+    }
+    x->uc = uc;
+    x->uc_bytes = plan.uc_bytes;
+    x->dev = dev;
+    a.status = (uint32_t*)uc;
     a.lm_ctr = a.status + 1;
     a.amax_keys = (unsigned long long*)(base + plan.keys);
-    a.ctr = (uint32_t*)(base + plan.ctr);
+    a.ctr = (uint32_t*)((char*)uc + kUcCtrOffset);
     a.head_ctr = (uint32_t*)(base + plan.head_ctr);
     a.task_off = (const uint32_t*)(base + plan.task_off);
     a.tasks = (const Task*)(base + plan.tasks);
@@ -499,6 +553,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.kv_layer_stride = (int64_t)kv->n_pages * 2 * c.n_kv_heads * c.page_size * c.head_dim;
 
     hipError_t e = launch_fill_u32((uint32_t*)base, plan.zero_bytes / 4, 0u, s);
+    if (e == hipSuccess) e = launch_fill_u32((uint32_t*)uc, plan.uc_bytes / 4, 0u, s);
     if (e == hipSuccess) e = hipMemcpyAsync(base + plan.task_off, off.data(), 4 * off.size(), hipMemcpyHostToDevice, s);
     if (e == hipSuccess)
         e = hipMemcpyAsync(base + plan.tasks, tasks.data(), sizeof(Task) * tasks.size(), hipMemcpyHostToDevice, s);
@@ -509,6 +564,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
         e = launch_rope_table((const double*)(base + plan.inv_freq), HALF, c.max_pos, (float2*)(base + plan.rope_cs), s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
+        uc_release(dev, plan.uc_bytes, uc);
         delete x;
         return hip_fail(e, "workspace upload");
     }
@@ -620,7 +676,14 @@ int mbg_read_routing(mbg_ctx* x, int32_t layer, int32_t* idx, float* weights, in
     return MBG_OK;
 }
 
-void mbg_destroy(mbg_ctx* x) { delete x; }
+void mbg_destroy(mbg_ctx* x) {
+    if (!x) return;
+    // the context's last launch must be done with the counters before another
+    // context reuses the block
+    (void)hipStreamSynchronize(x->stream);
+    uc_release(x->dev, x->uc_bytes, x->uc);
+    delete x;
+}
 
 // ------------------------------------------------------- standalone ops
 

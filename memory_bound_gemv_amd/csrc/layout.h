@@ -45,9 +45,14 @@ constexpr uint32_t kNoWait = 0xFFFFFFFFu;
 // to line (workgroup % kCtrLines) and a waiter sums all lines.  Same-address
 // atomics from hundreds of workgroups serialise at the memory side; spreading
 // them over lines keeps an all-to-all dependency point near two memory round
-// trips.
-constexpr uint32_t kCtrLines = 16;
+// trips.  Counters and the status word sit in uncached device memory, where
+// a waiter reads all lines with one batch of scalar loads.
+constexpr uint32_t kCtrLines = 8;
 constexpr uint32_t kLineU32 = 32;
+
+// Query heads per attention task (a KV head's larger group is split into
+// several tasks that read the same history).
+constexpr int kAttnHeadsPerTask = 2;
 
 // MoE limits of the compiled kernels.
 constexpr int kMaxExperts = 512;                 // routed experts (a multiple of 8)
@@ -113,10 +118,10 @@ struct StepArgs {
     // workspace
     const Task* tasks;
     const uint32_t* task_off;  // [grid + 1]
-    uint32_t* ctr;             // [n_layers * PH_COUNT + extra]
+    uint32_t* ctr;             // [n_layers * PH_COUNT][kCtrLines lines], uncached memory
     uint32_t* head_ctr;        // [n_layers * n_kv_heads] split arrivals
     uint32_t* lm_ctr;          // LM-head tiles finished
-    uint32_t* status;          // first device error
+    uint32_t* status;          // first device error (uncached memory, beside the LM-head counter)
     float* xres;               // [k][H] residual stream
     float* qbuf;               // [k][Hq][d]
     float* part;               // [k][Hq][splits][d + 2] attention partials

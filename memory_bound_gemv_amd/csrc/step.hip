@@ -127,10 +127,45 @@ __device__ __forceinline__ void release_before_signal() {
 #endif
 }
 
+// The kCtrLines lines of counter `lines` (128 bytes apart) and the status
+// word, in one batch of scalar loads with the cache-bypass bit.  Counters
+// and status live in uncached memory, so these loads return the memory-side
+// values; on the scalar path they do not queue behind the vector loads this
+// CU has in flight, which under a full HBM stream delay a vector poll by
+// about a microsecond.
+__device__ __forceinline__ void sload_counter(const uint32_t* lines, const uint32_t* status, uint32_t& sum,
+                                              uint32_t& st) {
+    static_assert(kCtrLines == 8 && kLineU32 == 32, "counter layout");
+    // both addresses are wave-uniform: make them scalar operands
+    auto uni = [](const uint32_t* p) {
+        const uint64_t v = (uint64_t)(uintptr_t)p;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+        return ((uint64_t)hi << 32) | lo;
+    };
+    const uint64_t la = uni(lines), sa = uni(status);
+    uint32_t c0, c1, c2, c3, c4, c5, c6, c7, s;
+    asm volatile(
+        "s_load_dword %0, %9, 0x0 glc\n\t"
+        "s_load_dword %1, %9, 0x80 glc\n\t"
+        "s_load_dword %2, %9, 0x100 glc\n\t"
+        "s_load_dword %3, %9, 0x180 glc\n\t"
+        "s_load_dword %4, %9, 0x200 glc\n\t"
+        "s_load_dword %5, %9, 0x280 glc\n\t"
+        "s_load_dword %6, %9, 0x300 glc\n\t"
+        "s_load_dword %7, %9, 0x380 glc\n\t"
+        "s_load_dword %8, %10, 0x0 glc\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&s"(c0), "=&s"(c1), "=&s"(c2), "=&s"(c3), "=&s"(c4), "=&s"(c5), "=&s"(c6), "=&s"(c7), "=&s"(s)
+        : "s"(la), "s"(sa)
+        : "memory");
+    sum = ((c0 + c1) + (c2 + c3)) + ((c4 + c5) + (c6 + c7));
+    st = s;
+}
+
 // Wait until counter `idx` (the sum of its kCtrLines lines) reaches
-// epoch * need (mod 2^32).  Wave 0 polls, one line per lane plus the status
-// word in one load instruction; the other waves wait at the barrier.  Returns
-// false when the launch is aborting.
+// epoch * need (mod 2^32).  Wave 0 polls; the other waves wait at the
+// barrier.  Returns false when the launch is aborting.
 __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
     __shared__ int s_ok;
     if (threadIdx.x < kWave) {
@@ -138,17 +173,12 @@ __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
         int ok = 1;
         if (idx != kNoWait) {
             const uint32_t target = a->epoch * need;
-            const MBG_GLOBAL uint32_t* line = gp(a->ctr) + ((size_t)idx * kCtrLines + (lane & (kCtrLines - 1))) * kLineU32;
-            const MBG_GLOBAL uint32_t* src = lane == (int)kCtrLines ? gp(a->status) : line;
+            const uint32_t* lines = a->ctr + (size_t)idx * kCtrLines * kLineU32;
             const uint64_t t0 = wall_clock64();
             uint32_t rounds = 0;
             while (true) {
-                uint32_t v = lane <= (int)kCtrLines ? __hip_atomic_load(src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0u;
-                const uint32_t st = __builtin_amdgcn_readlane(v, kCtrLines);
-                if (lane >= (int)kCtrLines) v = 0u;
-#pragma unroll
-                for (int m = kCtrLines / 2; m >= 1; m >>= 1) v += (uint32_t)__shfl_xor((int)v, m, kWave);
-                const uint32_t sum = __builtin_amdgcn_readfirstlane(v);
+                uint32_t sum, st;
+                sload_counter(lines, a->status, sum, st);
                 if ((int32_t)(sum - target) >= 0) break;
                 if (st != 0u) { ok = 0; break; }
                 // the clock is a scalar memory read: consult it every 32nd round
@@ -503,6 +533,10 @@ __device__ __forceinline__ void merge_weights(float m1, float m2, float& mn, flo
     w2 = m2 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m2 - mn);
 }
 
+// Query heads one attention task handles: at most two, so that the task's
+// online-softmax state stays in registers; larger groups are split.
+constexpr int attn_heads(int gq) { return gq < kAttnHeadsPerTask ? gq : kAttnHeadsPerTask; }
+
 // Online-softmax state of one lane: GQ query heads, EPC dims of the output.
 // Scores are in the log2 domain (q is pre-scaled by log2(e) / sqrt(d)).
 template <int GQ, int EPC, int LPT, int KVF>
@@ -596,15 +630,18 @@ __device__ __forceinline__ void wait_chunks(int k) {
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(6 * kAttnUnits));
 }
 
-// One (KV head, split) task: split-KV attention for the GQ query heads that
-// share KV head g, over positions [t0, t1) of the split, for every column of
-// the window.  History (positions < pos) streams straight from HBM into the
+// One (KV head, head group, split) task: split-KV attention for GH of the
+// query heads that share KV head g (head group hg of the GH / GH groups),
+// over positions [t0, t1) of the split, for every column of the window.  History (positions < pos) streams straight from HBM into the
 // wave's LDS ring (global_load_lds_dwordx4); up to kAttnBufs chunks are
 // requested before the task waits for this step's q and new K/V.
 template <int NC, class S>
 __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                         lds_f32* smem) {
-    constexpr int HD = S::HD, GQ = S::GQ, KVF = S::KVF;
+    constexpr int HD = S::HD, KVF = S::KVF;
+    constexpr int GH = attn_heads(S::GQ);    // query heads per task
+    constexpr int HG = S::GQ / GH;           // head groups per KV head
+    static_assert(S::GQ % GH == 0, "query-head groups");
     constexpr int EB = KVF == F_BF16 ? 2 : 1;
     constexpr int LPT = HD * EB / 16;        // lanes per token row
     constexpr int EPC = 16 / EB;             // elements per lane
@@ -614,13 +651,15 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     constexpr int stride = HD + kPartPad;
     static_assert(LPT == 4 || LPT == 8 || LPT == 16, "row layout");
     static_assert(EPC % 4 == 0, "lane slice");
-    using Lane = AttnLane<GQ, EPC, LPT, KVF>;
+    using Lane = AttnLane<GH, EPC, LPT, KVF>;
     const int lane = lane_id();
     const int wave = wave_id();
     const int Hq = a->n_q_heads, Hkv = a->n_kv_heads;
     const int S_ = a->attn_splits;
-    const int g = (int)tile / S_;
-    const int s = (int)tile - g * S_;
+    const int gg = (int)tile / S_;           // (KV head, head group)
+    const int s = (int)tile - gg * S_;
+    const int g = gg / HG;
+    const int qh0 = g * S::GQ + (gg - g * HG) * GH;   // first query head of the task
     const int pos = a->pos, ncol = a->ncol, page_size = a->page_size;
     const int n_tok = pos + ncol;
     // split length: a whole number of workgroup token slots, so that every
@@ -686,10 +725,10 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const bool empty = t0 >= t1;
     for (int col = 0; col < ncol && !empty; ++col) {
         const int te = min(t1, pos + col + 1);
-        float q[GQ][EPC];
+        float q[GH][EPC];
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-            const uint32_t qo = (uint32_t)((((size_t)col * Hq + g * GQ + h) * HD + cidx * EPC) * 4);
+        for (int h = 0; h < GH; ++h) {
+            const uint32_t qo = (uint32_t)((((size_t)col * Hq + qh0 + h) * HD + cidx * EPC) * 4);
 #pragma unroll
             for (int e = 0; e < EPC; e += 4) {
                 const f32x4 t = ldc4(rq, qo + 4u * e);
@@ -741,7 +780,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         }
         if constexpr (KVF == F_FP8) {
 #pragma unroll
-            for (int h = 0; h < GQ; ++h)
+            for (int h = 0; h < GH; ++h)
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) st.o[h][e] *= vsc;
         }
@@ -749,7 +788,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
 #pragma unroll
         for (int msk = LPT; msk < kWave; msk <<= 1) {
 #pragma unroll
-            for (int h = 0; h < GQ; ++h) {
+            for (int h = 0; h < GH; ++h) {
                 const float m2 = shfl_xor_f(st.m[h], msk);
                 const float l2 = shfl_xor_f(st.l[h], msk);
                 float mn, w1, w2;
@@ -766,8 +805,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         // then the waves, through LDS, in wave order
         if (lane < LPT) {
 #pragma unroll
-            for (int h = 0; h < GQ; ++h) {
-                lds_f32* r = red + ((size_t)wave * GQ + h) * stride;
+            for (int h = 0; h < GH; ++h) {
+                lds_f32* r = red + ((size_t)wave * GH + h) * stride;
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) r[cidx * EPC + e] = st.o[h][e];
                 if (cidx == 0) {
@@ -779,13 +818,13 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         __syncthreads();
         if (wave == 0 && lane < LPT) {
 #pragma unroll
-            for (int h = 0; h < GQ; ++h) {
+            for (int h = 0; h < GH; ++h) {
                 float M = red[h * stride + HD], Ls = red[h * stride + HD + 1];
                 float O[EPC];
 #pragma unroll
                 for (int e = 0; e < EPC; ++e) O[e] = red[h * stride + cidx * EPC + e];
                 for (int w = 1; w < kWaves; ++w) {
-                    const lds_f32* r = red + ((size_t)w * GQ + h) * stride;
+                    const lds_f32* r = red + ((size_t)w * GH + h) * stride;
                     float mn, w1, w2;
                     merge_weights(M, r[HD], mn, w1, w2);
                     Ls = Ls * w1 + r[HD + 1] * w2;
@@ -793,7 +832,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
                     for (int e = 0; e < EPC; ++e) O[e] = O[e] * w1 + r[cidx * EPC + e] * w2;
                     M = mn;
                 }
-                const uint32_t row = (uint32_t)((((size_t)col * Hq + g * GQ + h) * S_ + s) * stride * 4);
+                const uint32_t row = (uint32_t)((((size_t)col * Hq + qh0 + h) * S_ + s) * stride * 4);
 #pragma unroll
                 for (int e = 0; e < EPC; e += 4) {
                     f32x4 t;
@@ -822,7 +861,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     __syncthreads();
     if (threadIdx.x == 0) {
         release_before_signal();
-        const uint32_t old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv + g) * kLineU32, 1u,
+        const uint32_t old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv * HG + gg) * kLineU32, 1u,
                                                     __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old + 1u == a->epoch * (uint32_t)S_);
         if (s_last) acquire_after_wait();
@@ -832,7 +871,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     // Combine: softmax over [0, pos + col] = weights exp2(m_s - M) on the
     // split partials, normalised by their weighted sum.
     const int nsv = min(S_, (n_tok + T - 1) / T);   // splits that wrote partials
-    const int nch_ = ncol * GQ;                      // (column, head) rows
+    const int nch_ = ncol * GH;                      // (column, head) rows
     constexpr int HDV = HD / 4;                      // 16-byte vectors of o
     constexpr int RV = HDV + 1;                      // vectors of a partial row: o, then (m, l, pad)
     // stage 1: in one batch of loads, the whole partial rows of the group when
@@ -851,9 +890,9 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             const int idx = min(i0 + k * kThreads + (int)threadIdx.x, nload - 1);
             const int rs = idx / vpr, v = idx - rs * vpr;
             const int ch = rs / nsv, sp = rs - ch * nsv;
-            const int col = ch / GQ, h = ch - col * GQ;
+            const int col = ch / GH, h = ch - col * GH;
             const int vec = whole ? v : HDV;
-            t[k] = ldc4(rp, (uint32_t)(((((size_t)col * Hq + g * GQ + h) * S_ + sp) * stride + vec * 4) * 4));
+            t[k] = ldc4(rp, (uint32_t)(((((size_t)col * Hq + qh0 + h) * S_ + sp) * stride + vec * 4) * 4));
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -889,8 +928,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         const int pr = base + pl;
         const int prc = min(pr, pairs - 1);
         const int ch = prc / HDV, vec = prc - ch * HDV;
-        const int col = ch / GQ, h = ch - col * GQ;
-        const size_t row0 = ((size_t)col * Hq + g * GQ + h) * S_;
+        const int col = ch / GH, h = ch - col * GH;
+        const size_t row0 = ((size_t)col * Hq + qh0 + h) * S_;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         for (int i0 = grp; i0 < nsv; i0 += 8 * ng) {
             f32x4 v[8];
@@ -922,7 +961,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             const float tt = tot[ch];
 #pragma unroll
             for (int e = 0; e < 4; ++e) sum[e] = sum[e] / tt;
-            stc4(ra, (uint32_t)((((size_t)col * Hq + g * GQ + h) * HD + vec * 4) * 4), sum);
+            stc4(ra, (uint32_t)((((size_t)col * Hq + qh0 + h) * HD + vec * 4) * 4), sum);
         }
         __syncthreads();
     }
@@ -1593,7 +1632,7 @@ const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out) 
         const int xs_bytes = ncol * kmax * 4 + kWaves * kQkvRowsPerWave * ncol * 4;
         // attention: rings (reused by the combine), then the cross-wave merge
         // rows or the combine's group sums, whichever is larger
-        const int merge_bytes = kWaves * v.group * (v.head_dim + kPartPad) * 4;
+        const int merge_bytes = kWaves * attn_heads(v.group) * (v.head_dim + kPartPad) * 4;
         const int red_bytes = kAttnRingBytes + (merge_bytes > kThreads * 16 ? merge_bytes : kThreads * 16);
         const int moe_bytes = v.moe ? ncol * kSlotsPerPass * v.moe_ffn * 4 : 0;
         int m = xs_bytes > red_bytes ? xs_bytes : red_bytes;
