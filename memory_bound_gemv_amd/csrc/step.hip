@@ -1129,6 +1129,7 @@ struct RouteLds {
     float wt[kMaxSlots][4];      // weight of a slot in each column (0: not selected)
     int sel[4][kMaxTopK];
     float selw[4][kMaxTopK];
+    uint32_t layer, epoch;       // the routing these fields hold
 };
 __shared__ RouteLds s_route;
 
@@ -1149,7 +1150,7 @@ __device__ __forceinline__ uint32_t ordered_key32(float f) {
 // exp(r_j - r_max) / sum over the picked j, which equals the picked softmax
 // probabilities renormalised to sum to one.
 template <int NC>
-__device__ void route_slots(CArgs* a) {
+__device__ void route_slots(CArgs* a, uint32_t layer) {
     RouteLds& R = s_route;
     const int E = a->n_experts, K = a->top_k;
     const int lane = lane_id(), wave = wave_id();
@@ -1229,6 +1230,10 @@ __device__ void route_slots(CArgs* a) {
         const int c = threadIdx.x / a->n_shared, sh = threadIdx.x - c * a->n_shared;
         R.wt[R.nrouted + sh][c] = 1.f;
     }
+    if (threadIdx.x == 0) {
+        R.layer = layer;
+        R.epoch = a->epoch;
+    }
     __syncthreads();
 }
 
@@ -1275,23 +1280,27 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
     const int lane = lane_id(), wave = wave_id();
     CLayer* L = (CLayer*)a->layers + layer;
     if (!wait_counter(a, wctr, wneed)) return false;
-    route_slots<NC>(a);
+    route_slots<NC>(a, layer);
     const RouteLds& R = s_route;
     dma_input(a, a->xres, NC * H, xs);
     norm_in_place<NC, H>(a, L->ffn_norm, xs);
     stamp(0);
     const int E = a->n_experts;
     const int U = R.nslots;
-    const int nw = (int)a->tiles_egu * kWaves, gw = (int)tile * kWaves + wave;
+    // a workgroup owns a contiguous block of units (rows of one or two
+    // experts, so that few experts' pages pass through its address
+    // translation cache); its wavefronts interleave within the block
     const int total = U * MF;
-    const int nunits = gw < total ? (total - 1 - gw) / nw + 1 : 0;
+    const int per = (total + (int)a->tiles_egu - 1) / (int)a->tiles_egu;
+    const int u0 = (int)tile * per, u1 = min(total, u0 + per);
+    const int nunits = u0 + wave < u1 ? (u1 - 1 - u0 - wave) / kWaves + 1 : 0;
     const uint8_t* egc = L->eg_codes;
     const uint8_t* egs = L->eg_scales;
     const uint8_t* sgc = L->sg_codes;
     const uint8_t* sgs = L->sg_scales;
     constexpr size_t kMatCodes = (size_t)2 * MF * (H / 2), kMatScales = (size_t)2 * MF * (H / 32);
     auto rowf = [&](int rr) -> GRow {
-        const int u = gw + nw * (rr >> 1);
+        const int u = u0 + wave + kWaves * (rr >> 1);
         const int slot = u / MF;
         const int f = u - slot * MF;
         const int e = R.slot_exp[slot];
@@ -1319,7 +1328,7 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc)
             if (cc == c) { gv = gate[cc]; uv = s[cc]; }
-        const int u = gw + nw * (rr >> 1);
+        const int u = u0 + wave + kWaves * (rr >> 1);
         const int slot = u / MF;
         const float w = R.wt[slot][c];
         stc(hb + (size_t)c * ld + u, w * (gv / (1.0f + expf(-gv)) * uv));
@@ -1347,7 +1356,8 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
     const int lane = lane_id(), wave = wave_id();
     CLayer* L = (CLayer*)a->layers + layer;
     if (!wait_counter(a, wctr, wneed)) return false;
-    route_slots<NC>(a);
+    // this workgroup's expert gate/up task of the layer left the routing in LDS
+    if (s_route.layer != layer || s_route.epoch != a->epoch) route_slots<NC>(a, layer);
     const RouteLds& R = s_route;
     stamp(0);
     const int E = a->n_experts;
@@ -1532,7 +1542,10 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
     const MBG_CONST u32x4* tasks = (const MBG_CONST u32x4*)a->tasks;
     const uint32_t end = off[b + 1];
     MBG_GLOBAL unsigned long long* trace = a->trace ? gp(a->trace) : nullptr;
-    if (threadIdx.x == 0) s_stamp[2] = s_stamp[3] = 0;
+    if (threadIdx.x == 0) {
+        s_stamp[2] = s_stamp[3] = 0;
+        s_route.epoch = 0;   // no routing held yet (epochs start at 1)
+    }
     for (uint32_t ti = off[b]; ti < end; ++ti) {
         const u32x4 tv = tasks[ti];
         const Task tk{tv[0], tv[1], tv[2], tv[3]};
