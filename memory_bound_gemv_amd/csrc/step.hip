@@ -1279,11 +1279,14 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
     constexpr int H = S::H, MF = S::MF;
     const int lane = lane_id(), wave = wave_id();
     CLayer* L = (CLayer*)a->layers + layer;
+    // the input (the stream after the output projection) is complete before
+    // the router is: load and normalise it first, then wait for the logits
+    if (!wait_counter(a, ctr_index(layer, PH_OPROJ), a->tiles_o)) return false;
+    dma_input(a, a->xres, NC * H, xs);
+    norm_in_place<NC, H>(a, L->ffn_norm, xs);
     if (!wait_counter(a, wctr, wneed)) return false;
     route_slots<NC>(a, layer);
     const RouteLds& R = s_route;
-    dma_input(a, a->xres, NC * H, xs);
-    norm_in_place<NC, H>(a, L->ffn_norm, xs);
     stamp(0);
     const int E = a->n_experts;
     const int U = R.nslots;
@@ -1355,13 +1358,8 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
     constexpr int XLD = kSlotsPerPass * MF;          // LDS floats per column
     const int lane = lane_id(), wave = wave_id();
     CLayer* L = (CLayer*)a->layers + layer;
-    if (!wait_counter(a, wctr, wneed)) return false;
-    // this workgroup's expert gate/up task of the layer left the routing in LDS
-    if (s_route.layer != layer || s_route.epoch != a->epoch) route_slots<NC>(a, layer);
     const RouteLds& R = s_route;
-    stamp(0);
     const int E = a->n_experts;
-    const int U = R.nslots;
     const int nw = (int)a->tiles_edown * kWaves, gw = (int)tile * kWaves + wave;
     const int nrows = gw < H ? min((H - 1 - gw) / nw + 1, kMaxDownRows) : 0;
     const uint8_t* edc = L->ed_codes;
@@ -1369,26 +1367,10 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
     const uint8_t* sdc = L->sd_codes;
     const uint8_t* sds = L->sd_scales;
     constexpr size_t kMatCodes = (size_t)H * (MF / 2), kMatScales = (size_t)H * (MF / 32);
-    const rsrc_t hr = make_rsrc(a->hbuf);
-    const int ld = a->hb_ld;
-    float acc[kMaxDownRows][NC];
-#pragma unroll
-    for (int i = 0; i < kMaxDownRows; ++i)
-#pragma unroll
-        for (int c = 0; c < NC; ++c) acc[i][c] = 0.f;
-    for (int s0 = 0; s0 < U; s0 += kSlotsPerPass) {
-        const int ns = min(kSlotsPerPass, U - s0);
-        // h of this pass's slots -> LDS [c][slot][MF]
-        __syncthreads();
-        const int nvec = ns * MF / 4;
-        for (int c = 0; c < NC; ++c)
-            for (int j = threadIdx.x; j < nvec; j += kThreads)
-                *reinterpret_cast<MBG_LDS f32x4*>(xs + c * XLD + 4 * j) =
-                    ldc4(hr, (uint32_t)(((size_t)c * ld + (size_t)s0 * MF + 4 * j) * 4));
-        __syncthreads();
-        // every row's gathered vectors, all in flight at once
-        uint4 w[kMaxDownRows][NJ];
-        uint32_t sb[kMaxDownRows][NJ];
+    // every row's gathered vectors of a pass (slots s0 .. s0 + ns), all in flight at once
+    uint4 w[kMaxDownRows][NJ];
+    uint32_t sb[kMaxDownRows][NJ];
+    auto issue_pass = [&](int s0, int ns) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int v = lane + kWave * j;
@@ -1407,6 +1389,33 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
                 }
             }
         }
+    };
+    // this workgroup's expert gate/up task of the layer left the routing in
+    // LDS: then the first pass's weights are requested before the wait
+    const bool have_route = R.layer == layer && R.epoch == a->epoch;
+    if (have_route) issue_pass(0, min(kSlotsPerPass, R.nslots));
+    if (!wait_counter(a, wctr, wneed)) return false;
+    if (!have_route) route_slots<NC>(a, layer);
+    stamp(0);
+    const int U = R.nslots;
+    const rsrc_t hr = make_rsrc(a->hbuf);
+    const int ld = a->hb_ld;
+    float acc[kMaxDownRows][NC];
+#pragma unroll
+    for (int i = 0; i < kMaxDownRows; ++i)
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[i][c] = 0.f;
+    for (int s0 = 0; s0 < U; s0 += kSlotsPerPass) {
+        const int ns = min(kSlotsPerPass, U - s0);
+        // h of this pass's slots -> LDS [c][slot][MF]
+        __syncthreads();
+        const int nvec = ns * MF / 4;
+        for (int c = 0; c < NC; ++c)
+            for (int j = threadIdx.x; j < nvec; j += kThreads)
+                *reinterpret_cast<MBG_LDS f32x4*>(xs + c * XLD + 4 * j) =
+                    ldc4(hr, (uint32_t)(((size_t)c * ld + (size_t)s0 * MF + 4 * j) * 4));
+        __syncthreads();
+        if (s0 > 0 || !have_route) issue_pass(s0, ns);
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int v = lane + kWave * j;
