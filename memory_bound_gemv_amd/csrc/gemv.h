@@ -40,6 +40,7 @@ struct FmtInfo<F_FP8> { static constexpr int kEPV = 16; };
 template <>
 struct FmtInfo<F_MXFP4> { static constexpr int kEPV = 32; };
 
+
 template <class T>
 __device__ __forceinline__ MBG_GLOBAL T* gp(T* p) {
     return (MBG_GLOBAL T*)p;
@@ -123,6 +124,32 @@ struct ChunkRows {
     static constexpr int NJ = (NV + kWave - 1) / kWave;
     static constexpr int budget = (F == F_MXFP4) ? (NC <= 2 ? 8 : 4) : (NC <= 2 ? 16 : 8);
     static constexpr int value = budget / NJ > 0 ? budget / NJ : 1;
+};
+
+// Per-row binary32 scales of a wavefront's rows (its row rr is global row
+// idx(rr)) held in registers: lane l keeps rows l + 64 i, i < 4, so a row's
+// scale is one lane read instead of a memory load in the row epilogue
+// (which would wait for every load issued before it); rows from 256 on are
+// read from memory.
+struct RowScales {
+    float v[4];
+    const MBG_GLOBAL float* p;
+
+    template <class Idx>
+    __device__ __forceinline__ void load(const MBG_GLOBAL float* p_, int nrows, int lane, Idx idx) {
+        p = p_;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int rr = lane + kWave * i;
+            v[i] = rr < nrows ? p[idx(rr)] : 1.0f;
+        }
+    }
+    // rr is wave-uniform; r is its global row index
+    __device__ __forceinline__ float get(int rr, uint32_t r) const {
+        if (rr >= 4 * kWave) return p[r];
+        const float t = rr < kWave ? v[0] : rr < 2 * kWave ? v[1] : rr < 3 * kWave ? v[2] : v[3];
+        return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(t), rr & (kWave - 1)));
+    }
 };
 
 // One wavefront streams `nrows` rows (its own numbering; `row(rr)` gives the

@@ -21,8 +21,8 @@ __device__ __forceinline__ unsigned long long argmax_key(float f, uint32_t row) 
 
 // ------------------------------------------------------------- LM head
 
-// Every wavefront of the grid owns rows gw, gw + n_waves, ... of the head
-// and streams them back to back; one argmax key per workgroup is merged with
+// Workgroup b owns a contiguous block of rows of the head and its four
+// wavefronts take every fourth row of it, streamed back to back; one argmax key per workgroup is merged with
 // a 64-bit atomic max, and the last workgroup turns the keys into indices.
 template <int F, int NC, int H>
 __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
@@ -34,13 +34,15 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
     constexpr int NV = H / E;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int nw = gridDim.x * 4;
-    const int gw = blockIdx.x * 4 + wave;
-    const int nrows = gw < a.V ? (a.V - 1 - gw) / nw + 1 : 0;
+    // a workgroup owns a contiguous block of rows (few pages per address
+    // translation cache); its wavefronts interleave within the block
+    const int per = (int)((a.V + (int)gridDim.x - 1) / (int)gridDim.x);
+    const int r0 = (int)blockIdx.x * per + wave, r1 = min(a.V, (int)blockIdx.x * per + per);
+    const int nrows = r0 < r1 ? (r1 - 1 - r0) / 4 + 1 : 0;
     const MBG_GLOBAL uint4* W = gp(reinterpret_cast<const uint4*>(a.w));
     const MBG_GLOBAL uint8_t* Ws = gp(reinterpret_cast<const uint8_t*>(a.wscale));   // MXFP4: E8M0 [V][H/32]
     auto rowf = [&](int rr) -> GRow {
-        const size_t row = (size_t)gw + (size_t)nw * rr;
+        const size_t row = (size_t)(r0 + 4 * rr);
         return GRow{W + row * NV, F == F_MXFP4 ? Ws + row * NV : nullptr};
     };
     using RS = RowStream<F, NC, NV>;
@@ -48,6 +50,10 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
     typename RS::Buf A, B;
     st.issue(A, 0, rowf);  // weights do not depend on x: start streaming first
 
+    RowScales rsc;
+    if constexpr (F == F_FP8)
+        rsc.load(gp(reinterpret_cast<const float*>(a.wscale)), nrows, lane,
+                 [&](int rr) { return (size_t)(r0 + 4 * rr); });
     const MBG_GLOBAL float* x = gp(a.x);
     for (int i = threadIdx.x; i < NC * H; i += blockDim.x) xs[i] = x[i];
     __syncthreads();
@@ -56,10 +62,10 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) best[c] = 0ull;
     MBG_GLOBAL float* logits = a.logits ? gp(a.logits) : nullptr;
-    const MBG_GLOBAL float* wsc = gp(reinterpret_cast<const float*>(a.wscale));
     auto out = [&](int rr, const float (&s)[NC]) {
-        const uint32_t r = (uint32_t)(gw + nw * rr);
-        const float sc = (F == F_FP8) ? wsc[r] : 1.0f;
+        const uint32_t r = (uint32_t)(r0 + 4 * rr);
+        float sc = 1.0f;
+        if constexpr (F == F_FP8) sc = rsc.get(rr, r);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const float v = s[c] * sc;

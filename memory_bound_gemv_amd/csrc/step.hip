@@ -1474,16 +1474,21 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     __shared__ unsigned long long wbest[kWaves * 4];
     const int lane = lane_id(), wave = wave_id();
     const int V = a->vocab;
-    const int nw = (int)a->tiles_lm * kWaves, gw = (int)tile * kWaves + wave;
-    const int nrows = gw < V ? (V - 1 - gw) / nw + 1 : 0;
+    // a workgroup owns a contiguous block of rows (few pages per address
+    // translation cache); its wavefronts interleave within the block
+    const int per = (V + (int)a->tiles_lm - 1) / (int)a->tiles_lm;
+    const int r0 = (int)tile * per + wave, r1 = min(V, (int)tile * per + per);
+    const int nrows = r0 < r1 ? (r1 - 1 - r0) / kWaves + 1 : 0;
     const MBG_GLOBAL uint4* W = gp(reinterpret_cast<const uint4*>(a->lm_head));
-    auto rowf = [&](int rr) -> GRow { return GRow{W + (size_t)(gw + nw * rr) * (H / E), nullptr}; };
+    auto rowf = [&](int rr) -> GRow { return GRow{W + (size_t)(r0 + kWaves * rr) * (H / E), nullptr}; };
     using RS = RowStream<F, NC, H / E>;
     RS st(nrows, lane);
     typename RS::Buf A, B;
     int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
     if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
+    RowScales rsc;   // FP8 rows: their scales, requested before the wait
+    if constexpr (F == F_FP8) rsc.load(gp(a->lm_scale), nrows, lane, [&](int rr) { return (size_t)(r0 + kWaves * rr); });
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->xres, NC * H, xs);
     norm_in_place<NC, H>(a, a->final_norm, xs);
@@ -1493,10 +1498,10 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
 #pragma unroll
     for (int c = 0; c < NC; ++c) best[c] = 0ull;
     MBG_GLOBAL float* logits = a->logits ? gp(a->logits) : nullptr;
-    const MBG_GLOBAL float* lsc = gp(a->lm_scale);
     auto out = [&](int rr, const float (&s)[NC]) {
-        const uint32_t r = (uint32_t)(gw + nw * rr);
-        const float sc = F == F_FP8 ? lsc[r] : 1.0f;
+        const uint32_t r = (uint32_t)(r0 + kWaves * rr);
+        float sc = 1.0f;
+        if constexpr (F == F_FP8) sc = rsc.get(rr, r);
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const float v = s[c] * sc;
