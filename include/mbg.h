@@ -160,10 +160,14 @@ int mbg_workspace_size(const mbg_config *cfg, size_t *bytes);
  * call and touches no device memory.  w or kv may be NULL to check less. */
 int mbg_validate(const mbg_config *cfg, const mbg_weights *w, const mbg_kv *kv);
 
-/* Validate, build the static per-step task list and dependency counters in
- * the caller's workspace (device, >= mbg_workspace_size bytes, 256-byte
- * aligned) with copies enqueued on `stream`, and return a host context.
- * The weights, KV pool and workspace must outlive the context. */
+/* Validate, build the static per-step task list in the caller's workspace
+ * (device, >= mbg_workspace_size bytes, 256-byte aligned) with copies
+ * enqueued on `stream`, and return a host context.  The dependency counters
+ * and the device status word live in a small block of uncached device
+ * memory (under 1 MiB) that the library takes from a process-wide pool or
+ * allocates on the current device; the step kernel polls it with
+ * cache-bypassing scalar loads.  The weights, KV pool and workspace must
+ * outlive the context. */
 int mbg_decode_init(const mbg_config *cfg, const mbg_weights *w, const mbg_kv *kv,
                     void *d_workspace, size_t workspace_bytes, void *stream, mbg_ctx **out);
 
@@ -231,7 +235,10 @@ int mbg_read_routing(mbg_ctx *ctx, int32_t layer, int32_t *idx, float *weights, 
 /* Text of the last error on this thread ("" if none). */
 const char *mbg_last_error(void);
 
-/* Free the host context.  Does not touch caller memory. */
+/* Wait for the context's stream, return its uncached counter block to the
+ * process-wide pool (uncached memory is not handed back to the runtime once
+ * a kernel has read it; later contexts reuse it) and free the host context.
+ * Does not touch caller memory. */
 void mbg_destroy(mbg_ctx *ctx);
 
 /* ------------------------------------------------ standalone operations */
