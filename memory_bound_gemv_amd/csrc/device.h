@@ -121,12 +121,31 @@ __device__ __forceinline__ float group_sum(float v) {
     else return group16_sum(v);
 }
 
-// Whole-wavefront sum, identical in every lane.
+// Values of the two 16-lane rows of each row pair (rows 0/1 and 2/3) and of
+// the two 32-lane halves, exchanged by the gfx950 permlane swaps (plain VALU,
+// no LDS round trip).  Swapping a register with itself leaves in every lane
+// the even row's (lower half's) value in the first result and the odd row's
+// (upper half's) in the second.
+__device__ __forceinline__ void row_pair(float v, float& even, float& odd) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    even = __uint_as_float(r[0]);
+    odd = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void wave_halves(float v, float& lo, float& hi) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    lo = __uint_as_float(r[0]);
+    hi = __uint_as_float(r[1]);
+}
+
+// Whole-wavefront sum, identical in every lane: rows, then row pairs, then
+// halves, in a fixed order.
 __device__ __forceinline__ float wave_sum(float v) {
     v = group16_sum(v);
-    v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));  // xor 16
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
-           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    float a, b;
+    row_pair(v, a, b);
+    v = a + b;
+    wave_halves(v, a, b);
+    return a + b;
 }
 
 // Whole-wavefront maximum, identical in every lane.
@@ -135,14 +154,29 @@ __device__ __forceinline__ float wave_max(float v) {
     v = fmaxf(v, dpp_f<0x4E>(v));
     v = fmaxf(v, dpp_f<0x141>(v));
     v = fmaxf(v, dpp_f<0x140>(v));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F)));
-    return fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)),
-                 __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32)));
+    float a, b;
+    row_pair(v, a, b);
+    v = fmaxf(a, b);
+    wave_halves(v, a, b);
+    return fmaxf(a, b);
 }
 
-__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
-    return __shfl_xor(v, mask, kWave);
+// The value of lane (this lane ^ MSK): 8 within a row is a half-row
+// rotation (DPP), 16 and 32 are the permlane swaps above.
+template <int MSK>
+__device__ __forceinline__ float xor_lanes(float v) {
+    if constexpr (MSK == 8) {
+        return dpp_f<0x128>(v);   // row_ror:8
+    } else if constexpr (MSK == 16 || MSK == 32) {
+        float a, b;
+        if constexpr (MSK == 16) row_pair(v, a, b);
+        else wave_halves(v, a, b);
+        return (__lane_id() & MSK) ? a : b;
+    } else {
+        return __shfl_xor(v, MSK, kWave);
+    }
 }
+
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits [3:0] and [15:14],
 // expcnt [6:4], lgkmcnt [11:8]); unnamed counters are left at their maximum.

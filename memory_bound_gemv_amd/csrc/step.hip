@@ -434,6 +434,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     const MBG_GLOBAL f32x2* rcs = gp(reinterpret_cast<const f32x2*>(a->rope_cs));
     f32x2 cs_pre[2] = {{1.f, 0.f}, {1.f, 0.f}};
+    float ksc_pre[2] = {1.f, 1.f};   // FP8 cache: the scale of the item's (layer, head, K/V)
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int idx = lane + kWave * it;
@@ -442,8 +443,18 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
             const int u = gw + nw * pu;
             const int hh = u / HALF;
             if (hh < Hq + Hkv) cs_pre[it] = rcs[(size_t)(a->pos + c) * HALF + (u - hh * HALF)];
+            if (S::KVF == F_FP8 && hh >= Hq) {
+                const int kv = hh < Hq + Hkv ? 0 : 1;
+                const int gh = kv == 0 ? hh - Hq : hh - Hq - Hkv;
+                ksc_pre[it] = gp(a->kv_scales)[((size_t)layer * Hkv + gh) * 2 + kv];
+            }
         }
     }
+    // the pages of the window's positions (scalar loads)
+    const MBG_CONST int32_t* ptab_s = (const MBG_CONST int32_t*)a->page_table;
+    int page_c[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) page_c[c] = ptab_s[(a->pos + c) / a->page_size];
     if (!wait_counter(a, wctr, wneed)) return false;
     if (layer == 0) {
         int tok[NC];
@@ -469,7 +480,6 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
     st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     __syncthreads();
-    const MBG_GLOBAL int32_t* ptab = gp(a->page_table);
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
         const int idx = lane + kWave * it;
@@ -497,9 +507,11 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
         }
         const int kv = hh < Hq + Hkv ? 0 : 1;
         const int gh = kv == 0 ? hh - Hq : hh - Hq - Hkv;
-        const int lp = p / a->page_size;
-        const int page = ptab[lp];
-        const int slot = p - lp * a->page_size;
+        int page = page_c[0];
+#pragma unroll
+        for (int cc = 1; cc < NC; ++cc)
+            if (c == cc) page = page_c[cc];
+        const int slot = p - (p / a->page_size) * a->page_size;
         const size_t off = (size_t)layer * a->kv_layer_stride +
                            ((((size_t)page * 2 + kv) * Hkv + gh) * a->page_size + slot) * HD + i;
         if constexpr (S::KVF == F_BF16) {
@@ -508,7 +520,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
             stc_small<uint16_t>(pool + off + HALF, f32_to_bf16(x1));
         } else {
             MBG_GLOBAL uint8_t* pool = gp(reinterpret_cast<uint8_t*>(a->kv_pool));
-            const float sc = gp(a->kv_scales)[((size_t)layer * Hkv + gh) * 2 + kv];
+            const float sc = ksc_pre[it];
             stc_small<uint8_t>(pool + off, f32_to_fp8e4m3(x0 / sc));
             stc_small<uint8_t>(pool + off + HALF, f32_to_fp8e4m3(x1 / sc));
         }
@@ -608,6 +620,26 @@ struct AttnLane {
             }
         }
     }
+
+    // Merge with the state of lane (this lane ^ MSK): the same slice of the
+    // heads over other positions.  Both lanes end with the same state.
+    template <int MSK>
+    __device__ __forceinline__ void merge_partner() {
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+            const float m2 = xor_lanes<MSK>(m[h]);
+            const float l2 = xor_lanes<MSK>(l[h]);
+            float mn, w1, w2;
+            merge_weights(m[h], m2, mn, w1, w2);
+            l[h] = l[h] * w1 + l2 * w2;
+#pragma unroll
+            for (int e = 0; e < EPC; ++e) {
+                const float o2 = xor_lanes<MSK>(o[h][e]);
+                o[h][e] = o[h][e] * w1 + o2 * w2;
+            }
+            m[h] = mn;
+        }
+    }
 };
 
 // Attention LDS use: per wavefront a ring of kAttnBufs buffers of
@@ -675,16 +707,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const bool resident = nch <= NB;                // whole history stays in LDS
     const size_t layer_off = (size_t)layer * a->kv_layer_stride;
     const MBG_GLOBAL uint8_t* pool = gp(reinterpret_cast<const uint8_t*>(a->kv_pool));
-    const MBG_GLOBAL int32_t* ptab = gp(a->page_table);
     MBG_LDS uint8_t* ring = reinterpret_cast<MBG_LDS uint8_t*>(smem) + wave * kAttnWaveBytes;
 
-    auto row_ptr = [&](int t, int kv) -> const MBG_GLOBAL uint8_t* {
-        const int lp = t / page_size;
-        const int page = ptab[lp];
-        const int sl = t - lp * page_size;
-        const size_t el = layer_off + ((((size_t)page * 2 + kv) * Hkv + g) * page_size + sl) * HD;
-        return pool + el * EB + (size_t)cidx * 16;
-    };
     auto tok_of = [&](int i) { return t0 + (i * kWaves + wave) * TPI + tl; };
     const MBG_CONST int32_t* ptab_s = (const MBG_CONST int32_t*)a->page_table;
     const size_t lane_off = (size_t)tl * HD * EB + (size_t)cidx * 16;
@@ -713,12 +737,34 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     // the polling wave (0) may hold its loads back until its wait is over
     const int early = (wave != 0 || a->poll_wave_prefetch) ? min(npre, a->attn_pre) : 0;
     for (int c = 0; c < early; ++c) issue_chunk(c, c);
+    // known before the wait, read with scalar loads: the pages of the
+    // positions this step writes, the FP8 scales
+    int page_new[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) page_new[c] = ptab_s[(pos + c) / page_size];
+    const MBG_CONST float* kvs = (const MBG_CONST float*)a->kv_scales;
+    const float ksc = KVF == F_FP8 ? kvs[((size_t)layer * Hkv + g) * 2 + 0] : 1.f;
+    const float vsc = KVF == F_FP8 ? kvs[((size_t)layer * Hkv + g) * 2 + 1] : 1.f;
     if (!wait_counter(a, wctr, wneed)) return false;
     for (int c = early; c < npre; ++c) issue_chunk(c, c);
+    // the positions written this step (at most ncol of them, folded by wave 0
+    // after the history): requested now, read coherently
+    const bool has_new = wave == 0 && t1 > pos;   // wave-uniform
+    const int tn = max(t0, pos) + tl;             // this lane's position
+    uint4 Kn = make_uint4(0, 0, 0, 0), Vn = make_uint4(0, 0, 0, 0);
+    if (has_new && tl < ncol && tn < t1) {
+        int page = page_new[0];
+#pragma unroll
+        for (int c = 1; c < NC; ++c)
+            if (tn - pos == c) page = page_new[c];
+        const size_t el =
+            layer_off + ((((size_t)page * 2) * Hkv + g) * page_size + (tn - (tn / page_size) * page_size)) * HD;
+        const MBG_GLOBAL uint8_t* kp = pool + el * EB + (size_t)cidx * 16;
+        Kn = ldc16(reinterpret_cast<const MBG_GLOBAL uint4*>(kp));
+        Vn = ldc16(reinterpret_cast<const MBG_GLOBAL uint4*>(kp + (size_t)Hkv * page_size * HD * EB));
+    }
 
     const float qscale = a->attn_scale_log2;
-    const float ksc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 0] : 1.f;
-    const float vsc = KVF == F_FP8 ? gp(a->kv_scales)[((size_t)layer * Hkv + g) * 2 + 1] : 1.f;
     lds_f32* red = reinterpret_cast<lds_f32*>(reinterpret_cast<MBG_LDS uint8_t*>(smem) + kAttnRingBytes);
     const rsrc_t rq = make_rsrc(a->qbuf);
     const rsrc_t rp = make_rsrc(a->part);
@@ -764,18 +810,10 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             }
         }
         if (col == 0) stamp(2);
-        // positions written this step (at most ncol of them): wave 0, read coherently
-        if (wave == 0 && t1 > pos) {
-            const int tn = max(t0, pos) + tl;
-            uint4 K[1], V[1];
-            bool valid[1] = {tl < ncol && tn < te};
-            if (valid[0]) {
-                K[0] = ldc16(reinterpret_cast<const MBG_GLOBAL uint4*>(row_ptr(tn, 0)));
-                V[0] = ldc16(reinterpret_cast<const MBG_GLOBAL uint4*>(row_ptr(tn, 1)));
-            } else {
-                K[0] = make_uint4(0, 0, 0, 0);
-                V[0] = make_uint4(0, 0, 0, 0);
-            }
+        // positions written this step, up to this column's own
+        if (has_new) {
+            const uint4 K[1] = {Kn}, V[1] = {Vn};
+            const bool valid[1] = {tl < ncol && tn < te};
             st.template fold<1>(q, K, V, valid, ksc);
         }
         if constexpr (KVF == F_FP8) {
@@ -785,23 +823,10 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
                 for (int e = 0; e < EPC; ++e) st.o[h][e] *= vsc;
         }
         // merge the token slots of a wave (lanes with the same cidx)
-#pragma unroll
-        for (int msk = LPT; msk < kWave; msk <<= 1) {
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                const float m2 = shfl_xor_f(st.m[h], msk);
-                const float l2 = shfl_xor_f(st.l[h], msk);
-                float mn, w1, w2;
-                merge_weights(st.m[h], m2, mn, w1, w2);
-                st.l[h] = st.l[h] * w1 + l2 * w2;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    const float o2 = shfl_xor_f(st.o[h][e], msk);
-                    st.o[h][e] = st.o[h][e] * w1 + o2 * w2;
-                }
-                st.m[h] = mn;
-            }
-        }
+        if constexpr (LPT <= 4) st.template merge_partner<4>();
+        if constexpr (LPT <= 8) st.template merge_partner<8>();
+        if constexpr (LPT <= 16) st.template merge_partner<16>();
+        st.template merge_partner<32>();
         // then the waves, through LDS, in wave order
         if (lane < LPT) {
 #pragma unroll
