@@ -395,6 +395,30 @@ __device__ __forceinline__ void stamp(int k) {
     if (threadIdx.x == 0) s_stamp[k] = wall_clock64();
 }
 
+// Residual values of a wavefront's first kResRows output rows (lane c < NC
+// holds column c), read before the task's wait: the residual a GEMV adds to
+// is final once an earlier wait of the same workgroup has been satisfied, so
+// the row epilogue does not wait for a load issued behind the stream.
+constexpr int kResRows = 2;
+struct ResidPre {
+    float v[kResRows];
+    template <class LoadFn>
+    __device__ __forceinline__ void load(int nrows, bool lane_has, LoadFn f) {
+#pragma unroll
+        for (int i = 0; i < kResRows; ++i) v[i] = (i < nrows && lane_has) ? f(i) : 0.f;
+    }
+    // rr is wave-uniform; rows from kResRows on come from fallback()
+    template <class LoadFn>
+    __device__ __forceinline__ float get(int rr, LoadFn fallback) const {
+        if (rr >= kResRows) return fallback();
+        float r = v[0];
+#pragma unroll
+        for (int i = 1; i < kResRows; ++i)
+            if (rr == i) r = v[i];
+        return r;
+    }
+};
+
 // ------------------------------------------------------------------ QKV
 
 template <int NC, class S>
@@ -1014,26 +1038,36 @@ __device__ __forceinline__ bool op_oproj(CArgs* a, uint32_t layer, uint32_t tile
     int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
     if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
+    // the residual: the embedding rows at layer 0, else the stream as the
+    // previous layer left it (final since this workgroup's QKV wait)
+    int tok[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) tok[c] = layer == 0 ? token_of(a, c) : 0;
+    int tk_lane = 0;
+#pragma unroll
+    for (int cc = 0; cc < NC; ++cc)
+        if (cc == lane) tk_lane = tok[cc];
+    MBG_GLOBAL float* x = gp(a->xres);
+    const MBG_GLOBAL uint16_t* emb = gp(a->embed);
+    auto resid = [&](int rr) -> float {
+        const int r = gw + nw * rr;
+        return layer == 0 ? bf16_to_f32(emb[(size_t)tk_lane * H + r]) : ldc(x + lane * H + r);
+    };
+    ResidPre rp;
+    rp.load(nrows, lane < NC, resid);
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->attn, NC * K, xs);
     if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
-    int tok[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) tok[c] = layer == 0 ? token_of(a, c) : 0;
-    MBG_GLOBAL float* x = gp(a->xres);
-    const MBG_GLOBAL uint16_t* emb = gp(a->embed);
     auto out = [&](int rr, const float (&s)[NC]) {
         if (lane >= NC) return;
         const int c = lane;
         float v = 0.f;
-        int tk_ = 0;
 #pragma unroll
         for (int cc = 0; cc < NC; ++cc)
-            if (cc == c) { v = s[cc]; tk_ = tok[cc]; }
+            if (cc == c) v = s[cc];
         const int r = gw + nw * rr;
-        const float res = layer == 0 ? bf16_to_f32(emb[(size_t)tk_ * H + r]) : ldc(x + c * H + r);
-        stc(x + c * H + r, res + v);
+        stc(x + c * H + r, rp.get(rr, [&] { return resid(rr); }) + v);
     };
     st.run(A, B, rowf, xs, K, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
@@ -1108,11 +1142,16 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
     int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
     if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
+    // the residual after this layer's output projection (final since this
+    // workgroup's gate/up wait)
+    MBG_GLOBAL float* x = gp(a->xres);
+    auto resid = [&](int rr) -> float { return ldc(x + lane * H + gw + nw * rr); };
+    ResidPre rp;
+    rp.load(nrows, lane < NC, resid);
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->hbuf, NC * F, xs);
     if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
-    MBG_GLOBAL float* x = gp(a->xres);
     auto out = [&](int rr, const float (&s)[NC]) {
         if (lane >= NC) return;
         const int c = lane;
@@ -1121,7 +1160,7 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
         for (int cc = 0; cc < NC; ++cc)
             if (cc == c) v = s[cc];
         const int r = gw + nw * rr;
-        stc(x + c * H + r, ldc(x + c * H + r) + v);
+        stc(x + c * H + r, rp.get(rr, [&] { return resid(rr); }) + v);
     };
     st.run(A, B, rowf, xs, F, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
@@ -1419,6 +1458,13 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
     // LDS: then the first pass's weights are requested before the wait
     const bool have_route = R.layer == layer && R.epoch == a->epoch;
     if (have_route) issue_pass(0, min(kSlotsPerPass, R.nslots));
+    // the residual after this layer's output projection (final since this
+    // workgroup's expert gate/up wait)
+    MBG_GLOBAL float* x = gp(a->xres);
+    float res_pre[kMaxDownRows];
+#pragma unroll
+    for (int i = 0; i < kMaxDownRows; ++i)
+        res_pre[i] = (i < nrows && lane < NC) ? ldc(x + lane * H + gw + nw * i) : 0.f;
     if (!wait_counter(a, wctr, wneed)) return false;
     if (!have_route) route_slots<NC>(a, layer);
     stamp(0);
@@ -1475,7 +1521,6 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
         }
     }
     stamp(1);
-    MBG_GLOBAL float* x = gp(a->xres);
 #pragma unroll
     for (int i = 0; i < kMaxDownRows; ++i) {
         if (i >= nrows) continue;
@@ -1483,7 +1528,7 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const float sum = wave_sum(acc[i][c]);
-            if (lane == c) stc(x + c * H + r, ldc(x + c * H + r) + sum);
+            if (lane == c) stc(x + c * H + r, res_pre[i] + sum);
         }
     }
     release_counter(a, ctr_index(layer, PH_DOWN));
