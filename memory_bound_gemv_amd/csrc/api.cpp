@@ -436,6 +436,31 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     if (const char* e = getenv("MBG_WAVE0_INPUT")) a.wave0_input = atoi(e) != 0;
     if (const char* e = getenv("MBG_ATTN_PREFETCH")) a.attn_pre = std::max(0, std::min(kAttnBufsHost, atoi(e)));
     const uint32_t tiles_attn = (uint32_t)(c.n_kv_heads * head_groups * S);
+    // Attention placement: workgroup b runs on XCD b % 8 (the dispatcher
+    // deals workgroups round-robin over the 8 XCDs; the kernel checks it).
+    // When every group's splits fit on one XCD, group gg goes to XCD gg % 8
+    // and its splits exchange partials and arrivals through that XCD's L2
+    // instead of device-coherent memory.  Each group's block of partial rows
+    // must then be whole 128-byte lines: (heads per task x splits) % 8 == 0.
+    // The kernels for BF16 caches carry this path (the FP8-cache kernels,
+    // meant for long contexts, are built without it).  Long contexts keep
+    // the default placement: one XCD reading every page
+    // of a KV head misses its address translation caches far more often
+    // than eight XCDs reading an eighth of the pages each (measured slower
+    // at 200,000 positions), and there the combine is a small share.
+    const int NG = c.n_kv_heads * head_groups;
+    const int gh_task = gq / head_groups;
+    a.attn_local = (kv->dtype == MBG_BF16 && G % 8 == 0 && NG % 8 == 0 && (NG / 8) * S <= G / 8 &&
+                    (gh_task * S) % 8 == 0 && (int64_t)c.max_pos <= (int64_t)kAttnLocalMaxSplitLen * S)
+                       ? 1
+                       : 0;
+    if (const char* e = getenv("MBG_ATTN_LOCAL")) a.attn_local = a.attn_local && atoi(e) != 0;
+    auto attn_tile_of = [&](int wg) -> int {   // the attention tile workgroup wg runs, or -1
+        if (!a.attn_local) return wg < (int)tiles_attn ? wg : -1;
+        const int x = wg % 8, slot = wg / 8;
+        if (slot >= (NG / 8) * S) return -1;
+        return ((slot / S) * 8 + x) * S + slot % S;
+    };
 
     // task lists
     std::vector<uint32_t> off(G + 1, 0);
@@ -448,7 +473,8 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
             const uint32_t L8 = (uint32_t)l << 8;
             if (t < a.tiles_qkv)
                 tasks.push_back(Task{OP_QKV | L8, t, l == 0 ? kNoWait : ci(l - 1, PH_DOWN), l == 0 ? 0u : tiles_last});
-            if (t < tiles_attn) tasks.push_back(Task{OP_ATTN | L8, t, ci(l, PH_QKV), a.tiles_qkv});
+            if (attn_tile_of(wg) >= 0)
+                tasks.push_back(Task{OP_ATTN | L8, (uint32_t)attn_tile_of(wg), ci(l, PH_QKV), a.tiles_qkv});
             if (t < a.tiles_o)
                 tasks.push_back(Task{OP_OPROJ | L8, t, ci(l, PH_ATTN), (uint32_t)(c.n_kv_heads * head_groups)});
             if (!moe) {
@@ -614,6 +640,8 @@ int mbg_get_status(mbg_ctx* x) {
         HIP_TRY(hipStreamSynchronize(x->stream));
         if (st == kStatusTimeout) return fail(MBG_E_TIMEOUT, "a device wait exceeded its deadline");
         if (st == kStatusRange) return fail(MBG_E_RANGE, "a token id was outside [0, vocab)");
+        if (st == kStatusPlacement)
+            return fail(MBG_E_UNSUPPORTED, "workgroups are not placed on XCD blockIdx %% 8; set MBG_ATTN_LOCAL=0");
         return fail(MBG_E_HIP, "device status %u", st);
     }
     return MBG_OK;

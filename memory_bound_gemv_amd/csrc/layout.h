@@ -142,11 +142,15 @@ struct StepArgs {
     int32_t pos;
     int32_t ncol;
     uint32_t epoch;
+    int32_t attn_local;        // 1: the splits of an attention group run on one XCD (workgroup b on XCD b % 8)
+                               //    and exchange partials and arrivals through that XCD's L2
     uint64_t deadline_ticks;   // s_memrealtime ticks a wait may take
 };
 
 // Device status codes (positive on the device, negated at the boundary).
 constexpr uint32_t kStatusTimeout = 7;
 constexpr uint32_t kStatusRange = 4;
+constexpr int kAttnLocalMaxSplitLen = 1024;    // XCD-local attention groups only up to this many positions per split
+constexpr uint32_t kStatusPlacement = 2;   // a workgroup is not on the XCD its attention placement assumes
 
 }  // namespace mbg

@@ -115,6 +115,15 @@ __device__ __forceinline__ f32x4 ldc4(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ void stc4(rsrc_t r, uint32_t off, f32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, kCohAux);
 }
+// The same within one XCD: stores reach that XCD's L2 (the per-CU cache
+// writes through), loads bypass the per-CU cache (sc0) and read the L2.
+// Used only between workgroups that run on the same XCD.
+__device__ __forceinline__ f32x4 ldx4(rsrc_t r, uint32_t off) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 1));
+}
+__device__ __forceinline__ void stx4(rsrc_t r, uint32_t off, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
+}
 
 __device__ __forceinline__ void acquire_after_wait() {
 #if !MBG_COHERENT
@@ -792,6 +801,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     lds_f32* red = reinterpret_cast<lds_f32*>(reinterpret_cast<MBG_LDS uint8_t*>(smem) + kAttnRingBytes);
     const rsrc_t rq = make_rsrc(a->qbuf);
     const rsrc_t rp = make_rsrc(a->part);
+    // this group's splits share an XCD (and its L2); compiled for BF16 caches
+    const bool local = KVF == F_BF16 && a->attn_local != 0;
     const bool empty = t0 >= t1;
     for (int col = 0; col < ncol && !empty; ++col) {
         const int te = min(t1, pos + col + 1);
@@ -889,7 +900,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
                     t[1] = O[e + 1];
                     t[2] = O[e + 2];
                     t[3] = O[e + 3];
-                    stc4(rp, row + 4u * (cidx * EPC + e), t);
+                    if (local) stx4(rp, row + 4u * (cidx * EPC + e), t);
+                    else stc4(rp, row + 4u * (cidx * EPC + e), t);
                 }
                 if (cidx == 0) {
                     f32x4 t;
@@ -897,7 +909,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
                     t[1] = Ls;
                     t[2] = 0.f;
                     t[3] = 0.f;
-                    stc4(rp, row + 4u * HD, t);
+                    if (local) stx4(rp, row + 4u * HD, t);
+                    else stc4(rp, row + 4u * HD, t);
                 }
             }
         }
@@ -910,8 +923,14 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     __syncthreads();
     if (threadIdx.x == 0) {
         release_before_signal();
-        const uint32_t old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv * HG + gg) * kLineU32, 1u,
-                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // within the XCD: an L2 atomic; otherwise a device-scope one
+        uint32_t old;
+        if (local)
+            old = (uint32_t)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(
+                1, make_rsrc(a->head_ctr), (int)(((size_t)layer * Hkv * HG + gg) * kLineU32 * 4), 0, 0);
+        else
+            old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv * HG + gg) * kLineU32, 1u,
+                                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old + 1u == a->epoch * (uint32_t)S_);
         if (s_last) acquire_after_wait();
     }
@@ -941,7 +960,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             const int ch = rs / nsv, sp = rs - ch * nsv;
             const int col = ch / GH, h = ch - col * GH;
             const int vec = whole ? v : HDV;
-            t[k] = ldc4(rp, (uint32_t)(((((size_t)col * Hq + qh0 + h) * S_ + sp) * stride + vec * 4) * 4));
+            const uint32_t po = (uint32_t)(((((size_t)col * Hq + qh0 + h) * S_ + sp) * stride + vec * 4) * 4);
+            t[k] = local ? ldx4(rp, po) : ldc4(rp, po);
         }
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
@@ -986,7 +1006,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             for (int k = 0; k < 8; ++k) {
                 const int sp = min(i0 + k * ng, nsv - 1);
                 v[k] = whole ? *reinterpret_cast<const MBG_LDS f32x4*>(prt + ((size_t)(ch * nsv + sp) * RV + vec) * 4)
-                             : ldc4(rp, (uint32_t)(((row0 + sp) * stride + vec * 4) * 4));
+                             : local ? ldx4(rp, (uint32_t)(((row0 + sp) * stride + vec * 4) * 4))
+                                     : ldc4(rp, (uint32_t)(((row0 + sp) * stride + vec * 4) * 4));
             }
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
@@ -1629,6 +1650,11 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
     if (threadIdx.x == 0) {
         s_stamp[2] = s_stamp[3] = 0;
         s_route.epoch = 0;   // no routing held yet (epochs start at 1)
+        if (S::KVF == F_BF16 && a->attn_local) {   // the attention placement assumes workgroup b runs on XCD b % 8
+            uint32_t xcc;
+            asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+            if ((xcc & 0xFu) != (blockIdx.x & 7u)) latch_error(a->status, kStatusPlacement);
+        }
     }
     for (uint32_t ti = off[b]; ti < end; ++ti) {
         const u32x4 tv = tasks[ti];
