@@ -100,6 +100,7 @@ struct StepArgs {
     // wavefront (whole rows, at most two register chunks) and attention ring
     // chunks per wavefront (0 .. kAttnBufs)
     int32_t gemv_pre, attn_pre;
+    int32_t gu_pre, down_pre;    // the same budget (KiB) for the dense gate/up and down phases
     int32_t poll_wave_prefetch;  // 1: the polling wave (0) also prefetches before its wait
     int32_t wave0_input;         // 1: inputs copied to LDS by wave 0 alone (coherent DMA); 0: all waves load
     // weights

@@ -395,8 +395,12 @@ __device__ __forceinline__ f32x4 bf16x4(const MBG_GLOBAL u32x2* p) {
 // Rows of its stream a wavefront issues before it waits for its input: the
 // prefetch budget (KiB per wavefront) rounded up to whole rows.
 template <class RS>
+__device__ __forceinline__ int gemv_pre_rows(int kib) {
+    return (kib * 1024 + RS::kRowBytes - 1) / RS::kRowBytes;
+}
+template <class RS>
 __device__ __forceinline__ int gemv_pre_rows(CArgs* a) {
-    return (a->gemv_pre * 1024 + RS::kRowBytes - 1) / RS::kRowBytes;
+    return gemv_pre_rows<RS>(a->gemv_pre);
 }
 
 __shared__ uint64_t s_stamp[4];  // trace: input loaded, stream finished, two op-specific points
@@ -1116,11 +1120,11 @@ __device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t til
     typename RS::Buf A, B;
     int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
+    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a->gu_pre));
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->xres, NC * H, xs);
     norm_in_place<NC, H>(a, L->ffn_norm, xs);
-    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
+    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a->gu_pre));   // after the input loads, not ahead of them
     stamp(0);
     MBG_GLOBAL float* hb = gp(a->hbuf);
     float gate[NC];
@@ -1162,7 +1166,7 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
     typename RS::Buf A, B;
     int pre = 0;
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
+    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a->down_pre));
     // the residual after this layer's output projection (final since this
     // workgroup's gate/up wait)
     MBG_GLOBAL float* x = gp(a->xres);
@@ -1171,7 +1175,7 @@ __device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile,
     rp.load(nrows, lane < NC, resid);
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->hbuf, NC * F, xs);
-    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
+    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a->down_pre));   // after the input loads, not ahead of them
     stamp(0);
     auto out = [&](int rr, const float (&s)[NC]) {
         if (lane >= NC) return;
