@@ -1,14 +1,20 @@
 """Batch-1 decode benchmark on one MI355X.
 
-Workload: the 2B-class dense decoder (28 layers, hidden 2048, 16 query / 8 KV
-heads of 128, SwiGLU 8192, vocab 32000, BF16 weights ~N(0, 0.02)), BF16 KV
-cache prefilled with N(0, 1) to 4096 positions, greedy decode at batch 1.
-One step = one decode_step call = one persistent-kernel launch that runs all
-28 layers, the LM head and the argmax; the token of step i+1 is the argmax of
-step i, read on the device (no host round trip inside the timed region).
+Default workload: the routed decoder (42 layers, hidden 2560, 32 query / 4 KV
+heads of 128, 512 MXFP4 experts top-8 plus one shared expert, moe_ffn 768,
+BF16 attention and router, FP8 LM head over a 157,184-token vocabulary), KV
+prefilled to 2048 positions, greedy decode at batch 1 -- the largest
+configuration of the workload set that fits one GPU.  One step = one
+decode_step call = one persistent-kernel launch that runs every layer, the LM
+head and the argmax; the token of step i+1 is the argmax of step i, read on
+the device (no host round trip inside the timed region).  The same run times
+the 4-token verify window.
 
-Prints one JSON line (see the keys below).  --gpus N with N > 1 exits: this
-build runs on one GPU.
+Other workloads (--workload): dense2b, longctx (FP8 KV at 200,000
+positions), lmhead (the LM head GEMV alone, --lm-dtype bf16|fp8, --k 1..4).
+
+Prints one JSON line.  --gpus N with N > 1 exits: the decode path runs on one
+GPU.
 """
 from __future__ import annotations
 
@@ -22,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0   # MI355X HBM3E peak, GB/s
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "step_kernel_dense2b_traffic.txt")
+METRIC = "batch-1 decode tokens/s and achieved HBM GB/s (MBU % of peak) on 1 MI355X"
 
 WORKLOADS = {
     "dense2b": "dense 2B decoder: 28 layers, hidden 2048, 16 query / 8 KV heads of 128, SwiGLU 8192, vocab 32000, "
@@ -34,18 +40,25 @@ WORKLOADS = {
     "moe": "routed decoder: 42 layers, hidden 2560, 32 query / 4 KV heads of 128, 512 MXFP4 experts top-8 + 1 "
            "shared (moe_ffn 768), BF16 attention/router, FP8 LM head over vocab 157184, BF16 KV prefilled to 2048 "
            "positions, batch 1, greedy decode at positions 2048..2055",
+    "lmhead": "LM-head GEMV + argmax alone: 157184 x 2560 weight N(0,0.02), hidden vectors N(0,1), "
+              "3 weight copies rotated so the 256 MB last-level cache cannot serve repeats",
 }
 
 
-def stored_traffic():
-    """HBM bytes per launch of the decode-step kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, scaled by a plain-copy calibration), or
-    None when the summary is missing or was taken on other kernel sources."""
+def traffic_file(name: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
+
+
+def stored_traffic(name: str):
+    """HBM bytes per launch from the committed counter summary (FETCH_SIZE +
+    WRITE_SIZE, each scaled by a plain-copy calibration), or None when the
+    summary is missing or was taken on other kernel sources."""
     from memory_bound_gemv_amd.build import source_digest
-    if not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(name)
+    if not os.path.exists(path):
         return None
     fields = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for line in f:
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
@@ -82,6 +95,17 @@ def algorithmic_bytes(cfg, pos: int) -> tuple[int, int]:
     return w, kv
 
 
+def window_bytes(cfg, pos: int, k: int, n_distinct: float) -> int:
+    """Algorithmic bytes of a k-token verify window of the routed model at
+    pos .. pos+k-1 whose union of routed experts has n_distinct members per
+    layer on average: every weight once, KV of [0, pos + k)."""
+    w, _ = algorithmic_bytes(cfg, pos)
+    expert = 3 * cfg.moe_ffn * cfg.hidden * 17 // 32
+    w += int(round(cfg.n_layers * (n_distinct - cfg.top_k) * expert))
+    kv = (pos + k) * cfg.n_layers * 2 * cfg.n_kv_heads * cfg.head_dim * (1 if cfg.kv_dtype == "fp8" else 2)
+    return w + kv
+
+
 def fp8_pow2_scales(cfg, device, block=1 << 16):
     """Per (layer, KV head, K or V) power-of-two scale 2^ceil(log2(amax / 448))
     over the float32 prefill draws."""
@@ -100,7 +124,7 @@ def fp8_pow2_scales(cfg, device, block=1 << 16):
     return sc
 
 
-def build_device_model(cfg, host, dev):
+def build_device_model(cfg, host, dev, k_max=1):
     """The workload on the device: weights, prefilled KV cache, context."""
     import torch
 
@@ -127,11 +151,12 @@ def build_device_model(cfg, host, dev):
         lm_codes = torch.empty((V, H), **u8)
         lm_scales = torch.empty(V, dtype=torch.float32, device=dev)
         M.mbg_quantize_fp8_rows(lm_bf16, V, H, lm_codes, lm_scales, torch.cuda.current_stream(dev).cuda_stream)
-        dm = DeviceModel(cfg, host, pt, lm_fp8=(lm_codes, lm_scales), experts=experts, device=dev, k_max=1)
+        dm = DeviceModel(cfg, host, pt, lm_fp8=(lm_codes, lm_scales), experts=experts, device=dev, k_max=k_max)
     elif cfg.kv_dtype == "fp8":
-        dm = DeviceModel(cfg, host, pt, kv_dtype="fp8", kv_scales=fp8_pow2_scales(cfg, dev), device=dev, k_max=1)
+        dm = DeviceModel(cfg, host, pt, kv_dtype="fp8", kv_scales=fp8_pow2_scales(cfg, dev), device=dev,
+                         k_max=k_max)
     else:
-        dm = DeviceModel(cfg, host, pt, device=dev, k_max=1)
+        dm = DeviceModel(cfg, host, pt, device=dev, k_max=k_max)
     for li in range(cfg.n_layers):
         if cfg.kv_dtype == "fp8":
             blk = 1 << 16
@@ -146,65 +171,74 @@ def build_device_model(cfg, host, dev):
     return dm
 
 
-def cpu_baseline(cfg, host, steps: int = 3):
-    """Time the CPU oracle (float64, as it stands) on a few decode steps."""
-    import numpy as np
+def _threads():
     from threadpoolctl import threadpool_info
+    return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
 
-    from oracle import OracleCache, OracleModel
+
+def cpu_baseline(cfg, host, min_s: float = 10.0, max_steps: int = 20):
+    """Time the CPU oracle (float64, as it stands) on a few decode steps of
+    the same workload.  One untimed step first converts and caches the
+    weights (and, for the routed model, the experts that step routes to);
+    the timed steps repeat that step's token and position so that they read
+    the same cached weights."""
+    from oracle import OracleCache, OracleModel, quantize_fp8_rows
     from synth import gen
 
-    om = OracleModel(cfg, host)
+    t_prep = time.perf_counter()
+    if cfg.is_moe:
+        om = OracleModel(cfg, host, experts=lambda l, e, w: gen.expert_mxfp4(cfg, l, e, w),
+                         lm_fp8=quantize_fp8_rows(host["lm_head"]))
+    else:
+        om = OracleModel(cfg, host)
     oc = OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim)
     for li in range(cfg.n_layers):
         k, v = gen.kv_prefill_bf16(cfg, li)
         oc.k[li][:cfg.prefill] = k
         oc.v[li][:cfg.prefill] = v
-    toks = gen.prompt_tokens(cfg, steps + 1)
+    tok = int(gen.prompt_tokens(cfg, 1)[0])
+    om.step(oc, tok, cfg.prefill)
+    t_prep = time.perf_counter() - t_prep
     t0 = time.perf_counter()
-    om.step(oc, int(toks[0]), cfg.prefill)          # dequantises and caches the weights
-    t_first = time.perf_counter() - t0
-    t0 = time.perf_counter()
-    for i in range(steps):
-        om.step(oc, int(toks[i + 1]), cfg.prefill + 1 + i)
+    steps = 0
+    while steps < 2 or (time.perf_counter() - t0 < min_s and steps < max_steps):
+        om.step(oc, tok, cfg.prefill)
+        steps += 1
     dt = time.perf_counter() - t0
-    threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    return {"value": steps / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"{steps} float64 oracle decode steps of the same workload at positions "
-                       f"{cfg.prefill + 1}..{cfg.prefill + steps} after one untimed step "
-                       f"({t_first:.1f} s) that converted and cached the weights; "
-                       f"host cpu_count {os.cpu_count()}")}
+    what = "decode steps" + (" (top-8 of 512 MXFP4 experts + shared per layer, FP8 LM head)" if cfg.is_moe else "")
+    return {"value": round(steps / dt, 4), "unit": "tokens/s", "cores": _threads(), "kind": "oracle",
+            "sample": (f"{steps} float64 oracle {what} of the same workload, each at position {cfg.prefill} "
+                       f"with the same token, after one untimed step ({t_prep:.1f} s including weight "
+                       f"conversion{', FP8 LM-head quantisation' if cfg.is_moe else ''}) that cached the weights "
+                       f"it reads; {dt:.1f} s timed; host cpu_count {os.cpu_count()}")}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--trace", default="",
-                    help="after the timed region, run one traced step and save its per-task stamps (.npy)")
-    ap.add_argument("--copy-probe-mib", type=int, default=0,
-                    help="also run one plain device copy of this size (counter calibration)")
-    ap.add_argument("--workload", default="dense2b", choices=["dense2b", "longctx", "moe"],
-                    help="dense2b (default, the headline line), longctx (FP8 KV at 200K positions) "
-                         "or moe (42-layer routed model); only dense2b carries the CPU baseline")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has no "
-              "multi-GPU mode in this build", file=sys.stderr)
-        sys.exit(2)
+def timed(stream, fn, n):
+    """Milliseconds per call of fn() over n back-to-back calls, measured with
+    HIP events on the stream the calls are launched on."""
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(n):
+        fn(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / n
 
+
+def run_decode(args, cfg):
     import numpy as np
     import torch
 
-    from synth import CONFIGS, gen
+    from synth import gen
 
-    cfg = CONFIGS[args.workload]
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     host = gen.dense_weights(cfg)
-    dm = build_device_model(cfg, host, dev)
+    k_win = 4 if cfg.is_moe and not args.no_verify else 1
+    dm = build_device_model(cfg, host, dev, k_max=k_win)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     info = dm.info()
@@ -221,47 +255,22 @@ def main():
     if dm.status() != 0:
         raise RuntimeError("device status after warm-up")
 
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     wall0 = time.perf_counter()
-    start.record(stream)
-    for i in range(args.steps):
-        dm.step(buf, pos_of(args.warmup + i), logits, buf)
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms_per_step = timed(stream, lambda i: dm.step(buf, pos_of(args.warmup + i), logits, buf), args.steps)
     wall = time.perf_counter() - wall0
     st = dm.status()
     if st != 0:
         raise RuntimeError(f"device status {st}")
-    ms = start.elapsed_time(end)
-    ms_per_step = ms / args.steps
-    tok_s = args.steps / (ms / 1e3)
+    tok_s = 1e3 / ms_per_step
 
     wbytes, _ = algorithmic_bytes(cfg, 0)
     kv_avg = float(np.mean([algorithmic_bytes(cfg, pos_of(args.warmup + i))[1] for i in range(args.steps)]))
     step_bytes = wbytes + kv_avg
     achieved = step_bytes / (ms_per_step / 1e3) / 1e9
-
-    if args.trace:
-        from memory_bound_gemv_amd import _mbg as M
-        M.mbg_set_trace(dm.ctx, True)
-        dm.step(buf, pos_of(args.warmup + args.steps), logits, buf)
-        rec = M.mbg_read_trace(dm.ctx, info.n_tasks)
-        M.mbg_set_trace(dm.ctx, False)
-        np.save(args.trace, rec)
-        np.save(args.trace.replace(".npy", "_meta.npy"),
-                np.array([info.clock_khz, info.grid, cfg.n_layers], dtype=np.int64))
-
-    if args.copy_probe_mib:
-        n = args.copy_probe_mib * 1024 * 1024 // 4
-        a = torch.ones(n, dtype=torch.float32, device=dev)
-        b = torch.empty_like(a)
-        b.copy_(a)
-        torch.cuda.synchronize()
+    traffic = stored_traffic(f"step_kernel_{args.workload}")
 
     out = {
-        "metric": "batch-1 decode tokens/s and achieved HBM GB/s (MBU % of peak) on 1 MI355X",
+        "metric": METRIC,
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -275,7 +284,7 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": WORKLOADS[args.workload],
-            "weight_dtype": "bf16+mxfp4 experts+fp8 lm head" if cfg.is_moe else "bf16",
+            "weight_dtype": "bf16 attention/router + mxfp4 experts + fp8 lm head" if cfg.is_moe else "bf16",
             "kv_dtype": cfg.kv_dtype, "accumulate": "fp32",
             "global_batch": 1, "seq_len": cfg.prefill, "parallelism": "none (1 GPU)",
             "kernel": info.variant.decode(), "grid": info.grid, "launches_per_step": info.launches_per_step,
@@ -286,17 +295,144 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBS, 4),
-            "traffic": stored_traffic() if args.workload == "dense2b" else None,
+            "traffic": traffic,
         },
         "bytes_per_step": {"weights": wbytes, "kv_avg": round(kv_avg), "total": round(step_bytes)},
         "bound_tokens_s": round(PEAK_HBM_GBS * 1e9 / step_bytes, 1),
         "wall_tokens_s": round(args.steps / wall, 2),
         "setup_s": round(t_gen, 1),
     }
-    if not args.no_cpu_baseline and args.workload == "dense2b":
+    if traffic is not None:
+        # beta: bytes moved per algorithmic byte (the KV history is counted as read once)
+        beta = (traffic - kv_avg) / wbytes
+        out["beta"] = round(beta, 4)
+        out["bound_tokens_s_measured_beta"] = round(PEAK_HBM_GBS * 1e9 / (beta * wbytes + kv_avg), 1)
+
+    if k_win == 4:
+        # the 4-token verify window over the tokens of four steps, at the
+        # first decode position (rewriting the same four cache positions)
+        win = torch.tensor([int(t) for t in gen.prompt_tokens(cfg, 4)], dtype=torch.int32, device=dev)
+        wl = torch.empty((4, cfg.vocab), dtype=torch.float32, device=dev)
+        wa = torch.zeros(4, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            dm.verify(win, cfg.prefill, wl, wa)
+        ms_win = timed(stream, lambda i: dm.verify(win, cfg.prefill, wl, wa), max(5, args.steps // 4))
+        if dm.status() != 0:
+            raise RuntimeError("device status after the verify windows")
+        distinct = []
+        for li in range(cfg.n_layers):
+            idx, _ = dm.routing(li)
+            distinct.append(len(np.unique(idx)))
+        nd = float(np.mean(distinct))
+        wb = window_bytes(cfg, cfg.prefill, 4, nd)
+        out["verify_window"] = {
+            "k": 4, "ms_per_window": round(ms_win, 4), "tokens_s": round(4e3 / ms_win, 1),
+            "window_over_step": round(ms_win / ms_per_step, 3), "distinct_experts_per_layer": round(nd, 2),
+            "bytes_per_window": wb, "achieved_GBs": round(wb / (ms_win / 1e3) / 1e9, 1),
+        }
+
+    if args.trace:
+        from memory_bound_gemv_amd import _mbg as M
+        M.mbg_set_trace(dm.ctx, True)
+        dm.step(buf, pos_of(args.warmup + args.steps), logits, buf)
+        rec = M.mbg_read_trace(dm.ctx, info.n_tasks)
+        M.mbg_set_trace(dm.ctx, False)
+        np.save(args.trace, rec)
+        np.save(args.trace.replace(".npy", "_meta.npy"),
+                np.array([info.clock_khz, info.grid, cfg.n_layers], dtype=np.int64))
+
+    copy_probe(args, dev)
+    if not args.no_cpu_baseline and cfg.kv_dtype == "bf16":
         out["cpu_baseline"] = cpu_baseline(cfg, host)
-    print(json.dumps(out), flush=True)
     dm.close()
+    return out
+
+
+def copy_probe(args, dev):
+    if args.copy_probe_mib:
+        import torch
+        n = args.copy_probe_mib * 1024 * 1024 // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+
+
+def run_lmhead(args, cfg):
+    """The LM-head GEMV + argmax alone, BF16 or FP8 rows, k columns."""
+    import numpy as np
+    import torch
+
+    from memory_bound_gemv_amd import _mbg as M
+    from synth import gen
+
+    dev = torch.device("cuda:0")
+    V, H, k = cfg.vocab, cfg.hidden, args.k
+    stream = torch.cuda.current_stream(dev)
+    w = gen.lm_head_bf16(cfg)
+    wd = torch.from_numpy(np.ascontiguousarray(w).view(np.int16)).to(dev)
+    copies = []
+    for c in range(3):
+        if args.lm_dtype == "fp8":
+            codes = torch.empty((V, H), dtype=torch.uint8, device=dev)
+            scales = torch.empty(V, dtype=torch.float32, device=dev)
+            M.mbg_quantize_fp8_rows(wd, V, H, codes, scales, stream.cuda_stream)
+            copies.append((M.make_tensor(codes, "fp8", V, H, scale=scales), codes, scales))
+        else:
+            t = wd.clone()
+            copies.append((M.make_tensor(t, "bf16", V, H), t))
+    del wd
+    x = torch.from_numpy(gen.lm_head_inputs(cfg, k)).to(dev)
+    logits = torch.empty((k, V), dtype=torch.float32, device=dev)
+    amax = torch.zeros(k, dtype=torch.int32, device=dev)
+    nbytes = M.mbg_lm_head_workspace_size(k)
+    ws = torch.zeros(nbytes // 4, dtype=torch.int32, device=dev)
+    call = lambda i: M.mbg_lm_head(copies[i % 3][0], x, k, logits, amax, ws, nbytes, stream.cuda_stream)
+    for i in range(args.warmup):
+        call(i)
+    ms = timed(stream, call, args.steps)
+    wbytes = V * H * (1 if args.lm_dtype == "fp8" else 2) + (4 * V if args.lm_dtype == "fp8" else 0)
+    achieved = wbytes / (ms / 1e3) / 1e9
+    name = f"lm_head_kernel_{args.lm_dtype}_k{k}"
+    copy_probe(args, dev)
+    return {
+        "metric": "LM-head GEMV + argmax: calls/s and achieved HBM GB/s (MBU % of peak) on 1 MI355X",
+        "value": round(1e3 / ms, 1), "unit": "calls/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp32", "data": "synthetic",
+        "config": {"workload": WORKLOADS["lmhead"], "weight_dtype": args.lm_dtype, "columns": k},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": stored_traffic(name)},
+        "bytes_per_call": wbytes,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense2b", "longctx", "lmhead"],
+                    help="moe (default: the routed 42-layer model), dense2b, longctx (FP8 KV at 200K "
+                         "positions) or lmhead (the LM-head GEMV alone)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-verify", action="store_true", help="moe: skip the 4-token verify-window timing")
+    ap.add_argument("--lm-dtype", default="fp8", choices=["bf16", "fp8"], help="lmhead: weight format")
+    ap.add_argument("--k", type=int, default=1, help="lmhead: activation columns (1..4)")
+    ap.add_argument("--trace", default="",
+                    help="after the timed region, run one traced step and save its per-task stamps (.npy)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the decode path has no "
+              "multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+
+    from synth import CONFIGS
+    cfg = CONFIGS[args.workload]
+    out = run_lmhead(args, cfg) if args.workload == "lmhead" else run_decode(args, cfg)
+    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

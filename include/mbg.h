@@ -23,8 +23,8 @@
  *     E4M3FN.  MXFP4 is OCP E2M1 (element 2i in the low nibble of byte i)
  *     with one E8M0 scale byte per 32 consecutive elements of a row.
  *   - The caller owns every buffer (weights, KV pool, page table, workspace,
- *     outputs).  The library never allocates or frees device memory; an
- *     mbg_ctx is a host object.
+ *     dependency-counter block, outputs).  No call allocates or frees device
+ *     memory; an mbg_ctx is a host object.
  *   - Calls that take a stream enqueue work on it and return without
  *     waiting.  A stream is a hipStream_t passed as void* (NULL = the null
  *     stream).
@@ -141,6 +141,7 @@ typedef struct {
     int32_t launches_per_step;
     int32_t lm_dtype, kv_dtype, expert_dtype, attn_dtype;
     int32_t attn_splits;      /* split-KV partitions per KV head */
+    int32_t attn_local;       /* 1: a KV head's splits run on one XCD and exchange partials through its L2 */
     int32_t trace;            /* 1 while in-kernel trace stamps are on (mbg_set_trace) */
     int64_t weight_bytes_per_step; /* bytes of weights one step reads (dense/shared; MoE routed excluded) */
     int64_t workspace_bytes;
@@ -152,33 +153,70 @@ typedef struct mbg_ctx mbg_ctx;
 
 /* ------------------------------------------------------ decode context */
 
-/* Bytes of device workspace a context for `cfg` needs. */
+/* Bytes of device workspace a context for `cfg` needs: task lists, RoPE
+ * table, the activations that pass between the ops of a step (residual
+ * stream, q, split-KV partials, attention output, FFN hidden), argmax keys
+ * and the trace buffer.  The step is the persistent one-launch kernel of
+ * the Kog article "Real-time LLM inference on standard GPUs: 3k tokens/s
+ * per request" (section on co-designing engine, GPU code and model: the
+ * monokernel), whose intermediate values never leave device memory.
+ * Host-only; errors: MBG_E_INVALID_ARG, MBG_E_UNSUPPORTED for the config. */
 int mbg_workspace_size(const mbg_config *cfg, size_t *bytes);
+
+/* Bytes of the dependency-counter block a context for `cfg` needs (one
+ * 128-byte line for the status, LM-head counter and flag words, then
+ * 8 x 128 bytes per (layer, phase) counter; under 1 MiB for 64 layers).
+ * The counters replace kernel boundaries with flag polling inside one
+ * launch ("Muse Spark Open: 1,109 tokens/s" article, section on the three
+ * bills of a kernel this large: synchronisation).  Host-only. */
+int mbg_counter_bytes(const mbg_config *cfg, size_t *bytes);
 
 /* Host-only check of a configuration, weight set and KV description: shapes,
  * dtypes, scale presence, alignment, supported combinations.  Makes no HIP
- * call and touches no device memory.  w or kv may be NULL to check less. */
+ * call and touches no device memory.  w or kv may be NULL to check less.
+ * This is the start-up check the 163.com Ling-3.0-flash article asks for
+ * (caveat section and conclusion: an FP8 LM head read as BF16 by a part of
+ * the model that did not share the module fell back silently and ran slower
+ * than no optimisation); every tensor here carries its own dtype and scale,
+ * and a mismatch is MBG_E_DTYPE_MISMATCH rather than a silent fallback.
+ * Errors: MBG_E_INVALID_ARG (null data, bad shape, misaligned rows),
+ * MBG_E_DTYPE_MISMATCH, MBG_E_UNSUPPORTED (no compiled kernel). */
 int mbg_validate(const mbg_config *cfg, const mbg_weights *w, const mbg_kv *kv);
 
 /* Validate, build the static per-step task list in the caller's workspace
  * (device, >= mbg_workspace_size bytes, 256-byte aligned) with copies
- * enqueued on `stream`, and return a host context.  The dependency counters
- * and the device status word live in a small block of uncached device
- * memory (under 1 MiB) that the library takes from a process-wide pool or
- * allocates on the current device; the step kernel polls it with
- * cache-bypassing scalar loads.  The weights, KV pool and workspace must
- * outlive the context. */
+ * enqueued on `stream`, zero the caller's counter block, and return a host
+ * context (Kog article, monokernel section: the whole step becomes one
+ * resident program; the task lists are its schedule).
+ *   d_counters: device memory of >= mbg_counter_bytes bytes, 256-byte
+ *     aligned, that the L2 does not cache (hipExtMallocWithFlags with
+ *     hipDeviceMallocUncached).  The step kernel polls it with
+ *     cache-bypassing scalar loads, which see other XCDs' counter updates
+ *     only in uncached memory.  The caller keeps it while the context
+ *     lives; per the HIP runtime's rules for uncached memory it should
+ *     not be freed before the process ends once a kernel has read it, so
+ *     a caller reuses it for later contexts.  One context per block.
+ * The weights, KV pool, workspace and counter block must outlive the
+ * context.  Errors: as mbg_validate, MBG_E_WORKSPACE (workspace or counter
+ * block missing, small or misaligned), MBG_E_RANGE (a page-table entry
+ * outside the pool), MBG_E_HIP. */
 int mbg_decode_init(const mbg_config *cfg, const mbg_weights *w, const mbg_kv *kv,
-                    void *d_workspace, size_t workspace_bytes, void *stream, mbg_ctx **out);
+                    void *d_workspace, size_t workspace_bytes, void *d_counters, size_t counter_bytes,
+                    void *stream, mbg_ctx **out);
 
 /* One decode step, one kernel launch on the init stream.  Reads the token
  * id at d_token[0] (device int32; may alias the previous step's d_argmax so
  * a greedy loop needs no host round trip), writes K/V of every layer at
  * `pos`, attends over [0, pos], and writes logits (device float [vocab], may
  * be NULL) and the argmax (device int32 [1], lowest index among equal
- * maxima).  Token ids outside [0, vocab) are clamped on the device and
- * latch MBG_E_RANGE (reported by mbg_get_status).  Returns MBG_E_RANGE if
- * pos is outside [0, max_pos). */
+ * maxima).  What the step computes is the chain of matrix-vector products
+ * over every active weight of the Kog article's bandwidth section; one
+ * launch per step removes the launch and clean-up costs of its section on
+ * where standard stacks lose microseconds.  A token id outside [0, vocab)
+ * is clamped on the device, the step completes, and MBG_E_RANGE is
+ * reported by the next mbg_get_status.  Returns MBG_E_RANGE if pos is
+ * outside [0, max_pos), MBG_E_INVALID_ARG for null pointers, MBG_E_HIP if
+ * the launch fails. */
 int mbg_decode_step(mbg_ctx *ctx, const int32_t *d_token, int32_t pos,
                     float *d_logits, int32_t *d_argmax);
 
@@ -193,17 +231,32 @@ int mbg_decode_step(mbg_ctx *ctx, const int32_t *d_token, int32_t pos,
 int mbg_decode_verify(mbg_ctx *ctx, const int32_t *d_tokens, int32_t k, int32_t pos,
                       float *d_logits, int32_t *d_argmax);
 
-/* Wait for the init stream, then return the latched device status (0, or
- * MBG_E_TIMEOUT / MBG_E_RANGE from a kernel) and clear it. */
+/* Wait for the init stream, then return the device status of the calls
+ * since the last mbg_get_status: 0, MBG_E_TIMEOUT (a dependency wait
+ * exceeded its deadline and the launch drained), MBG_E_UNSUPPORTED (the
+ * workgroups were not placed on the XCDs the attention placement assumes),
+ * or MBG_E_RANGE (a token id was clamped; that step completed).  After
+ * MBG_E_TIMEOUT or MBG_E_UNSUPPORTED every counter of the context is reset
+ * and its launch count starts over, so the next call runs normally; until
+ * mbg_get_status is called, later launches give up at their first wait.
+ * The positions an aborted launch was writing hold partial K/V: the caller
+ * reruns that step.  The watchdog is the device-side reading of the
+ * synchronisation bill ("Muse Spark Open" article, section on the three
+ * bills): a polled flag that never arrives must not hang the GPU. */
 int mbg_get_status(mbg_ctx *ctx);
 
 /* Describe the active configuration (see mbg_info). */
 int mbg_query(const mbg_ctx *ctx, mbg_info *info);
 
-/* Set the device wait deadline in microseconds (default 2,000,000).  A wait
- * on a dependency counter that exceeds it makes its workgroup record
- * MBG_E_TIMEOUT and leave; every other wait then ends the same way, so the
- * launch always drains. */
+/* Set the device wait deadline in microseconds (default 2,000,000) for
+ * later launches.  A wait on a dependency counter that exceeds it makes its
+ * workgroup record MBG_E_TIMEOUT and leave; every other wait then ends the
+ * same way, so the launch always drains (see mbg_get_status for recovery).
+ * A spinning wait reads the clock every 32nd poll, every poll under a
+ * deadline below 1,000 us.  The deadline is the watchdog side of the flag
+ * polling that replaces kernel boundaries ("Muse Spark Open" article,
+ * section on the three bills: synchronisation).  MBG_E_INVALID_ARG for
+ * us <= 0. */
 int mbg_set_timeout_us(mbg_ctx *ctx, int64_t us);
 
 /* Per-task self-profiling.  With `on` != 0, every later step makes thread 0
@@ -235,10 +288,9 @@ int mbg_read_routing(mbg_ctx *ctx, int32_t layer, int32_t *idx, float *weights, 
 /* Text of the last error on this thread ("" if none). */
 const char *mbg_last_error(void);
 
-/* Wait for the context's stream, return its uncached counter block to the
- * process-wide pool (uncached memory is not handed back to the runtime once
- * a kernel has read it; later contexts reuse it) and free the host context.
- * Does not touch caller memory. */
+/* Wait for the context's stream and free the host context.  Does not touch
+ * caller memory (the counter block can then serve another context).  The
+ * counterpart of mbg_decode_init's set-up of the Kog article's monokernel. */
 void mbg_destroy(mbg_ctx *ctx);
 
 /* ------------------------------------------------ standalone operations */
@@ -272,7 +324,13 @@ int mbg_quantize_fp8_rows(const uint16_t *d_w, int64_t rows, int64_t cols, uint8
  * into the paged cache in its storage format (BF16 nearest-even, or FP8
  * value / scale in binary32, nearest-even, saturating), the same rounding a
  * decode step applies to the K/V it produces.  d_k, d_v: device float
- * [n][n_kv_heads][head_dim].  Used to fill a cache from a prefill. */
+ * [n][n_kv_heads][head_dim].  Used to fill a cache from a prefill: the
+ * paged FP8 cache with per-head scales of the wmrh.cn Kimi-K3 long-context
+ * report (test environment and configuration: 64-token pages, fp8_e4m3; its
+ * warnings section: a missing scale fell back to 1.0, so an FP8 cache
+ * without scales is MBG_E_DTYPE_MISMATCH here).  Errors: MBG_E_RANGE
+ * (layer, positions or a page-table entry out of range), MBG_E_INVALID_ARG,
+ * MBG_E_UNSUPPORTED, MBG_E_HIP. */
 int mbg_kv_write(const mbg_config *cfg, const mbg_kv *kv, int32_t layer, int32_t pos0, int32_t n,
                  const float *d_k, const float *d_v, void *stream);
 

@@ -8,8 +8,7 @@ import ctypes as C
 import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# MBG_LIBRARY names another build of the same library (A/B measurements)
-LIB_PATH = os.environ.get("MBG_LIBRARY") or os.path.join(HERE, "libmbg.so")
+LIB_PATH = os.path.join(HERE, "libmbg.so")
 
 MBG_OK = 0
 MBG_E_INVALID_ARG = -1
@@ -66,7 +65,7 @@ class mbg_config(C.Structure):
 
 class mbg_info(C.Structure):
     _fields_ = [(f, C.c_int32) for f in ("grid", "block", "n_tasks", "launches_per_step", "lm_dtype", "kv_dtype",
-                                          "expert_dtype", "attn_dtype", "attn_splits", "trace")] + [
+                                          "expert_dtype", "attn_dtype", "attn_splits", "attn_local", "trace")] + [
         ("weight_bytes_per_step", C.c_int64), ("workspace_bytes", C.c_int64), ("clock_khz", C.c_int64),
         ("variant", C.c_char * 64)]
 
@@ -86,8 +85,10 @@ def _load():
     sig = {
         "mbg_workspace_size": (C.c_int, [C.POINTER(mbg_config), C.POINTER(C.c_size_t)]),
         "mbg_validate": (C.c_int, [C.POINTER(mbg_config), C.POINTER(mbg_weights), C.POINTER(mbg_kv)]),
+        "mbg_counter_bytes": (C.c_int, [C.POINTER(mbg_config), C.POINTER(C.c_size_t)]),
         "mbg_decode_init": (C.c_int, [C.POINTER(mbg_config), C.POINTER(mbg_weights), C.POINTER(mbg_kv),
-                                      C.c_void_p, C.c_size_t, C.c_void_p, C.POINTER(CTX_P)]),
+                                      C.c_void_p, C.c_size_t, C.c_void_p, C.c_size_t, C.c_void_p,
+                                      C.POINTER(CTX_P)]),
         "mbg_decode_step": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
         "mbg_decode_verify": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
         "mbg_get_status": (C.c_int, [CTX_P]),
@@ -114,7 +115,7 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("mbg_workspace_size", "mbg_validate", "mbg_decode_init", "mbg_decode_step", "mbg_decode_verify",
+EXPORTED = ("mbg_workspace_size", "mbg_counter_bytes", "mbg_validate", "mbg_decode_init", "mbg_decode_step", "mbg_decode_verify",
             "mbg_get_status", "mbg_query", "mbg_set_timeout_us", "mbg_set_trace", "mbg_read_trace",
             "mbg_read_routing", "mbg_last_error", "mbg_destroy",
             "mbg_lm_head_workspace_size", "mbg_lm_head", "mbg_quantize_fp8_rows", "mbg_kv_write")
@@ -184,6 +185,12 @@ def mbg_workspace_size(cfg: mbg_config) -> int:
     return n.value
 
 
+def mbg_counter_bytes(cfg: mbg_config) -> int:
+    n = C.c_size_t(0)
+    _check(_lib.mbg_counter_bytes(C.byref(cfg), C.byref(n)))
+    return n.value
+
+
 def mbg_validate(cfg: mbg_config, weights=None, kv=None) -> int:
     """Returns the library's code (0 or negative); does not raise."""
     w = C.byref(weights.struct) if weights is not None else None
@@ -191,10 +198,11 @@ def mbg_validate(cfg: mbg_config, weights=None, kv=None) -> int:
     return _lib.mbg_validate(C.byref(cfg), w, k)
 
 
-def mbg_decode_init(cfg, weights: WeightSet, kv, workspace, ws_bytes: int, stream: int):
+def mbg_decode_init(cfg, weights: WeightSet, kv, workspace, ws_bytes: int, counters, counter_bytes: int,
+                    stream: int):
     ctx = CTX_P()
     _check(_lib.mbg_decode_init(C.byref(cfg), C.byref(weights.struct), C.byref(kv), _ptr(workspace), ws_bytes,
-                                stream, C.byref(ctx)))
+                                _ptr(counters), counter_bytes, stream, C.byref(ctx)))
     return ctx
 
 

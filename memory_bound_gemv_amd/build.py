@@ -19,7 +19,9 @@ ARCH = "gfx950"
 # Packed FP32 instructions stay off: plain float code only.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wno-unused-command-line-argument"]
-SOURCES = ["step.hip", "ops.hip", "api.cpp"]
+# step.hip is built once per compiled model family (-DMBG_STEP_SHAPE=i), in parallel
+STEP_SHAPES = 4
+SOURCES = [("step.hip", i) for i in range(STEP_SHAPES)] + [("ops.hip", None), ("api.cpp", None)]
 
 
 def source_digest() -> str:
@@ -38,10 +40,13 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def _compile(src: str, extra) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
+def _compile(item, extra) -> str:
+    src, shape = item
+    tag = "" if shape is None else f".shape{shape}"
+    obj = os.path.join(BUILD, os.path.basename(src) + tag + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    defs = [] if shape is None else [f"-DMBG_STEP_SHAPE={shape}"]
+    cmd = [HIPCC, *FLAGS, *defs, *extra, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed on {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

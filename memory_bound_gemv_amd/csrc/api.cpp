@@ -53,13 +53,14 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct Plan {
     size_t keys, head_ctr, task_off, tasks, layers, inv_freq, rope_cs;
     size_t xres, qbuf, part, attn, hbuf, rlogits, route_w, route_idx, trace, total;
-    int64_t hb_ld;
+    int64_t hb_ld, part_layer;
     size_t n_ctr, max_tasks, zero_bytes;
-    size_t uc_bytes;   // library-owned uncached block: status word, LM-head counter, dependency counters
+    size_t uc_bytes;   // caller's uncached counter block: status, LM-head counter, flags, dependency counters
 };
 
-// Bytes of the uncached block: one 128-byte line for the status word and the
-// LM-head counter, then the dependency counters.
+// The counter block: one 128-byte line for the status word (word 0), the
+// LM-head counter (word 1) and the flag word (word 2), then the dependency
+// counters.
 constexpr size_t kUcCtrOffset = 128;
 
 Plan make_plan(const mbg_config& c) {
@@ -85,7 +86,8 @@ Plan make_plan(const mbg_config& c) {
     p.rope_cs = take(8 * (size_t)c.max_pos * (c.head_dim / 2));
     p.xres = take(4 * k * c.hidden);
     p.qbuf = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
-    p.part = take(4 * k * (size_t)c.n_q_heads * kMaxSplits * (c.head_dim + 4));   // rows: o, m, l, 2 pad
+    p.part_layer = (int64_t)k * c.n_q_heads * kMaxSplits * (c.head_dim + 4);   // rows: o, m, l, 2 pad
+    p.part = take(4 * L * (size_t)p.part_layer);
     p.attn = take(4 * k * (size_t)c.n_q_heads * c.head_dim);
     // MoE: a window of k tokens uses at most k * top_k routed experts plus the shared ones
     p.hb_ld = c.n_experts > 0 ? (int64_t)(k * c.top_k + c.n_shared) * c.moe_ffn : c.ffn;
@@ -100,38 +102,6 @@ Plan make_plan(const mbg_config& c) {
 }
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
-
-// Uncached device memory for the dependency counters and the status word
-// (the step kernel polls them with cache-bypassing scalar loads, which
-// return the memory-side value only for memory the L2 does not cache).
-// Uncached blocks are not handed back to the runtime once a kernel has read
-// them: a destroyed context returns its block to this process-wide pool and
-// later contexts on the same device reuse it.
-struct UcBlock {
-    int dev;
-    size_t bytes;
-    void* p;
-};
-std::mutex g_uc_mu;
-std::vector<UcBlock> g_uc_free;
-
-hipError_t uc_acquire(int dev, size_t bytes, void** out) {
-    std::lock_guard<std::mutex> lk(g_uc_mu);
-    for (size_t i = 0; i < g_uc_free.size(); ++i) {
-        if (g_uc_free[i].dev == dev && g_uc_free[i].bytes >= bytes) {
-            *out = g_uc_free[i].p;
-            g_uc_free.erase(g_uc_free.begin() + (long)i);
-            return hipSuccess;
-        }
-    }
-    return hipExtMallocWithFlags(out, bytes, hipDeviceMallocUncached);
-}
-
-void uc_release(int dev, size_t bytes, void* p) {
-    if (!p) return;
-    std::lock_guard<std::mutex> lk(g_uc_mu);
-    g_uc_free.push_back(UcBlock{dev, bytes, p});
-}
 
 int check_tensor(const mbg_tensor& t, const char* name, int dtype, int64_t n, int64_t rows, int64_t cols) {
     if (t.data == nullptr) return fail(MBG_E_INVALID_ARG, "%s: data is NULL", name);
@@ -196,6 +166,22 @@ StepVariant variant_of(const mbg_config* c, int kv_dtype) {
     return v;
 }
 
+}  // namespace
+
+namespace mbg {
+const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out) {
+    using Fn = const void* (*)(const StepVariant&, int, int*);
+    static const Fn fns[kStepShapes] = {step_kernel_shape_0, step_kernel_shape_1, step_kernel_shape_2,
+                                        step_kernel_shape_3};
+    for (Fn f : fns)
+        if (const void* k = f(v, ncol, lds_bytes_out)) return k;
+    return nullptr;
+}
+bool step_variant_supported(const StepVariant& v) { return step_kernel_for(v, 1, nullptr) != nullptr; }
+}  // namespace mbg
+
+namespace {
+
 int device_cus(int* cus) {
     int dev = 0;
     HIP_TRY(hipGetDevice(&dev));
@@ -221,9 +207,10 @@ struct mbg_ctx {
     int n_tasks;
     int trace_on;
     int last_ncol;   // columns of the last step/verify call (0: none yet)
-    void* uc;        // uncached block (counters, status), from the pool
+    void* uc;        // the caller's uncached counter block
     size_t uc_bytes;
-    int dev;
+    void* ws_zero;   // start of the workspace region that starts at zero (argmax keys, head counters)
+    size_t ws_zero_bytes;
     unsigned long long* trace_buf;
     char variant[64];
 };
@@ -237,6 +224,14 @@ int mbg_workspace_size(const mbg_config* cfg, size_t* bytes) {
     if (rc) return rc;
     if (!bytes) return fail(MBG_E_INVALID_ARG, "bytes is NULL");
     *bytes = make_plan(*cfg).total;
+    return MBG_OK;
+}
+
+int mbg_counter_bytes(const mbg_config* cfg, size_t* bytes) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!bytes) return fail(MBG_E_INVALID_ARG, "bytes is NULL");
+    *bytes = make_plan(*cfg).uc_bytes;
     return MBG_OK;
 }
 
@@ -298,7 +293,7 @@ int mbg_validate(const mbg_config* c, const mbg_weights* w, const mbg_kv* kv) {
 }
 
 int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* kv, void* d_ws, size_t ws_bytes,
-                    void* stream, mbg_ctx** out) {
+                    void* d_counters, size_t counter_bytes, void* stream, mbg_ctx** out) {
     if (!out) return fail(MBG_E_INVALID_ARG, "out is NULL");
     *out = nullptr;
     if (!w || !kv) return fail(MBG_E_INVALID_ARG, "weights and kv are required");
@@ -309,6 +304,9 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     if (!d_ws || ws_bytes < plan.total)
         return fail(MBG_E_WORKSPACE, "workspace %zu bytes, need %zu", ws_bytes, plan.total);
     if (((uintptr_t)d_ws & 255u) != 0) return fail(MBG_E_WORKSPACE, "workspace not 256-byte aligned");
+    if (!d_counters || counter_bytes < plan.uc_bytes)
+        return fail(MBG_E_WORKSPACE, "counter block %zu bytes, need %zu", counter_bytes, plan.uc_bytes);
+    if (((uintptr_t)d_counters & 255u) != 0) return fail(MBG_E_WORKSPACE, "counter block not 256-byte aligned");
     hipStream_t s = reinterpret_cast<hipStream_t>(stream);
 
     int cus = 0;
@@ -540,17 +538,14 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     for (int i = 0; i < HALF; ++i) inv[i] = std::pow((double)c.rope_theta, -2.0 * i / c.head_dim);
 
     char* base = static_cast<char*>(d_ws);
-    void* uc = nullptr;
-    hipError_t eu = uc_acquire(dev, plan.uc_bytes, &uc);
-    if (eu != hipSuccess) {
-        delete x;
-        return hip_fail(eu, "uncached counter block");
-    }
+    void* uc = d_counters;
     x->uc = uc;
     x->uc_bytes = plan.uc_bytes;
-    x->dev = dev;
+    x->ws_zero = base;
+    x->ws_zero_bytes = plan.zero_bytes;
     a.status = (uint32_t*)uc;
     a.lm_ctr = a.status + 1;
+    a.flags = a.status + 2;
     a.amax_keys = (unsigned long long*)(base + plan.keys);
     a.ctr = (uint32_t*)((char*)uc + kUcCtrOffset);
     a.head_ctr = (uint32_t*)(base + plan.head_ctr);
@@ -562,6 +557,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.xres = (float*)(base + plan.xres);
     a.qbuf = (float*)(base + plan.qbuf);
     a.part = (float*)(base + plan.part);
+    a.part_layer = plan.part_layer;
     a.attn = (float*)(base + plan.attn);
     a.hbuf = (float*)(base + plan.hbuf);
     a.hb_ld = (int32_t)plan.hb_ld;
@@ -594,7 +590,6 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
         e = launch_rope_table((const double*)(base + plan.inv_freq), HALF, c.max_pos, (float2*)(base + plan.rope_cs), s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
     if (e != hipSuccess) {
-        uc_release(dev, plan.uc_bytes, uc);
         delete x;
         return hip_fail(e, "workspace upload");
     }
@@ -617,6 +612,7 @@ static int launch_step(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t p
     a.ncol = k;
     a.epoch = ++x->epoch;
     a.deadline_ticks = (uint64_t)x->timeout_us * (uint64_t)x->wall_khz / 1000ull;
+    a.clock_mask = x->timeout_us < 1000 ? 0u : 31u;
     void* args[] = {&a};
     hipError_t e = hipLaunchCooperativeKernel(x->fn[k], dim3(x->grid), dim3(kBlock), args, (unsigned)x->lds[k],
                                               x->stream);
@@ -637,16 +633,27 @@ int mbg_decode_verify(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t po
 int mbg_get_status(mbg_ctx* x) {
     if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
     HIP_TRY(hipStreamSynchronize(x->stream));
-    uint32_t st = 0;
-    HIP_TRY(hipMemcpy(&st, x->base.status, 4, hipMemcpyDeviceToHost));
+    uint32_t w[3] = {0, 0, 0};   // status, LM-head counter, flags
+    HIP_TRY(hipMemcpy(w, x->base.status, sizeof w, hipMemcpyDeviceToHost));
+    const uint32_t st = w[0], fl = w[2];
     if (st != 0) {
-        HIP_TRY(launch_fill_u32(x->base.status, 1, 0u, x->stream));
+        // An aborted launch leaves dependency, arrival and LM-head counters
+        // short of epoch x need and may leave argmax keys set: start the
+        // context over from epoch 0 with every counter and key at zero.
+        HIP_TRY(launch_fill_u32((uint32_t*)x->uc, x->uc_bytes / 4, 0u, x->stream));
+        HIP_TRY(launch_fill_u32((uint32_t*)x->ws_zero, x->ws_zero_bytes / 4, 0u, x->stream));
         HIP_TRY(hipStreamSynchronize(x->stream));
+        x->epoch = 0;
         if (st == kStatusTimeout) return fail(MBG_E_TIMEOUT, "a device wait exceeded its deadline");
-        if (st == kStatusRange) return fail(MBG_E_RANGE, "a token id was outside [0, vocab)");
         if (st == kStatusPlacement)
             return fail(MBG_E_UNSUPPORTED, "workgroups are not placed on XCD blockIdx %% 8; set MBG_ATTN_LOCAL=0");
         return fail(MBG_E_HIP, "device status %u", st);
+    }
+    if (fl != 0) {
+        HIP_TRY(launch_fill_u32(x->base.flags, 1, 0u, x->stream));
+        HIP_TRY(hipStreamSynchronize(x->stream));
+        if (fl == kStatusRange) return fail(MBG_E_RANGE, "a token id was outside [0, vocab) and was clamped");
+        return fail(MBG_E_HIP, "device flag %u", fl);
     }
     return MBG_OK;
 }
@@ -663,6 +670,7 @@ int mbg_query(const mbg_ctx* x, mbg_info* info) {
     info->expert_dtype = x->cfg.n_experts ? MBG_MXFP4 : 0;
     info->attn_dtype = MBG_BF16;
     info->attn_splits = x->base.attn_splits;
+    info->attn_local = x->base.attn_local;
     info->trace = x->trace_on;
     info->clock_khz = x->wall_khz;
     info->weight_bytes_per_step = x->weight_bytes;
@@ -710,10 +718,8 @@ int mbg_read_routing(mbg_ctx* x, int32_t layer, int32_t* idx, float* weights, in
 
 void mbg_destroy(mbg_ctx* x) {
     if (!x) return;
-    // the context's last launch must be done with the counters before another
-    // context reuses the block
+    // the context's last launch must be done with the caller's buffers
     (void)hipStreamSynchronize(x->stream);
-    uc_release(x->dev, x->uc_bytes, x->uc);
     delete x;
 }
 
@@ -726,8 +732,7 @@ int mbg_lm_head_workspace_size(int32_t k, size_t* bytes) {
     return MBG_OK;
 }
 
-int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logits, int32_t* d_argmax,
-                void* d_ws, size_t ws_bytes, void* stream) {
+static int lm_head_check(const mbg_tensor* w, const float* d_x, int32_t k, const int32_t* d_argmax) {
     if (!w || !d_x || !d_argmax) return fail(MBG_E_INVALID_ARG, "w/x/argmax is NULL");
     if (k < 1 || k > 4) return fail(MBG_E_RANGE, "k %d outside [1, 4]", k);
     if (w->dtype != MBG_BF16 && w->dtype != MBG_FP8_E4M3 && w->dtype != MBG_MXFP4)
@@ -742,8 +747,14 @@ int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logit
         return fail(MBG_E_UNSUPPORTED, "lm head hidden size %lld not compiled in", (long long)w->cols);
     if ((size_t)k * w->cols * 4 + 256 > 160 * 1024)
         return fail(MBG_E_UNSUPPORTED, "k * cols too large for on-chip activations");
-    if (!d_ws || ws_bytes < 256) return fail(MBG_E_WORKSPACE, "workspace %zu bytes, need 256", ws_bytes);
+    return MBG_OK;
+}
+
+// keys at d_ws, counter at d_ws + 64; both zero on entry and left at zero
+static int lm_head_launch(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logits, int32_t* d_argmax,
+                          void* d_ws, void* stream) {
     static int cus = 0;
+    int rc = 0;
     if (cus == 0 && (rc = device_cus(&cus))) return rc;
     LmHeadArgs a;
     a.w = w->data;
@@ -760,6 +771,14 @@ int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logit
     hipError_t e = launch_lm_head(a, k, fmt, (int)grid, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "lm_head launch");
     return MBG_OK;
+}
+
+int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logits, int32_t* d_argmax,
+                void* d_ws, size_t ws_bytes, void* stream) {
+    int rc = lm_head_check(w, d_x, k, d_argmax);
+    if (rc) return rc;
+    if (!d_ws || ws_bytes < 256) return fail(MBG_E_WORKSPACE, "workspace %zu bytes, need 256", ws_bytes);
+    return lm_head_launch(w, d_x, k, d_logits, d_argmax, d_ws, stream);
 }
 
 int mbg_quantize_fp8_rows(const uint16_t* d_w, int64_t rows, int64_t cols, uint8_t* d_codes, float* d_scales,

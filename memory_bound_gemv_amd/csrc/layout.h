@@ -122,10 +122,13 @@ struct StepArgs {
     uint32_t* ctr;             // [n_layers * PH_COUNT][kCtrLines lines], uncached memory
     uint32_t* head_ctr;        // [n_layers * n_kv_heads] split arrivals
     uint32_t* lm_ctr;          // LM-head tiles finished
-    uint32_t* status;          // first device error (uncached memory, beside the LM-head counter)
+    uint32_t* status;          // first device error that ends the launch (uncached memory)
+    uint32_t* flags;           // conditions that do not end the launch (a clamped token id)
     float* xres;               // [k][H] residual stream
     float* qbuf;               // [k][Hq][d]
-    float* part;               // [k][Hq][splits][d + 2] attention partials
+    float* part;               // [L][k][Hq][splits][d + 4] attention partials: each layer has its own
+                               // rows, so a partial-row address is written and read once per launch
+    int64_t part_layer;        // floats per layer of part
     float* attn;               // [k][Hq * d]
     float* hbuf;               // [k][F] or MoE [k][hb_ld]: column c, slot s, row f at c * hb_ld + s * M + f
     int32_t hb_ld;             // floats per column of hbuf
@@ -146,9 +149,12 @@ struct StepArgs {
     int32_t attn_local;        // 1: the splits of an attention group run on one XCD (workgroup b on XCD b % 8)
                                //    and exchange partials and arrivals through that XCD's L2
     uint64_t deadline_ticks;   // s_memrealtime ticks a wait may take
+    uint32_t clock_mask;       // a spinning wait reads the clock on poll rounds r with (r & mask) == 0
 };
 
 // Device status codes (positive on the device, negated at the boundary).
+// kStatusTimeout and kStatusPlacement end the launch (every wait gives up);
+// kStatusRange is a flag: the token id was clamped and the step completes.
 constexpr uint32_t kStatusTimeout = 7;
 constexpr uint32_t kStatusRange = 4;
 constexpr int kAttnLocalMaxSplitLen = 1024;    // XCD-local attention groups only up to this many positions per split

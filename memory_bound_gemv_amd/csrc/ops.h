@@ -49,5 +49,11 @@ struct StepVariant {
 // Returns the kernel entry for ncol columns, or null when not compiled in.
 const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out);
 bool step_variant_supported(const StepVariant& v);
+// One per compiled model family (step.hip built with MBG_STEP_SHAPE = i).
+constexpr int kStepShapes = 4;
+const void* step_kernel_shape_0(const StepVariant& v, int ncol, int* lds_bytes_out);
+const void* step_kernel_shape_1(const StepVariant& v, int ncol, int* lds_bytes_out);
+const void* step_kernel_shape_2(const StepVariant& v, int ncol, int* lds_bytes_out);
+const void* step_kernel_shape_3(const StepVariant& v, int ncol, int* lds_bytes_out);
 
 }  // namespace mbg

@@ -63,48 +63,27 @@ __shared__ uint64_t s_twait;  // trace: when the current task's wait was satisfi
 // policy), so no L2 write-back or invalidate is needed between phases: a
 // producer waits until its stores have completed, then bumps the phase
 // counter; a consumer that has seen the counter reads the data coherently.
-// Built with MBG_COHERENT=0 the same data moves through plain cached
-// accesses, ordered by release/acquire fences on the counters instead.
-#ifndef MBG_COHERENT
-#define MBG_COHERENT 1
-#endif
 __device__ __forceinline__ float ldc(const MBG_GLOBAL float* p) {
-#if MBG_COHERENT
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-    return *p;
-#endif
 }
 __device__ __forceinline__ void stc(MBG_GLOBAL float* p, float v) {
-#if MBG_COHERENT
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-    *p = v;
-#endif
 }
 template <class T>
 __device__ __forceinline__ void stc_small(MBG_GLOBAL T* p, T v) {
-#if MBG_COHERENT
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#else
-    *p = v;
-#endif
 }
 __device__ __forceinline__ uint4 ldc16(const MBG_GLOBAL uint4* p) {
-#if MBG_COHERENT
     const MBG_GLOBAL uint32_t* q = reinterpret_cast<const MBG_GLOBAL uint32_t*>(p);
     return make_uint4(__hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                       __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                       __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT),
                       __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-#else
-    return ld_g(p);
-#endif
 }
 // 16-byte device-coherent accesses: buffer instructions with the sc1 cache
 // policy, which is what a relaxed agent-scope atomic access of 4 bytes
 // compiles to on gfx950, four times wider.  Offsets are in bytes.
-constexpr int kCohAux = MBG_COHERENT ? 16 : 0;
+constexpr int kCohAux = 16;   // sc1
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
@@ -123,17 +102,6 @@ __device__ __forceinline__ f32x4 ldx4(rsrc_t r, uint32_t off) {
 }
 __device__ __forceinline__ void stx4(rsrc_t r, uint32_t off, f32x4 v) {
     __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, off, 0, 0);
-}
-
-__device__ __forceinline__ void acquire_after_wait() {
-#if !MBG_COHERENT
-    fence_acquire();
-#endif
-}
-__device__ __forceinline__ void release_before_signal() {
-#if !MBG_COHERENT
-    fence_release();
-#endif
 }
 
 // The kCtrLines lines of counter `lines` (128 bytes apart) and the status
@@ -190,8 +158,9 @@ __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
                 sload_counter(lines, a->status, sum, st);
                 if ((int32_t)(sum - target) >= 0) break;
                 if (st != 0u) { ok = 0; break; }
-                // the clock is a scalar memory read: consult it every 32nd round
-                if ((++rounds & 31u) == 0u && wall_clock64() - t0 > a->deadline_ticks) {
+                // the clock is a scalar memory read: consult it every 32nd
+                // round (every round under a deadline shorter than a millisecond)
+                if ((++rounds & a->clock_mask) == 0u && wall_clock64() - t0 > a->deadline_ticks) {
                     if (lane == 0) latch_error(a->status, kStatusTimeout);
                     ok = 0;
                     break;
@@ -200,7 +169,6 @@ __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
             }
         }
         if (lane == 0) {
-            if (ok) acquire_after_wait();
             s_ok = ok;
             s_twait = wall_clock64();
         }
@@ -215,16 +183,17 @@ __device__ __forceinline__ void release_counter(CArgs* a, uint32_t idx) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // vmcnt(0): this wave's stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
-        release_before_signal();
         MBG_GLOBAL uint32_t* line = gp(a->ctr) + ((size_t)idx * kCtrLines + (blockIdx.x & (kCtrLines - 1))) * kLineU32;
         __hip_atomic_fetch_add(line, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
+// Token id of column c, clamped into [0, vocab); a clamp raises the range
+// flag (reported by mbg_get_status) and the step completes normally.
 __device__ __forceinline__ int token_of(CArgs* a, int c) {
     int t = gp(a->tokens)[c];
     if (t < 0 || t >= a->vocab) {
-        if (threadIdx.x == 0) latch_error(a->status, kStatusRange);
+        if (threadIdx.x == 0) latch_error(a->flags, kStatusRange);
         t = t < 0 ? 0 : a->vocab - 1;
     }
     return t;
@@ -804,7 +773,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const float qscale = a->attn_scale_log2;
     lds_f32* red = reinterpret_cast<lds_f32*>(reinterpret_cast<MBG_LDS uint8_t*>(smem) + kAttnRingBytes);
     const rsrc_t rq = make_rsrc(a->qbuf);
-    const rsrc_t rp = make_rsrc(a->part);
+    const rsrc_t rp = make_rsrc(a->part + (size_t)layer * a->part_layer);
     // this group's splits share an XCD (and its L2); compiled for BF16 caches
     const bool local = KVF == F_BF16 && a->attn_local != 0;
     const bool empty = t0 >= t1;
@@ -926,7 +895,6 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if (threadIdx.x == 0) {
-        release_before_signal();
         // within the XCD: an L2 atomic; otherwise a device-scope one
         uint32_t old;
         if (local)
@@ -936,7 +904,6 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv * HG + gg) * kLineU32, 1u,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old + 1u == a->epoch * (uint32_t)S_);
-        if (s_last) acquire_after_wait();
     }
     __syncthreads();
     if (!s_last) return true;
@@ -1623,10 +1590,8 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __syncthreads();
     if (threadIdx.x == 0) {
-        release_before_signal();
         const uint32_t old = __hip_atomic_fetch_add(gp(a->lm_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         s_last = (old + 1u == a->epoch * a->tiles_lm);
-        if (s_last) acquire_after_wait();
     }
     __syncthreads();
     if (s_last && threadIdx.x < NC) {
@@ -1692,7 +1657,12 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
                 break;
             default: break;
         }
-        if (!ok) return;
+        if (!ok) {
+            // the launch is aborting: let every load this wave issued (weight
+            // prefetch, LDS DMA) land before the wave ends
+            __builtin_amdgcn_s_waitcnt(0);
+            return;
+        }
         __syncthreads();  // LDS is reused by the next task
         if (trace && threadIdx.x == 0) {
             MBG_GLOBAL unsigned long long* r = trace + (size_t)ti * 8;
@@ -1713,12 +1683,22 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
 // ----------------------------------------------------------- variants
 
 // Model families compiled in: Shape<hidden, ffn, q_heads * head_dim,
-// head_dim, q heads per KV head, KV format, MoE, moe_ffn>.
-using ShapeTiny = Shape<256, 1024, 256, 64, 2, F_BF16, 0, 0>;
-using ShapeDense2B = Shape<2048, 8192, 2048, 128, 2, F_BF16, 0, 0>;
-using ShapeDense2BFp8Kv = Shape<2048, 8192, 2048, 128, 2, F_FP8, 0, 0>;
-using ShapeMoE = Shape<2560, 0, 4096, 128, 8, F_BF16, 1, 768>;
-#define MBG_VARIANTS(X) X(ShapeTiny) X(ShapeDense2B) X(ShapeDense2BFp8Kv) X(ShapeMoE)
+// head_dim, q heads per KV head, KV format, MoE, moe_ffn>.  This file is
+// compiled once per family (MBG_STEP_SHAPE = 0 .. kStepShapes - 1), so the
+// families build in parallel; step_kernel_for (api side) asks each.
+#if !defined(MBG_STEP_SHAPE)
+#error "compile step.hip with -DMBG_STEP_SHAPE=<0..3>"
+#elif MBG_STEP_SHAPE == 0
+using ThisShape = Shape<256, 1024, 256, 64, 2, F_BF16, 0, 0>;         // tiny dense
+#elif MBG_STEP_SHAPE == 1
+using ThisShape = Shape<2048, 8192, 2048, 128, 2, F_BF16, 0, 0>;      // dense 2B, BF16 KV
+#elif MBG_STEP_SHAPE == 2
+using ThisShape = Shape<2048, 8192, 2048, 128, 2, F_FP8, 0, 0>;       // dense 2B, FP8 KV
+#elif MBG_STEP_SHAPE == 3
+using ThisShape = Shape<2560, 0, 4096, 128, 8, F_BF16, 1, 768>;       // routed
+#else
+#error "unknown MBG_STEP_SHAPE"
+#endif
 
 template <class S>
 static bool matches(const StepVariant& v) {
@@ -1737,20 +1717,12 @@ static const void* pick(int ncol) {
     return nullptr;
 }
 
-bool step_variant_supported(const StepVariant& v) {
-#define X(SH) \
-    if (matches<SH>(v)) return true;
-    MBG_VARIANTS(X)
-#undef X
-    return false;
-}
+#define MBG_CAT2(a, b) a##b
+#define MBG_CAT(a, b) MBG_CAT2(a, b)
 
-const void* step_kernel_for(const StepVariant& v, int ncol, int* lds_bytes_out) {
-    const void* fn = nullptr;
-#define X(SH) \
-    if (!fn && matches<SH>(v)) fn = pick<SH>(ncol);
-    MBG_VARIANTS(X)
-#undef X
+const void* MBG_CAT(step_kernel_shape_, MBG_STEP_SHAPE)(const StepVariant& v, int ncol, int* lds_bytes_out) {
+    if (!matches<ThisShape>(v)) return nullptr;
+    const void* fn = pick<ThisShape>(ncol);
     if (fn && lds_bytes_out) {
         int kmax = v.hidden;
         if (v.ffn > kmax) kmax = v.ffn;

@@ -5,10 +5,72 @@ workspace, and forward step/verify calls.  No decode arithmetic happens here
 work)."""
 from __future__ import annotations
 
+import ctypes
+import threading
+
 import numpy as np
 import torch
 
 from . import _mbg as M
+
+_HIP_DEVICE_MALLOC_UNCACHED = 0x3   # hipDeviceMallocUncached (hip_runtime_api.h)
+
+
+def _hip_runtime() -> ctypes.CDLL:
+    """The HIP runtime this process already uses (the one torch loaded and
+    libmbg.so links against), opened by its path so that no second runtime
+    is loaded."""
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if "libamdhip64.so" in path and path.startswith("/"):
+                return ctypes.CDLL(path)
+    raise RuntimeError("the HIP runtime is not loaded (import torch and use a GPU first)")
+
+
+class UncachedPool:
+    """Dependency-counter blocks in device memory that the L2 does not cache.
+
+    The decode kernel polls its counters with cache-bypassing scalar loads,
+    which see other XCDs' updates only in uncached memory; torch cannot
+    allocate such memory, so it comes from the HIP runtime directly.  A block
+    that a kernel has read is not freed before the process ends: released
+    blocks go back to this pool and later contexts on the same device reuse
+    them."""
+
+    def __init__(self):
+        self._free = {}          # device index -> [(bytes, address)]
+        self._lock = threading.Lock()
+        self._hip = None
+
+    def acquire(self, nbytes: int, device: torch.device) -> tuple[int, int]:
+        dev = device.index if device.index is not None else torch.cuda.current_device()
+        with self._lock:
+            free = self._free.setdefault(dev, [])
+            for i, (n, addr) in enumerate(free):
+                if n >= nbytes:
+                    del free[i]
+                    return addr, n
+            if self._hip is None:
+                self._hip = _hip_runtime()
+                self._hip.hipExtMallocWithFlags.restype = ctypes.c_int
+                self._hip.hipExtMallocWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_size_t,
+                                                            ctypes.c_uint]
+            nbytes = (nbytes + 4095) // 4096 * 4096
+            p = ctypes.c_void_p()
+            with torch.cuda.device(dev):
+                rc = self._hip.hipExtMallocWithFlags(ctypes.byref(p), nbytes, _HIP_DEVICE_MALLOC_UNCACHED)
+            if rc != 0 or not p.value:
+                raise RuntimeError(f"hipExtMallocWithFlags(uncached, {nbytes}) failed with {rc}")
+            return p.value, nbytes
+
+    def release(self, addr: int, nbytes: int, device: torch.device) -> None:
+        dev = device.index if device.index is not None else torch.cuda.current_device()
+        with self._lock:
+            self._free.setdefault(dev, []).append((nbytes, addr))
+
+
+UNCACHED = UncachedPool()
 
 
 def _dev(a: np.ndarray, device) -> torch.Tensor:
@@ -95,6 +157,8 @@ class DeviceModel:
                                   cfg.rms_eps, cfg.page_size, cfg.max_pos, self.k_max)
         self.ws_bytes = M.mbg_workspace_size(self.mcfg)
         self.ws = torch.zeros(self.ws_bytes // 4 + 64, dtype=torch.int32, device=self.device)
+        self.ctr_bytes = M.mbg_counter_bytes(self.mcfg)
+        self.ctr = None           # (address, bytes) of the uncached counter block while a context lives
         self.stream = torch.cuda.current_stream(self.device)
         self.ctx = None
 
@@ -124,8 +188,14 @@ class DeviceModel:
 
     # ------------------------------------------------------------------ decode
     def init(self) -> None:
-        self.ctx = M.mbg_decode_init(self.mcfg, self.weights, self.kv, self.ws, self.ws_bytes,
-                                     self.stream.cuda_stream)
+        self.ctr = UNCACHED.acquire(self.ctr_bytes, self.device)
+        try:
+            self.ctx = M.mbg_decode_init(self.mcfg, self.weights, self.kv, self.ws, self.ws_bytes, self.ctr[0],
+                                         self.ctr[1], self.stream.cuda_stream)
+        except Exception:
+            UNCACHED.release(*self.ctr, self.device)
+            self.ctr = None
+            raise
 
     def info(self):
         return M.mbg_query(self.ctx)
@@ -145,8 +215,11 @@ class DeviceModel:
 
     def close(self) -> None:
         if self.ctx is not None:
-            M.mbg_destroy(self.ctx)
+            M.mbg_destroy(self.ctx)     # waits for the context's stream
             self.ctx = None
+        if self.ctr is not None:
+            UNCACHED.release(*self.ctr, self.device)
+            self.ctr = None
 
     def __del__(self):
         try:

@@ -56,6 +56,8 @@ class DecodeConfig:
     shuffled_pages: bool = False
     weight_sigma: float = 0.02
     k_max: int = 4                # widest verify window
+    norm_gains: str = "ones"      # RMSNorm gains: "ones" (the configured 1.0) or
+                                  # "random" (1 + 0.1 N(0, 1) per element, distinct per norm)
 
     @property
     def max_pos(self) -> int:

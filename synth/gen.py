@@ -13,6 +13,9 @@ Seeds (root seed 0 for weights):
     for a float32 prefill of hundreds of thousands of positions (the
     long-context FP8 cache), N(0, 1) drawn on the GPU by torch's generator,
     seeded per (seed 2, layer, K or V, block of KV_BLOCK positions);
+  * non-unit RMSNorm gains (the "random" gain option): per norm tensor,
+    ``SeedSequence([5, crc32(name)])``, float32 1 + 0.1 N(0, 1), BF16 by
+    truncation, so every norm of every layer gets its own vector;
   * page-table shuffle: seed 3, a uniform permutation of the physical pages;
   * LM-head input vectors: seed 4, float32 N(0, 1);
   * MXFP4 expert codes and scales: a counter-based integer hash (SplitMix64,
@@ -34,6 +37,7 @@ PROMPT_SEED = 1
 KV_SEED = 2
 PAGE_SEED = 3
 XVEC_SEED = 4
+GAIN_SEED = 5
 
 BF16_ONE = np.uint16(0x3F80)
 
@@ -71,6 +75,14 @@ def ones_bf16(shape) -> np.ndarray:
     return np.full(shape, BF16_ONE, dtype=np.uint16)
 
 
+def gain_bf16(name: str, shape, spread: float = 0.1) -> np.ndarray:
+    """BF16 bit patterns of 1 + spread * N(0, 1) draws for norm `name`."""
+    rng = _rng(GAIN_SEED, tensor_id(name))
+    x = rng.standard_normal(int(np.prod(shape)), dtype=np.float32)
+    x = np.float32(1.0) + np.float32(spread) * x
+    return _f32_to_bf16_bits_trunc(x).reshape(shape)
+
+
 # ---------------------------------------------------------------------------
 # Weights
 # ---------------------------------------------------------------------------
@@ -99,7 +111,8 @@ def dense_weights(cfg: DecodeConfig, with_lm_head: bool = True) -> dict:
     """All BF16 tensors of a model, generated in parallel (one stream each).
 
     Keys: ``embed``, ``final_norm``, ``lm_head`` and ``l{i}.{tensor}``.  MoE
-    expert tensors are not included (see ``expert_mxfp4``).
+    expert tensors are not included (see ``expert_mxfp4``).  Norm gains are
+    1.0 unless ``cfg.norm_gains == "random"``.
     """
     jobs = {}
     V, H = cfg.vocab, cfg.hidden
@@ -117,6 +130,8 @@ def dense_weights(cfg: DecodeConfig, with_lm_head: bool = True) -> dict:
     def run(item):
         name, (kind, shp) = item
         if kind == "ones":
+            if cfg.norm_gains == "random":
+                return name, gain_bf16(f"{cfg.name}.{name}", shp)
             return name, ones_bf16(shp)
         return name, normal_bf16(f"{cfg.name}.{name}", shp, sig)
 

@@ -142,3 +142,45 @@ def test_standalone_argument_errors(M):
     with pytest.raises(M.MbgError) as e:
         M.mbg_quantize_fp8_rows(FAKE, 10, 20, FAKE, FAKE, 0)
     assert e.value.code == M.MBG_E_INVALID_ARG
+
+
+def _kv_ok(M):
+    return M.make_kv("bf16", 1, FAKE, FAKE)
+
+
+def test_counter_block_size_and_init_ownership_checks(M):
+    """The caller owns the counter block: init rejects a missing, short or
+    misaligned one before touching the device (host-side checks only)."""
+    cfg = _cfg(M)
+    n = M.mbg_counter_bytes(cfg)
+    L = 2
+    assert n == 128 + L * 6 * 8 * 128     # status line + 8 lines per (layer, phase) counter
+    assert M.mbg_counter_bytes(_cfg(M, n_layers=64)) < 1 << 20
+    ws = M.mbg_workspace_size(cfg)
+    for ctr, nbytes in ((None, n), (FAKE, n - 4), (FAKE + 16, n)):
+        with pytest.raises(M.MbgError) as e:
+            M.mbg_decode_init(cfg, _weights(M), _kv_ok(M), FAKE, ws, ctr, nbytes, 0)
+        assert e.value.code == M.MBG_E_WORKSPACE, M.mbg_last_error()
+        assert "counter block" in M.mbg_last_error()
+    with pytest.raises(M.MbgError) as e:
+        M.mbg_decode_init(cfg, _weights(M), _kv_ok(M), FAKE, ws - 256, FAKE, n, 0)
+    assert e.value.code == M.MBG_E_WORKSPACE and "workspace" in M.mbg_last_error()
+
+
+def test_header_states_ownership_and_passages():
+    """Every declared entry point's comment cites a page passage (or, for the
+    no-allocation variant, names the callers it is for), and the header says
+    that no call allocates device memory."""
+    src = open(os.path.join(ROOT, "include", "mbg.h")).read()
+    assert "No call allocates or frees device" in src
+    assert "never allocates" not in src
+    blocks = re.findall(r"/\*((?:(?!\*/).)*?)\*/\s*(?:const char \*|void|int)\s*\*?\s*(mbg_[a-z0-9_]+)\s*\(",
+                        src, flags=re.S)
+    seen = {name for _, name in blocks}
+    assert set(_declared()) <= seen
+    for text, name in blocks:
+        cites = any(w in text for w in ("article", "report", "cannot allocate"))
+        if name in ("mbg_last_error", "mbg_query", "mbg_read_trace", "mbg_read_routing",
+                    "mbg_lm_head_workspace_size"):
+            continue    # accessors of what another call documented
+        assert cites, f"{name}: no passage cited"

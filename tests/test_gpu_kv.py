@@ -113,10 +113,48 @@ def test_dense2b_fp8_kv_steps():
     _teacher_forced(dm, om, oc, cfg, 3, "dense2b-fp8kv")
 
 
+@pytest.mark.parametrize("k", [2, 4])
+def test_fp8_kv_verify_window(k):
+    """Verify window on the FP8-cache kernel: k tokens in one launch against
+    the oracle (token j sees [0, pos + j], the window's own FP8 K/V included)
+    and against k single steps of a second context."""
+    cfg = CONFIGS["dense2b"].with_(name="dense2b", kv_dtype="fp8", prefill=1000, n_decode=8,
+                                   shuffled_pages=True)
+    say("fp8 kv verify", k)
+    host = gen.dense_weights(cfg)
+    dm, om, oc = build_dense(cfg, host=host)
+    p0 = cfg.prefill
+    toks = [int(t) for t in gen.prompt_tokens(cfg, k)]
+    win = torch.tensor(toks, dtype=torch.int32, device="cuda")
+    logits = torch.empty((k, cfg.vocab), dtype=torch.float32, device="cuda")
+    am = torch.zeros(k, dtype=torch.int32, device="cuda")
+    dm.verify(win, p0, logits, am)
+    torch.cuda.synchronize()
+    g = logits.cpu().numpy()
+    amh = am.cpu().numpy()
+    ref = om.verify(oc, toks, p0)
+    for j in range(k):
+        compare_logits(g[j], ref[j], what=f"fp8 verify col {j}")
+        check_argmax(int(amh[j]), g[j], ref[j], what=f"fp8 verify col {j}")
+    assert dm.status() == 0
+    dm2, _, _ = build_dense(cfg, host=host, kv_scales=oc.scales)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    l1 = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    a1 = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for j in range(k):
+        tok.fill_(toks[j])
+        dm2.step(tok, p0 + j, l1, a1)
+        d = float(np.max(np.abs(l1.cpu().numpy() - g[j])))
+        assert d < 2e-3, f"verify col {j} vs step: max abs {d}"
+    assert dm2.status() == 0
+
+
 @pytest.mark.timeout(1500)
 def test_longctx_fp8_kv_200k():
     """The long-context workload: FP8 cache prefilled to 200,000 positions in
-    64-token pages under a shuffled page table; one decode step at 200,000."""
+    64-token pages under a shuffled page table; two greedy decode steps at
+    200,000 and 200,001 (the second reads the FP8 K/V the kernel wrote in
+    the first)."""
     cfg = CONFIGS["longctx"]
     assert cfg.prefill == 200000 and cfg.kv_dtype == "fp8" and cfg.shuffled_pages
     say("longctx build (prefill 200000, fp8)")
@@ -124,4 +162,19 @@ def test_longctx_fp8_kv_200k():
     pt = dm.page_table_host
     assert not np.array_equal(pt, np.arange(pt.size))
     say("longctx info", dm.info().grid, dm.info().attn_splits, dm.info().variant)
-    _teacher_forced(dm, om, oc, cfg, 1, "longctx")
+    _teacher_forced(dm, om, oc, cfg, 2, "longctx")
+    # the cache entries the kernel wrote at 200,000 and 200,001 equal the
+    # oracle's codes, up to one FP8 step where the binary32 values straddle
+    # a rounding boundary
+    for li in (0, cfg.n_layers - 1):
+        P = cfg.page_size
+        for pos in (cfg.prefill, cfg.prefill + 1):
+            page = int(dm.page_table_host[pos // P])
+            for which, ref in ((0, oc.k[li][pos]), (1, oc.v[li][pos])):
+                got = dm.pool[li, page, which, :, pos % P, :].cpu().numpy()
+                a = codecs.fp8e4m3_to_f64(got)
+                b = codecs.fp8e4m3_to_f64(ref)
+                frac = float(np.mean(got == ref))
+                say(f"longctx cache layer {li} pos {pos} kv {which}: bit-equal {frac:.4f}")
+                assert frac > 0.95
+                assert np.all(np.abs(a - b) <= 2.0 ** -3 * np.maximum(np.abs(a), np.abs(b)) + 2.0 ** -9)

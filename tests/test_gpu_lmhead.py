@@ -125,27 +125,41 @@ def test_lm_head_full_size_bf16(k):
         check_argmax(int(idx[j]), got[j], ref[j], what=f"col {j}")
 
 
-@pytest.mark.parametrize("k", [1, 4])
-def test_lm_head_full_size_fp8_sampled(k):
-    """Full 157,184 x 2,560 FP8 head; the oracle quantises and evaluates a
-    sample of rows (plus the GPU's argmax rows) one by one."""
+@pytest.mark.timeout(900)
+def test_lm_head_full_size_fp8():
+    """The full 157,184 x 2,560 head quantised to FP8 by the library: every
+    row's codes and scale equal the oracle's quantiser, and for k = 1 and 4
+    every logit matches the oracle's dequantise-then-dot, with the argmax
+    graded against the oracle's wherever its top-2 margin exceeds 1e-2."""
     cfg = CONFIGS["lmhead"]
-    say("lm_head full fp8", k)
+    say("lm_head full fp8")
     w = gen.lm_head_bf16(cfg)
-    x = gen.lm_head_inputs(cfg, k)
     M = _M()
     wd = _dev_bits(w)
-    codes = torch.empty((cfg.vocab, cfg.hidden), dtype=torch.uint8, device="cuda")
-    scales = torch.empty((cfg.vocab,), dtype=torch.float32, device="cuda")
-    M.mbg_quantize_fp8_rows(wd, cfg.vocab, cfg.hidden, codes, scales, torch.cuda.current_stream().cuda_stream)
-    got, idx = _run_lm(M.make_tensor(codes, "fp8", cfg.vocab, cfg.hidden, scale=scales), x, cfg.vocab)
-    rows = np.random.default_rng(9).choice(cfg.vocab, 3000, replace=False)
-    rows = np.unique(np.concatenate([rows, idx.astype(np.int64), [0, cfg.vocab - 1]]))
-    rc, rs = quantize_fp8_rows(w[rows])
-    assert np.array_equal(codes[torch.from_numpy(rows).cuda()].cpu().numpy(), rc)
-    assert np.array_equal(scales[torch.from_numpy(rows).cuda()].cpu().numpy(), rs)
-    deq = codecs.fp8e4m3_to_f64(rc) * rs.astype(np.float64)[:, None]
-    ref = x.astype(np.float64) @ deq.T                    # [k][rows]
-    for j in range(k):
-        compare_logits(got[j][rows], ref[j], what=f"col {j} sampled rows")
-        assert int(idx[j]) == int(np.flatnonzero(got[j] == got[j].max())[0])
+    V, H = cfg.vocab, cfg.hidden
+    codes = torch.empty((V, H), dtype=torch.uint8, device="cuda")
+    scales = torch.empty((V,), dtype=torch.float32, device="cuda")
+    M.mbg_quantize_fp8_rows(wd, V, H, codes, scales, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    del wd
+    xs = {k: gen.lm_head_inputs(cfg, k) for k in (1, 4)}
+    got = {k: _run_lm(M.make_tensor(codes, "fp8", V, H, scale=scales), xs[k], V) for k in (1, 4)}
+    gc = codes.cpu().numpy()
+    gs = scales.cpu().numpy()
+    ref = {k: np.empty((k, V)) for k in (1, 4)}
+    chunk = 16384
+    for r0 in range(0, V, chunk):
+        rc, rs = quantize_fp8_rows(w[r0:r0 + chunk])
+        assert np.array_equal(gc[r0:r0 + chunk], rc), f"codes of rows {r0}.."
+        assert np.array_equal(gs[r0:r0 + chunk], rs), f"scales of rows {r0}.."
+        deq = codecs.fp8e4m3_to_f64(rc) * rs.astype(np.float64)[:, None]
+        for k in (1, 4):
+            ref[k][:, r0:r0 + chunk] = xs[k].astype(np.float64) @ deq.T
+        say(f"rows {r0}..{min(V, r0 + chunk)} checked")
+    graded = 0
+    for k in (1, 4):
+        g, idx = got[k]
+        for j in range(k):
+            compare_logits(g[j], ref[k][j], what=f"k {k} col {j}")
+            graded += check_argmax(int(idx[j]), g[j], ref[k][j], what=f"k {k} col {j}")
+    say("fp8 head argmax graded", graded, "of 5")

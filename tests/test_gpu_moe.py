@@ -172,16 +172,16 @@ def test_moe_small_steps_and_verify():
 
 @pytest.mark.timeout(1500)
 def test_moe_full_step_and_verify():
-    """The routed workload at full size: 4 steps at 2048..2051, then the
-    4-token verify window at 2048 over the same tokens."""
+    """The routed workload at full size: all 8 decode steps at 2048..2055,
+    then the 4-token verify window at 2048 over the first four tokens."""
     cfg = CONFIGS["moe"]
     assert cfg.n_layers == 42 and cfg.n_experts == 512 and cfg.vocab == 157184 and cfg.prefill == 2048
     say("moe full build")
     dm, om, oc = build_moe(cfg, cache_experts=False)
     info = dm.info()
     say("moe full info", info.grid, info.attn_splits, info.variant, info.weight_bytes_per_step)
-    toks = gen.prompt_tokens(cfg, 4)
+    toks = gen.prompt_tokens(cfg, cfg.n_decode)
     steps, routed = _steps(dm, om, oc, cfg, cfg.prefill, toks, "moe")
-    say("moe graded routing decisions", routed)
-    assert routed >= 42
-    _verify(dm, cfg, cfg.prefill, toks, steps, "moe")
+    say("moe graded routing decisions", routed, "of", cfg.n_decode * cfg.n_layers)
+    assert routed >= 8 * 42 // 2
+    _verify(dm, cfg, cfg.prefill, toks[:4], steps[:4], "moe")

@@ -65,10 +65,10 @@ def matvec(W, x):
     return out
 
 
-def rms(x, eps):
+def rms(x, eps, g):
     ms = sum(v * v for v in x) / len(x)
     r = 1.0 / math.sqrt(ms + eps)
-    return [v * r for v in x]
+    return [v * r * gi for v, gi in zip(x, g)]
 
 
 def rot(vec, pos, theta):
@@ -146,7 +146,7 @@ class Naive:
         d, Hq, Hkv = cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads
         x = list(self.W["embed"][token])
         for li in range(self.L):
-            xn = rms(x, cfg.rms_eps)          # gains are 1.0 in every workload
+            xn = rms(x, cfg.rms_eps, self.W[f"l{li}.attn_norm"])
             q = matvec(self.W[f"l{li}.wq"], xn)
             k = matvec(self.W[f"l{li}.wk"], xn)
             v = matvec(self.W[f"l{li}.wv"], xn)
@@ -175,10 +175,10 @@ class Naive:
                 att.extend(o)
             y = matvec(self.W[f"l{li}.wo"], att)
             x = [a + b for a, b in zip(x, y)]
-            xn = rms(x, cfg.rms_eps)
+            xn = rms(x, cfg.rms_eps, self.W[f"l{li}.ffn_norm"])
             f = self.ffn(li, xn)
             x = [a + b for a, b in zip(x, f)]
-        xn = rms(x, cfg.rms_eps)
+        xn = rms(x, cfg.rms_eps, self.W["final_norm"])
         return matvec(self.W["lm_head"], xn)
 
 
@@ -200,9 +200,17 @@ TINY_MOE = DecodeConfig(name="naive_moe", n_layers=2, hidden=32, n_q_heads=4, n_
                         moe_ffn=32, prefill=3, n_decode=3, weight_sigma=0.3, lm_dtype="fp8")
 
 
-def _run(cfg, kv_dtype="bf16", lm_fp8=False):
-    cfg = cfg.with_(kv_dtype=kv_dtype)
+def _run(cfg, kv_dtype="bf16", lm_fp8=False, gains="ones"):
+    cfg = cfg.with_(kv_dtype=kv_dtype, norm_gains=gains)
     T = gen.dense_weights(cfg)
+    if gains == "random":
+        # three distinct non-unit gain vectors per layer plus the final one
+        norms = [T[f"l{li}.{n}"] for li in range(cfg.n_layers) for n in ("attn_norm", "ffn_norm")]
+        norms.append(T["final_norm"])
+        for i, a in enumerate(norms):
+            assert np.all(a != 0x3F80) or np.mean(a == 0x3F80) < 0.2
+            for b in norms[i + 1:]:
+                assert not np.array_equal(a, b)
     experts = (lambda l, e, w: gen.expert_mxfp4(cfg, l, e, w)) if cfg.is_moe else None
     lm = quantize_fp8_rows(T["lm_head"]) if lm_fp8 else None
     model = OracleModel(cfg, T, experts=experts, lm_fp8=lm)
@@ -237,6 +245,42 @@ def test_naive_dense_fp8_lm_head():
 
 def test_naive_moe():
     _run(TINY_MOE, lm_fp8=True)
+
+
+def test_naive_dense_random_gains():
+    _run(TINY_DENSE, gains="random")
+
+
+def test_naive_dense_random_gains_fp8_kv():
+    _run(TINY_DENSE, kv_dtype="fp8", gains="random")
+
+
+def test_naive_moe_random_gains():
+    _run(TINY_MOE, lm_fp8=True, gains="random")
+
+
+def _first_step(cfg, T):
+    m = OracleModel(cfg, T)
+    c = OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim)
+    return m.step(c, 3, 0)
+
+
+@pytest.mark.parametrize("swap", ["attn_ffn", "final_dropped"])
+def test_gain_placement_matters(swap):
+    """A planted mistake in the oracle's gain placement (attention and FFN
+    norms exchanged, or the final gain dropped) moves the logits far beyond
+    the parity tolerance, so the gain tests above can see it."""
+    cfg = TINY_DENSE.with_(norm_gains="random")
+    T = gen.dense_weights(cfg)
+    ref = _first_step(cfg, T)
+    U = dict(T)
+    if swap == "attn_ffn":
+        for li in range(cfg.n_layers):
+            U[f"l{li}.attn_norm"], U[f"l{li}.ffn_norm"] = T[f"l{li}.ffn_norm"], T[f"l{li}.attn_norm"]
+    else:
+        U["final_norm"] = gen.ones_bf16(T["final_norm"].shape)
+    bad = _first_step(cfg, U)
+    assert np.max(np.abs(bad - ref)) > 5e-2 * np.max(np.abs(ref))
 
 
 def test_float32_mode_agrees_with_float64():
