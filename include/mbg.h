@@ -310,6 +310,20 @@ int mbg_lm_head_workspace_size(int32_t k, size_t *bytes);
 int mbg_lm_head(const mbg_tensor *w, const float *d_x, int32_t k, float *d_logits,
                 int32_t *d_argmax, void *d_workspace, size_t workspace_bytes, void *stream);
 
+/* mbg_lm_head for callers that cannot allocate device memory (code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc): the
+ * same kernel and arguments without the workspace.  Its argmax keys and
+ * arrival counter live in a fixed 256-byte device array of the library (one
+ * copy per GPU, held until the process ends), set up and zeroed on the
+ * first call on each device; every call leaves it zeroed again.  All calls
+ * on one GPU share that array, so calls that overlap on one GPU (different
+ * streams, or threads) race and must be serialised by the caller.
+ * Allocates nothing.  Errors: as mbg_lm_head; k outside [1, 4] (more argmax
+ * keys than the array holds) is MBG_E_RANGE; MBG_E_HIP if the array's device
+ * address cannot be obtained. */
+int mbg_lm_head_noalloc(const mbg_tensor *w, const float *d_x, int32_t k, float *d_logits,
+                        int32_t *d_argmax, void *stream);
+
 /* Online FP8 quantisation of a BF16 matrix with one scale per row (163.com
  * Ling-3.0-flash article, "optimisation 2: online FP8 LM head
  * quantisation"): scale[r] = max_i |W[r][i]| / 448 in binary32 (1.0 for an

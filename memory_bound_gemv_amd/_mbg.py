@@ -102,6 +102,8 @@ def _load():
         "mbg_lm_head_workspace_size": (C.c_int, [C.c_int32, C.POINTER(C.c_size_t)]),
         "mbg_lm_head": (C.c_int, [C.POINTER(mbg_tensor), C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
                                   C.c_void_p, C.c_size_t, C.c_void_p]),
+        "mbg_lm_head_noalloc": (C.c_int, [C.POINTER(mbg_tensor), C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p,
+                                          C.c_void_p]),
         "mbg_quantize_fp8_rows": (C.c_int, [C.c_void_p, C.c_int64, C.c_int64, C.c_void_p, C.c_void_p,
                                             C.c_void_p]),
         "mbg_kv_write": (C.c_int, [C.POINTER(mbg_config), C.POINTER(mbg_kv), C.c_int32, C.c_int32, C.c_int32,
@@ -118,7 +120,8 @@ _lib = _load()
 EXPORTED = ("mbg_workspace_size", "mbg_counter_bytes", "mbg_validate", "mbg_decode_init", "mbg_decode_step", "mbg_decode_verify",
             "mbg_get_status", "mbg_query", "mbg_set_timeout_us", "mbg_set_trace", "mbg_read_trace",
             "mbg_read_routing", "mbg_last_error", "mbg_destroy",
-            "mbg_lm_head_workspace_size", "mbg_lm_head", "mbg_quantize_fp8_rows", "mbg_kv_write")
+            "mbg_lm_head_workspace_size", "mbg_lm_head", "mbg_lm_head_noalloc", "mbg_quantize_fp8_rows",
+            "mbg_kv_write")
 
 
 def _check(rc: int) -> int:
@@ -265,6 +268,10 @@ def mbg_lm_head_workspace_size(k: int) -> int:
 def mbg_lm_head(w: mbg_tensor, x, k: int, logits, argmax, workspace, ws_bytes: int, stream: int) -> None:
     _check(_lib.mbg_lm_head(C.byref(w), _ptr(x), k, _ptr(logits), _ptr(argmax), _ptr(workspace), ws_bytes,
                             stream))
+
+
+def mbg_lm_head_noalloc(w: mbg_tensor, x, k: int, logits, argmax, stream: int) -> None:
+    _check(_lib.mbg_lm_head_noalloc(C.byref(w), _ptr(x), k, _ptr(logits), _ptr(argmax), stream))
 
 
 def mbg_quantize_fp8_rows(w, rows: int, cols: int, codes, scales, stream: int) -> None:

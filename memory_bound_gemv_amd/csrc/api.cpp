@@ -781,6 +781,17 @@ int mbg_lm_head(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logit
     return lm_head_launch(w, d_x, k, d_logits, d_argmax, d_ws, stream);
 }
 
+int mbg_lm_head_noalloc(const mbg_tensor* w, const float* d_x, int32_t k, float* d_logits, int32_t* d_argmax,
+                        void* stream) {
+    int rc = lm_head_check(w, d_x, k, d_argmax);
+    if (rc) return rc;
+    if ((size_t)k * 8 > 64) return fail(MBG_E_RANGE, "k %d: the fixed scratch holds at most 8 argmax keys", k);
+    void* p = nullptr;
+    hipError_t e = lm_head_scratch((hipStream_t)stream, &p);
+    if (e != hipSuccess) return hip_fail(e, "lm_head scratch set-up");
+    return lm_head_launch(w, d_x, k, d_logits, d_argmax, p, stream);
+}
+
 int mbg_quantize_fp8_rows(const uint16_t* d_w, int64_t rows, int64_t cols, uint8_t* d_codes, float* d_scales,
                           void* stream) {
     if (!d_w || !d_codes || !d_scales) return fail(MBG_E_INVALID_ARG, "NULL pointer");

@@ -31,6 +31,10 @@ struct KvWriteArgs {
 };
 
 hipError_t launch_lm_head(const LmHeadArgs& a, int ncol, int fmt, int grid, hipStream_t s);
+// Device address of this device's fixed LM-head scratch array (argmax keys at
+// offset 0, arrival counter at offset 64), set up and zeroed on first use.
+constexpr size_t kLmScratchBytes = 256;
+hipError_t lm_head_scratch(hipStream_t s, void** out);
 bool lm_head_hidden_supported(int H);
 hipError_t launch_quantize_fp8_rows(const uint16_t* w, int64_t rows, int64_t cols, uint8_t* codes, float* scales,
                                     hipStream_t s);

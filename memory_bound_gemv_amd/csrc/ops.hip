@@ -2,6 +2,8 @@
 // quantisation, and the quantising K/V write into the paged cache.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "gemv.h"
 #include "ops.h"
 
@@ -154,6 +156,44 @@ hipError_t launch_lm_head(const LmHeadArgs& a, int ncol, int fmt, int grid, hipS
         }
     }
     return hipErrorInvalidValue;
+}
+
+// ------------------------------------------- LM head without allocation
+//
+// The argmax keys (k <= 4 of 8 bytes at offset 0) and the arrival counter
+// (offset 64) of the LM head live in this fixed device array instead of a
+// caller workspace, for callers that cannot allocate device memory.  Each
+// GPU holds its own copy until the process ends.  In host code `scratch`
+// names a host-side stand-in, never the device memory: its device address
+// comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) uint8_t scratch[kLmScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+hipError_t lm_head_scratch(hipStream_t s, void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        // keys and counter start at zero; every call leaves them at zero
+        e = launch_fill_u32(static_cast<uint32_t*>(p), kLmScratchBytes / 4, 0u, s);
+        if (e != hipSuccess) return e;
+        e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // ------------------------------------------------- FP8 row quantisation
