@@ -165,7 +165,8 @@ int mbg_workspace_size(const mbg_config *cfg, size_t *bytes);
 
 /* Bytes of the dependency-counter block a context for `cfg` needs (one
  * 128-byte line for the status, LM-head counter and flag words, then
- * 8 x 128 bytes per (layer, phase) counter; under 1 MiB for 64 layers).
+ * 8 x 128 bytes per (layer, phase) counter and one more for the step
+ * token of multi-step launches; under 1 MiB for 64 layers).
  * The counters replace kernel boundaries with flag polling inside one
  * launch ("Muse Spark Open: 1,109 tokens/s" article, section on the three
  * bills of a kernel this large: synchronisation).  Host-only. */
@@ -231,6 +232,22 @@ int mbg_decode_step(mbg_ctx *ctx, const int32_t *d_token, int32_t pos,
 int mbg_decode_verify(mbg_ctx *ctx, const int32_t *d_tokens, int32_t k, int32_t pos,
                       float *d_logits, int32_t *d_argmax);
 
+/* n_steps greedy decode steps (1 .. 4096) in ONE kernel launch: step s runs
+ * at pos + s; step 0 reads its token at d_token[0], step s > 0 takes the
+ * argmax of step s - 1 on the device, and the persistent kernel moves from
+ * one step to the next without returning (the Kog article "Real-time LLM
+ * inference on standard GPUs: 3k tokens/s per request", section on
+ * co-designing engine, GPU code and model: the monokernel keeps the whole
+ * generation on the GPU; the "Muse Spark Open" article's step still
+ * launches one kernel per layer).  Writes K/V at pos .. pos + n_steps - 1,
+ * logits (device float [n_steps][vocab], may be NULL) and the tokens
+ * (device int32 d_argmax[n_steps]).  Same arithmetic as n_steps calls of
+ * mbg_decode_step with d_token aliasing the previous argmax: results are
+ * bitwise equal.  Errors: MBG_E_RANGE if n_steps is outside [1, 4096] or
+ * pos + n_steps exceeds max_pos; otherwise as mbg_decode_step. */
+int mbg_decode_steps(mbg_ctx *ctx, const int32_t *d_token, int32_t n_steps, int32_t pos,
+                     float *d_logits, int32_t *d_argmax);
+
 /* Wait for the init stream, then return the device status of the calls
  * since the last mbg_get_status: 0, MBG_E_TIMEOUT (a dependency wait
  * exceeded its deadline and the launch drained), MBG_E_UNSUPPORTED (the
@@ -264,7 +281,8 @@ int mbg_set_timeout_us(mbg_ctx *ctx, int64_t us);
  * device clock at task start, when its dependency wait was satisfied, when
  * its input vector was loaded, when its weight/KV stream finished, and at
  * task end; then (op | layer << 8 | tile << 32) and two op-specific stamps
- * (attention: history folded, split-KV combine weights ready; else 0).  An external profiler
+ * (attention: history folded, split-KV combine weights ready; expert
+ * gate/up: router logits loaded, top-k picked; else 0).  An external profiler
  * sees one long kernel per step, so the kernel times itself (the "Muse Spark
  * Open: 1,109 tokens/s" article describes the same in-kernel stamps, section
  * on where the step time goes).  Stamps do not change any result. */

@@ -91,6 +91,7 @@ def _load():
                                       C.POINTER(CTX_P)]),
         "mbg_decode_step": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
         "mbg_decode_verify": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+        "mbg_decode_steps": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
         "mbg_get_status": (C.c_int, [CTX_P]),
         "mbg_query": (C.c_int, [CTX_P, C.POINTER(mbg_info)]),
         "mbg_set_timeout_us": (C.c_int, [CTX_P, C.c_int64]),
@@ -117,7 +118,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTED = ("mbg_workspace_size", "mbg_counter_bytes", "mbg_validate", "mbg_decode_init", "mbg_decode_step", "mbg_decode_verify",
+EXPORTED = ("mbg_workspace_size", "mbg_counter_bytes", "mbg_validate", "mbg_decode_init", "mbg_decode_step",
+            "mbg_decode_verify", "mbg_decode_steps",
             "mbg_get_status", "mbg_query", "mbg_set_timeout_us", "mbg_set_trace", "mbg_read_trace",
             "mbg_read_routing", "mbg_last_error", "mbg_destroy",
             "mbg_lm_head_workspace_size", "mbg_lm_head", "mbg_lm_head_noalloc", "mbg_quantize_fp8_rows",
@@ -215,6 +217,10 @@ def mbg_decode_step(ctx, token, pos: int, logits, argmax) -> None:
 
 def mbg_decode_verify(ctx, tokens, k: int, pos: int, logits, argmax) -> None:
     _check(_lib.mbg_decode_verify(ctx, _ptr(tokens), k, pos, _ptr(logits), _ptr(argmax)))
+
+
+def mbg_decode_steps(ctx, token, n_steps: int, pos: int, logits, argmax) -> None:
+    _check(_lib.mbg_decode_steps(ctx, _ptr(token), n_steps, pos, _ptr(logits), _ptr(argmax)))
 
 
 def mbg_get_status(ctx) -> int:

@@ -43,6 +43,7 @@ int hip_fail(hipError_t e, const char* what) {
     } while (0)
 
 constexpr int kMaxGrid = 1024;   // workgroups of the persistent kernel (upper bound)
+constexpr int kMaxStepsPerLaunch = 4096;   // greedy steps one mbg_decode_steps launch may run
 constexpr int kMaxSplits = 64;   // split-KV partitions per KV head (upper bound)
 constexpr int kBlock = 256;
 constexpr int kAttnBufsHost = 4;   // attention ring chunks per wave (step.hip)
@@ -74,7 +75,7 @@ Plan make_plan(const mbg_config& c) {
         return o;
     };
     p.keys = take(8 * 4);
-    p.n_ctr = L * PH_COUNT;
+    p.n_ctr = L * PH_COUNT + 1;   // the per-(layer, phase) counters and the step-token counter
     p.uc_bytes = kUcCtrOffset + 4 * kLineU32 * kCtrLines * p.n_ctr;
     p.head_ctr = take(4 * kLineU32 * L * (size_t)c.n_q_heads);   // one line per (layer, KV head, head group)
     p.zero_bytes = off;  // everything above starts at zero
@@ -598,19 +599,25 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
 }
 
 static int launch_step(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t pos, float* d_logits,
-                       int32_t* d_argmax) {
+                       int32_t* d_argmax, int32_t nsteps = 1) {
     if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
     if (!d_tokens || !d_argmax) return fail(MBG_E_INVALID_ARG, "tokens/argmax is NULL");
     if (k < 1 || k > x->cfg.k_max) return fail(MBG_E_RANGE, "k %d outside [1, %d]", k, x->cfg.k_max);
-    if (pos < 0 || (int64_t)pos + k > x->cfg.max_pos)
-        return fail(MBG_E_RANGE, "positions %d..%d outside [0, %d)", pos, pos + k - 1, x->cfg.max_pos);
+    if (nsteps < 1 || nsteps > kMaxStepsPerLaunch)
+        return fail(MBG_E_RANGE, "n_steps %d outside [1, %d]", nsteps, kMaxStepsPerLaunch);
+    const int64_t span = (int64_t)k + nsteps - 1;
+    if (pos < 0 || (int64_t)pos + span > x->cfg.max_pos)
+        return fail(MBG_E_RANGE, "positions %d..%lld outside [0, %d)", pos, (long long)(pos + span - 1),
+                    x->cfg.max_pos);
     StepArgs a = x->base;
     a.tokens = d_tokens;
     a.logits = d_logits;
     a.argmax = d_argmax;
     a.pos = pos;
     a.ncol = k;
-    a.epoch = ++x->epoch;
+    a.nsteps = nsteps;
+    a.epoch = x->epoch + 1;
+    x->epoch += (uint32_t)nsteps;
     a.deadline_ticks = (uint64_t)x->timeout_us * (uint64_t)x->wall_khz / 1000ull;
     a.clock_mask = x->timeout_us < 1000 ? 0u : 31u;
     void* args[] = {&a};
@@ -628,6 +635,11 @@ int mbg_decode_step(mbg_ctx* x, const int32_t* d_token, int32_t pos, float* d_lo
 int mbg_decode_verify(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t pos, float* d_logits,
                       int32_t* d_argmax) {
     return launch_step(x, d_tokens, k, pos, d_logits, d_argmax);
+}
+
+int mbg_decode_steps(mbg_ctx* x, const int32_t* d_token, int32_t n_steps, int32_t pos, float* d_logits,
+                     int32_t* d_argmax) {
+    return launch_step(x, d_token, 1, pos, d_logits, d_argmax, n_steps);
 }
 
 int mbg_get_status(mbg_ctx* x) {

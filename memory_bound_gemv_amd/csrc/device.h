@@ -161,6 +161,62 @@ __device__ __forceinline__ float wave_max(float v) {
     return fmaxf(a, b);
 }
 
+// Whole-wavefront maximum of 64-bit unsigned keys, identical in every lane:
+// the same DPP and permlane pattern as wave_max on both 32-bit halves (VALU
+// lane moves, no LDS round trip per step).
+template <int CTRL>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ unsigned long long max_u64(unsigned long long a, unsigned long long b) {
+    return a > b ? a : b;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+    v = max_u64(v, dpp_u64<0xB1>(v));   // quad_perm [1,0,3,2]
+    v = max_u64(v, dpp_u64<0x4E>(v));   // quad_perm [2,3,0,1]
+    v = max_u64(v, dpp_u64<0x141>(v));  // row_half_mirror
+    v = max_u64(v, dpp_u64<0x140>(v));  // row_mirror
+    {
+        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = max_u64(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
+    }
+    {
+        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
+        v = max_u64(((unsigned long long)hi[0] << 32) | lo[0], ((unsigned long long)hi[1] << 32) | lo[1]);
+    }
+    return v;
+}
+
+// Whole-wavefront maximum of 32-bit unsigned values, identical in every lane.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, dpp_u32<0xB1>(v));    // quad_perm [1,0,3,2]
+    v = max(v, dpp_u32<0x4E>(v));    // quad_perm [2,3,0,1]
+    v = max(v, dpp_u32<0x141>(v));   // row_half_mirror
+    v = max(v, dpp_u32<0x140>(v));   // row_mirror
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    v = max(r[0], r[1]);
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return max(r[0], r[1]);
+}
+
+// Inclusive prefix sum within each 16-lane row (Hillis-Steele over row
+// shifts; lanes shifted in from outside the row contribute 0).
+__device__ __forceinline__ uint32_t row_prefix_sum(uint32_t v) {
+    v += dpp_u32<0x111>(v);   // row_shr:1
+    v += dpp_u32<0x112>(v);   // row_shr:2
+    v += dpp_u32<0x114>(v);   // row_shr:4
+    v += dpp_u32<0x118>(v);   // row_shr:8
+    return v;
+}
+
 // The value of lane (this lane ^ MSK): 8 within a row is a half-row
 // rotation (DPP), 16 and 32 are the permlane swaps above.
 template <int MSK>

@@ -119,7 +119,8 @@ struct StepArgs {
     // workspace
     const Task* tasks;
     const uint32_t* task_off;  // [grid + 1]
-    uint32_t* ctr;             // [n_layers * PH_COUNT][kCtrLines lines], uncached memory
+    uint32_t* ctr;             // [n_layers * PH_COUNT + 1][kCtrLines lines], uncached memory; the
+                               // last counts steps whose argmax (next token) is written
     uint32_t* head_ctr;        // [n_layers * n_kv_heads] split arrivals
     uint32_t* lm_ctr;          // LM-head tiles finished
     uint32_t* status;          // first device error that ends the launch (uncached memory)
@@ -143,9 +144,10 @@ struct StepArgs {
     const int32_t* tokens;
     float* logits;
     int32_t* argmax;
-    int32_t pos;
+    int32_t pos;               // position of the launch's first step (column 0)
     int32_t ncol;
-    uint32_t epoch;
+    uint32_t epoch;            // epoch of the launch's first step; step s runs with epoch + s
+    int32_t nsteps;            // greedy steps in this launch (token of step s > 0 = argmax of step s - 1)
     int32_t attn_local;        // 1: the splits of an attention group run on one XCD (workgroup b on XCD b % 8)
                                //    and exchange partials and arrivals through that XCD's L2
     uint64_t deadline_ticks;   // s_memrealtime ticks a wait may take

@@ -57,6 +57,15 @@ __device__ __forceinline__ uint32_t ctr_index(uint32_t layer, uint32_t ph) { ret
 
 __shared__ uint64_t s_twait;  // trace: when the current task's wait was satisfied
 
+// The step a workgroup is running within a launch of several greedy steps:
+// its epoch (the launch epoch plus the step index) and position.
+__shared__ uint32_t s_ep;
+__shared__ int32_t s_pos, s_step;
+__device__ __forceinline__ uint32_t cur_epoch() { return __builtin_amdgcn_readfirstlane(s_ep); }
+__device__ __forceinline__ int cur_pos() { return __builtin_amdgcn_readfirstlane(s_pos); }
+__device__ __forceinline__ int cur_step() { return __builtin_amdgcn_readfirstlane(s_step); }
+__device__ __forceinline__ uint32_t token_ctr_index(CArgs* a) { return (uint32_t)a->n_layers * PH_COUNT; }
+
 // Cross-workgroup data (residual stream, q, new K/V, attention partials and
 // output, FFN hidden) is written and read with device-coherent accesses
 // (agent-scope relaxed atomics: loads and stores with the device-scope cache
@@ -143,13 +152,12 @@ __device__ __forceinline__ void sload_counter(const uint32_t* lines, const uint3
 // Wait until counter `idx` (the sum of its kCtrLines lines) reaches
 // epoch * need (mod 2^32).  Wave 0 polls; the other waves wait at the
 // barrier.  Returns false when the launch is aborting.
-__device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
+__device__ __forceinline__ bool wait_until(CArgs* a, uint32_t idx, uint32_t target) {
     __shared__ int s_ok;
     if (threadIdx.x < kWave) {
         const int lane = threadIdx.x;
         int ok = 1;
         if (idx != kNoWait) {
-            const uint32_t target = a->epoch * need;
             const uint32_t* lines = a->ctr + (size_t)idx * kCtrLines * kLineU32;
             const uint64_t t0 = wall_clock64();
             uint32_t rounds = 0;
@@ -177,6 +185,10 @@ __device__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
     return s_ok != 0;
 }
 
+__device__ __forceinline__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
+    return wait_until(a, idx, cur_epoch() * need);
+}
+
 // Make this workgroup's stores visible at device scope, then count the task
 // on this workgroup's line of the counter.
 __device__ __forceinline__ void release_counter(CArgs* a, uint32_t idx) {
@@ -191,7 +203,12 @@ __device__ __forceinline__ void release_counter(CArgs* a, uint32_t idx) {
 // Token id of column c, clamped into [0, vocab); a clamp raises the range
 // flag (reported by mbg_get_status) and the step completes normally.
 __device__ __forceinline__ int token_of(CArgs* a, int c) {
-    int t = gp(a->tokens)[c];
+    // the first step reads the caller's token; a later step of the same
+    // launch reads the previous step's argmax (written this launch)
+    const int st = cur_step();
+    int t = st == 0 ? gp(a->tokens)[c]
+                    : (int)__hip_atomic_load(gp(a->argmax) + (size_t)(st - 1) * a->ncol + c, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
     if (t < 0 || t >= a->vocab) {
         if (threadIdx.x == 0) latch_error(a->flags, kStatusRange);
         t = t < 0 ? 0 : a->vocab - 1;
@@ -204,7 +221,7 @@ __device__ __forceinline__ int token_of(CArgs* a, int c) {
 // squares in a fixed order (per thread over its quads, then the wave tree,
 // then the four waves in order).
 template <int NC, int H, class Src4>
-__device__ void load_normed(CArgs* a, Src4 src4, const uint16_t* gain, lds_f32* xs) {
+__device__ __forceinline__ void load_normed(CArgs* a, Src4 src4, const uint16_t* gain, lds_f32* xs) {
     __shared__ float red[kWaves * 4];
     static_assert(H % 4 == 0, "hidden size");
     constexpr int NV = H / 4;
@@ -258,7 +275,7 @@ __device__ void load_normed(CArgs* a, Src4 src4, const uint16_t* gain, lds_f32* 
 // xs[0 .. NC*K) = src[...] (float32, written this step): all 16-byte
 // coherent loads issued before any LDS write.
 template <int NC, int K>
-__device__ void load_plain(const float* src, lds_f32* xs) {
+__device__ __forceinline__ void load_plain(const float* src, lds_f32* xs) {
     static_assert(K % 4 == 0, "row length");
     constexpr int NV = NC * K / 4;
     constexpr int PER = (NV + kThreads - 1) / kThreads;
@@ -300,7 +317,7 @@ __device__ __forceinline__ void dma_input(CArgs* a, const float* src, int n, lds
 // xs[c][i] (already in LDS) *= 1 / sqrt(mean_i xs[c][i]^2 + eps) * gain[i]:
 // the same per-thread quads and reduction order as load_normed.
 template <int NC, int H>
-__device__ void norm_in_place(CArgs* a, const uint16_t* gain, lds_f32* xs) {
+__device__ __forceinline__ void norm_in_place(CArgs* a, const uint16_t* gain, lds_f32* xs) {
     __shared__ float red[kWaves * 4];
     constexpr int NV = H / 4;
     constexpr int PER = (NV + kThreads - 1) / kThreads;
@@ -448,7 +465,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
             const int pu = idx / NC, c = idx - pu * NC;
             const int u = gw + nw * pu;
             const int hh = u / HALF;
-            if (hh < Hq + Hkv) cs_pre[it] = rcs[(size_t)(a->pos + c) * HALF + (u - hh * HALF)];
+            if (hh < Hq + Hkv) cs_pre[it] = rcs[(size_t)(cur_pos() + c) * HALF + (u - hh * HALF)];
             if (S::KVF == F_FP8 && hh >= Hq) {
                 const int kv = hh < Hq + Hkv ? 0 : 1;
                 const int gh = kv == 0 ? hh - Hq : hh - Hq - Hkv;
@@ -460,7 +477,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
     const MBG_CONST int32_t* ptab_s = (const MBG_CONST int32_t*)a->page_table;
     int page_c[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) page_c[c] = ptab_s[(a->pos + c) / a->page_size];
+    for (int c = 0; c < NC; ++c) page_c[c] = ptab_s[(cur_pos() + c) / a->page_size];
     if (!wait_counter(a, wctr, wneed)) return false;
     if (layer == 0) {
         int tok[NC];
@@ -497,7 +514,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
         const int u = gw + nw * pu;
         const int hh = u / HALF;
         const int i = u - hh * HALF;
-        const int p = a->pos + c;
+        const int p = cur_pos() + c;
         if (hh < Hq + Hkv) {
             const float cs = cs_pre[it][0], sn = cs_pre[it][1];
             const float y0 = x0 * cs - x1 * sn;
@@ -698,7 +715,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const int s = (int)tile - gg * S_;
     const int g = gg / HG;
     const int qh0 = g * S::GQ + (gg - g * HG) * GH;   // first query head of the task
-    const int pos = a->pos, ncol = a->ncol, page_size = a->page_size;
+    const int pos = cur_pos(), ncol = a->ncol, page_size = a->page_size;
     const int n_tok = pos + ncol;
     // split length: a whole number of workgroup token slots, so that every
     // wave instruction's TPI positions start TPI-aligned and sit in one page
@@ -734,8 +751,13 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             const size_t vstep = (size_t)Hkv * page_size * HD * EB;   // K -> V of the same page
             const MBG_GLOBAL uint8_t* kp = pool + el * EB + lane_off;
             MBG_LDS uint8_t* dst = ring + (b * NUB + u) * 2 * kUnitBytes;
-            lds_dma16(kp, (MBG_LDS void*)dst);
-            lds_dma16(kp + vstep, (MBG_LDS void*)(dst + kUnitBytes));
+            if (tb + TPI > a->pos) {   // rows this launch writes (an earlier step's K/V): coherent loads
+                lds_dma16_coh(kp, (MBG_LDS void*)dst);
+                lds_dma16_coh(kp + vstep, (MBG_LDS void*)(dst + kUnitBytes));
+            } else {
+                lds_dma16(kp, (MBG_LDS void*)dst);
+                lds_dma16(kp + vstep, (MBG_LDS void*)(dst + kUnitBytes));
+            }
         }
     };
 
@@ -903,7 +925,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         else
             old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv * HG + gg) * kLineU32, 1u,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old + 1u == a->epoch * (uint32_t)S_);
+        s_last = (old + 1u == cur_epoch() * (uint32_t)S_);
     }
     __syncthreads();
     if (!s_last) return true;
@@ -1182,12 +1204,17 @@ struct RouteLds {
     uint32_t mask[kMaxExperts / 32];
     int nslots, nrouted;
     int slot_exp[kMaxSlots];     // expert id; ids >= n_experts are shared experts
+    uint8_t slot_of[kMaxExperts];   // slot of a selected routed expert
     float wt[kMaxSlots][4];      // weight of a slot in each column (0: not selected)
     int sel[4][kMaxTopK];
     float selw[4][kMaxTopK];
     uint32_t layer, epoch;       // the routing these fields hold
 };
 __shared__ RouteLds s_route;
+// The normalised FFN input a ROUTER task left at the start of LDS (layer and
+// launch epoch it belongs to; epoch 0: none): the same workgroup's expert
+// gate/up task of that layer reuses it instead of loading it again.
+__shared__ uint32_t s_xs_layer, s_xs_epoch;
 
 __device__ __forceinline__ float from_ordered_key32(uint32_t k) {
     return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
@@ -1201,22 +1228,35 @@ __device__ __forceinline__ uint32_t ordered_key32(float f) {
 
 // Routing of this step, from the router logits (float32 [k][E]), into
 // s_route.  Wave c < NC picks column c's top-k: lane l holds experts
-// 8l .. 8l+7 as 64-bit keys (value order, then lower index), and k rounds of
-// a wave-wide maximum take them out one by one.  Weights are
-// exp(r_j - r_max) / sum over the picked j, which equals the picked softmax
-// probabilities renormalised to sum to one.
+// 8l .. 8l+7, each as a 32-bit order key of its logit and a 32-bit key of
+// its index (larger for a lower index); k rounds take the largest (value,
+// then lower index) out one by one, each round a wave maximum of the value
+// keys followed by one of the index keys among the values equal to it.
+// Weights are exp(r_j - r_max) / sum over the picked j, which equals the
+// picked softmax probabilities renormalised to sum to one.  The slots (the
+// union of picked experts, by increasing id, then the shared experts) come
+// from a prefix sum over the 16 words of the selection mask.
+// Inlined: as a called function the argument block would reach it through a
+// vector register, and every field read would become a vector memory load.
 template <int NC>
-__device__ void route_slots(CArgs* a, uint32_t layer) {
+__device__ __forceinline__ void route_slots(CArgs* a, uint32_t layer) {
     RouteLds& R = s_route;
     const int E = a->n_experts, K = a->top_k;
     const int lane = lane_id(), wave = wave_id();
-    for (int i = threadIdx.x; i < kMaxExperts / 32; i += kThreads) R.mask[i] = 0u;
-    for (int i = threadIdx.x; i < kMaxSlots * 4; i += kThreads) (&R.wt[0][0])[i] = 0.f;
-    __syncthreads();
+    constexpr int kMaskWords = kMaxExperts / 32;
+    static_assert(kMaskWords <= 16, "one row of lanes scans the mask");
+    if constexpr (NC > 1) {   // several waves add to the mask: clear it first
+        for (int i = threadIdx.x; i < kMaskWords; i += kThreads) R.mask[i] = 0u;
+        for (int i = threadIdx.x; i < kMaxSlots * 4; i += kThreads) (&R.wt[0][0])[i] = 0.f;
+        __syncthreads();
+    } else if (wave == 0) {   // wave 0 alone writes it below
+        if (lane < kMaskWords) R.mask[lane] = 0u;
+        for (int i = lane; i < kMaxSlots * 4; i += kWave) (&R.wt[0][0])[i] = 0.f;
+    }
     if (wave < NC) {
         const int c = wave;
         const rsrc_t rl = make_rsrc(a->rlogits);
-        unsigned long long key[8];
+        uint32_t hi[8], lo[8];
         const bool has = 8 * lane < E;
         f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
         if (has) {
@@ -1226,61 +1266,66 @@ __device__ void route_slots(CArgs* a, uint32_t layer) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const float v = i < 4 ? v0[i] : v1[i - 4];
-            const uint32_t e = 8u * lane + i;
-            key[i] = has ? ((unsigned long long)ordered_key32(v) << 32) | (0xFFFFFFFFu - e) : 0ull;
+            hi[i] = has ? ordered_key32(v) : 0u;      // finite logits give keys > 0
+            lo[i] = 0xFFFFFFFFu - (8u * lane + i);
         }
+        if (threadIdx.x == 0) s_stamp[2] = wall_clock64() | (hi[0] & 1u);   // logits loaded
         float top_v = 0.f, wsum = 0.f;
+        uint32_t word = 0u;   // lane w < kMaskWords: bit b = expert 32 w + b picked (wave 0, NC = 1)
 #pragma unroll
         for (int k = 0; k < kMaxTopK; ++k) {
             if (k >= K) break;
-            unsigned long long m = key[0];
+            uint32_t hm = hi[0];
 #pragma unroll
-            for (int i = 1; i < 8; ++i) m = key[i] > m ? key[i] : m;
+            for (int i = 1; i < 8; ++i) hm = max(hm, hi[i]);
+            hm = wave_max_u32(hm);
+            uint32_t lm = 0u;
 #pragma unroll
-            for (int o = 32; o >= 1; o >>= 1) {
-                const uint32_t lo = (uint32_t)__shfl_xor((int)(uint32_t)m, o, kWave);
-                const uint32_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(m >> 32), o, kWave);
-                const unsigned long long om = ((unsigned long long)hi << 32) | lo;
-                m = om > m ? om : m;
-            }
+            for (int i = 0; i < 8; ++i) lm = max(lm, hi[i] == hm ? lo[i] : 0u);
+            lm = wave_max_u32(lm);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                if (key[i] == m) key[i] = 0ull;
-            const int esel = (int)(0xFFFFFFFFu - (uint32_t)(m & 0xFFFFFFFFull));
-            const float vsel = from_ordered_key32((uint32_t)(m >> 32));
+                if (hi[i] == hm && lo[i] == lm) hi[i] = 0u;
+            const int esel = (int)(0xFFFFFFFFu - lm);
+            const float vsel = from_ordered_key32(hm);
             if (k == 0) top_v = vsel;
             const float ex = expf(vsel - top_v);
             wsum += ex;
             if (lane == 0) {
                 R.sel[c][k] = esel;
                 R.selw[c][k] = ex;
-                atomicOr(&R.mask[esel >> 5], 1u << (esel & 31));
+                if constexpr (NC > 1) atomicOr(&R.mask[esel >> 5], 1u << (esel & 31));
             }
+            if constexpr (NC == 1) word |= lane == (esel >> 5) ? 1u << (esel & 31) : 0u;
         }
         if (lane < K) R.selw[c][lane] = R.selw[c][lane] / wsum;
+        if constexpr (NC == 1) {
+            if (lane < kMaskWords) R.mask[lane] = word;
+        }
+        if (threadIdx.x == 0) s_stamp[3] = wall_clock64();   // top-k picked
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-        int n = 0;
-        for (int w = 0; w < kMaxExperts / 32; ++w) {
-            uint32_t m = R.mask[w];
-            while (m) {
-                const int b = __builtin_ctz(m);
-                R.slot_exp[n++] = w * 32 + b;
-                m &= m - 1u;
-            }
+    if (wave == 0) {
+        const uint32_t m = lane < kMaskWords ? R.mask[lane] : 0u;
+        const uint32_t cnt = (uint32_t)__builtin_popcount(m);
+        const uint32_t incl = row_prefix_sum(cnt);
+        int n = (int)(incl - cnt);
+        for (uint32_t mm = m; mm; mm &= mm - 1u) {
+            const int e = lane * 32 + __builtin_ctz(mm);
+            R.slot_of[e] = (uint8_t)n;
+            R.slot_exp[n++] = e;
         }
-        R.nrouted = n;
-        for (int sh = 0; sh < a->n_shared; ++sh) R.slot_exp[n + sh] = E + sh;
-        R.nslots = n + a->n_shared;
+        const int nr = __builtin_amdgcn_readlane((int)incl, kMaskWords - 1);
+        if (lane < a->n_shared) R.slot_exp[nr + lane] = E + lane;
+        if (lane == 0) {
+            R.nrouted = nr;
+            R.nslots = nr + a->n_shared;
+        }
     }
     __syncthreads();
     if ((int)threadIdx.x < NC * K) {
         const int c = threadIdx.x / K, k = threadIdx.x - c * K;
-        const int e = R.sel[c][k];
-        int slot = 0;
-        while (R.slot_exp[slot] != e) ++slot;
-        R.wt[slot][c] = R.selw[c][k];
+        R.wt[R.slot_of[R.sel[c][k]]][c] = R.selw[c][k];
     }
     if ((int)threadIdx.x < NC * a->n_shared) {
         const int c = threadIdx.x / a->n_shared, sh = threadIdx.x - c * a->n_shared;
@@ -1288,7 +1333,7 @@ __device__ void route_slots(CArgs* a, uint32_t layer) {
     }
     if (threadIdx.x == 0) {
         R.layer = layer;
-        R.epoch = a->epoch;
+        R.epoch = cur_epoch();
     }
     __syncthreads();
 }
@@ -1315,6 +1360,10 @@ __device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t til
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->xres, NC * H, xs);
     norm_in_place<NC, H>(a, L->ffn_norm, xs);
+    if (threadIdx.x == 0) {
+        s_xs_layer = layer;
+        s_xs_epoch = cur_epoch();
+    }
     if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
     MBG_GLOBAL float* rl = gp(a->rlogits);
@@ -1336,10 +1385,13 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
     const int lane = lane_id(), wave = wave_id();
     CLayer* L = (CLayer*)a->layers + layer;
     // the input (the stream after the output projection) is complete before
-    // the router is: load and normalise it first, then wait for the logits
-    if (!wait_counter(a, ctr_index(layer, PH_OPROJ), a->tiles_o)) return false;
-    dma_input(a, a->xres, NC * H, xs);
-    norm_in_place<NC, H>(a, L->ffn_norm, xs);
+    // the router is: load and normalise it first, then wait for the logits;
+    // a workgroup whose router task of this layer left it in LDS keeps it
+    if (!(s_xs_layer == layer && s_xs_epoch == cur_epoch())) {
+        if (!wait_counter(a, ctr_index(layer, PH_OPROJ), a->tiles_o)) return false;
+        dma_input(a, a->xres, NC * H, xs);
+        norm_in_place<NC, H>(a, L->ffn_norm, xs);
+    }
     if (!wait_counter(a, wctr, wneed)) return false;
     route_slots<NC>(a, layer);
     const RouteLds& R = s_route;
@@ -1368,7 +1420,11 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
         const uint8_t* sb = e < E ? egs + (size_t)e * kMatScales : sgs + (size_t)(e - E) * kMatScales;
         return GRow{gp(reinterpret_cast<const uint4*>(cb + row * (H / 2))), gp(sb + row * (H / 32))};
     };
-    using RS = RowStream<F_MXFP4, NC, H / 32>;
+    // a wave's rows (about 14 of 1.3 KiB for the routed model) are issued at
+    // once: the rows are only known after routing, so nothing was prefetched
+    // before the wait, and with a chunk of 4 rows in flight per wave the
+    // stream is bound by memory latency
+    using RS = RowStream<F_MXFP4, NC, H / 32, (NC <= 2 ? 8 : 4)>;
     RS st(2 * nunits, lane);
     typename RS::Buf A, B;
     st.issue(A, 0, rowf);
@@ -1448,7 +1504,7 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
     };
     // this workgroup's expert gate/up task of the layer left the routing in
     // LDS: then the first pass's weights are requested before the wait
-    const bool have_route = R.layer == layer && R.epoch == a->epoch;
+    const bool have_route = R.layer == layer && R.epoch == cur_epoch();
     if (have_route) issue_pass(0, min(kSlotsPerPass, R.nslots));
     // the residual after this layer's output projection (final since this
     // workgroup's expert gate/up wait)
@@ -1559,7 +1615,7 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     unsigned long long best[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) best[c] = 0ull;
-    MBG_GLOBAL float* logits = a->logits ? gp(a->logits) : nullptr;
+    MBG_GLOBAL float* logits = a->logits ? gp(a->logits) + (size_t)cur_step() * NC * a->vocab : nullptr;
     auto out = [&](int rr, const float (&s)[NC]) {
         const uint32_t r = (uint32_t)(r0 + kWaves * rr);
         float sc = 1.0f;
@@ -1591,15 +1647,19 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t old = __hip_atomic_fetch_add(gp(a->lm_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old + 1u == a->epoch * a->tiles_lm);
+        s_last = (old + 1u == cur_epoch() * a->tiles_lm);
     }
     __syncthreads();
     if (s_last && threadIdx.x < NC) {
         const int c = threadIdx.x;
         const unsigned long long k = __hip_atomic_load(keys + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        gp(a->argmax)[c] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+        // device-coherent: the next step of a multi-step launch reads it as its token
+        __hip_atomic_store(gp(a->argmax) + (size_t)cur_step() * NC + c,
+                           (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(keys + c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (s_last) release_counter(a, token_ctr_index(a));   // this step's token is written
     return true;
 }
 
@@ -1619,11 +1679,26 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
     if (threadIdx.x == 0) {
         s_stamp[2] = s_stamp[3] = 0;
         s_route.epoch = 0;   // no routing held yet (epochs start at 1)
+        s_xs_epoch = 0;      // no router input held yet
         if (S::KVF == F_BF16 && a->attn_local) {   // the attention placement assumes workgroup b runs on XCD b % 8
             uint32_t xcc;
             asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
             if ((xcc & 0xFu) != (blockIdx.x & 7u)) latch_error(a->status, kStatusPlacement);
         }
+    }
+    const int nsteps = a->nsteps;
+    for (int step = 0; step < nsteps; ++step) {
+    if (threadIdx.x == 0) {
+        s_ep = a->epoch + (uint32_t)step;
+        s_pos = a->pos + step;
+        s_step = step;
+    }
+    __syncthreads();
+    // a later step of the launch starts when the previous step's argmax (its
+    // token) is written
+    if (step > 0 && !wait_until(a, token_ctr_index(a), a->epoch + (uint32_t)(step - 1))) {
+        __builtin_amdgcn_s_waitcnt(0);
+        return;
     }
     for (uint32_t ti = off[b]; ti < end; ++ti) {
         const u32x4 tv = tasks[ti];
@@ -1677,6 +1752,7 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
             s_stamp[2] = 0;
             s_stamp[3] = 0;
         }
+    }
     }
 }
 

@@ -203,6 +203,10 @@ class DeviceModel:
     def step(self, token: torch.Tensor, pos: int, logits: torch.Tensor | None, argmax: torch.Tensor) -> None:
         M.mbg_decode_step(self.ctx, token, pos, logits, argmax)
 
+    def steps(self, token: torch.Tensor, n_steps: int, pos: int, logits, argmax: torch.Tensor) -> None:
+        """n_steps greedy steps in one launch (argmax [n_steps], logits [n_steps][V] or None)."""
+        M.mbg_decode_steps(self.ctx, token, n_steps, pos, logits, argmax)
+
     def verify(self, tokens: torch.Tensor, pos: int, logits, argmax) -> None:
         M.mbg_decode_verify(self.ctx, tokens, tokens.numel(), pos, logits, argmax)
 

@@ -154,7 +154,7 @@ def test_counter_block_size_and_init_ownership_checks(M):
     cfg = _cfg(M)
     n = M.mbg_counter_bytes(cfg)
     L = 2
-    assert n == 128 + L * 6 * 8 * 128     # status line + 8 lines per (layer, phase) counter
+    assert n == 128 + (L * 6 + 1) * 8 * 128   # status line + 8 lines per (layer, phase) counter + step token
     assert M.mbg_counter_bytes(_cfg(M, n_layers=64)) < 1 << 20
     ws = M.mbg_workspace_size(cfg)
     for ctr, nbytes in ((None, n), (FAKE, n - 4), (FAKE + 16, n)):

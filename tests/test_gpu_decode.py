@@ -355,3 +355,67 @@ def test_token_out_of_range_is_clamped_and_flagged():
         check_argmax(int(amax.item()), g, ref, what=f"pos {pos}")
         st = dm.status()
         assert st == (M.MBG_E_RANGE if bad else 0), (pos, st)
+
+
+def _multi_vs_single(cfg, host, build, p0, n, what, rel_tol=None):
+    """n greedy steps in one launch vs n single-step launches (bitwise) and
+    vs the oracle teacher-forced with the GPU's tokens."""
+    import gpu_util
+    t0 = int(gen.prompt_tokens(cfg, 1)[0])
+    V = cfg.vocab
+    dm1, om, oc = build(cfg, host=host)
+    dm2, _, _ = build(cfg, host=host)
+    say(what, "launches: 1 x", n, "steps and", n, "x 1 step")
+    tok = torch.tensor([t0], dtype=torch.int32, device="cuda")
+    logits = torch.empty((n, V), dtype=torch.float32, device="cuda")
+    toks = torch.full((n,), -1, dtype=torch.int32, device="cuda")
+    dm1.steps(tok, n, p0, logits, toks)
+    buf = torch.tensor([t0], dtype=torch.int32, device="cuda")
+    single = []
+    one = torch.empty(V, dtype=torch.float32, device="cuda")
+    stoks = []
+    for i in range(n):
+        dm2.step(buf, p0 + i, one, buf)
+        single.append(one.cpu().numpy().copy())
+        stoks.append(int(buf.item()))
+    torch.cuda.synchronize()
+    g = logits.cpu().numpy()
+    gt = [int(t) for t in toks.cpu().numpy()]
+    assert dm1.status() == 0 and dm2.status() == 0
+    assert gt == stoks, f"{what}: tokens {gt} vs single steps {stoks}"
+    assert np.array_equal(g, np.stack(single)), f"{what}: logits differ from single-step launches"
+    t = t0
+    graded = 0
+    for i in range(n):
+        ref = om.step(oc, t, p0 + i)
+        kw = {} if rel_tol is None else {"rel_tol": rel_tol}
+        compare_logits(g[i], ref, what=f"{what} step {i}", **kw)
+        graded += check_argmax(gt[i], g[i], ref, what=f"{what} step {i}")
+        t = gt[i]
+    say(what, "graded", graded, "of", n)
+    dm1.close()
+    dm2.close()
+
+
+def test_multi_step_launch_tiny():
+    """A whole greedy generation in one launch (tokens stay on the device)."""
+    cfg = CONFIGS["tiny"]
+    _multi_vs_single(cfg, gen.dense_weights(cfg), build_dense, 0, 24, "tiny multi-step")
+
+
+def test_multi_step_launch_dense2b():
+    cfg = CONFIGS["dense2b"]
+    _multi_vs_single(cfg, gen.dense_weights(cfg), build_dense, cfg.prefill, 8, "dense2b multi-step")
+
+
+def test_multi_step_range_checks():
+    from memory_bound_gemv_amd import _mbg as M
+    cfg = CONFIGS["tiny"]
+    dm, _, _ = build_dense(cfg)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.zeros(64, dtype=torch.int32, device="cuda")
+    for n, pos in ((0, 0), (4097, 0), (2, cfg.max_pos - 1)):
+        with pytest.raises(M.MbgError) as e:
+            dm.steps(tok, n, pos, None, out)
+        assert e.value.code == M.MBG_E_RANGE
+    assert dm.status() == 0

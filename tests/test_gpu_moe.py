@@ -185,3 +185,13 @@ def test_moe_full_step_and_verify():
     say("moe graded routing decisions", routed, "of", cfg.n_decode * cfg.n_layers)
     assert routed >= 8 * 42 // 2
     _verify(dm, cfg, cfg.prefill, toks[:4], steps[:4], "moe")
+
+
+def test_moe_small_multi_step_launch():
+    """Routed model: 6 greedy steps in one launch equal 6 single-step
+    launches bit for bit (routing, expert phases and KV across steps) and
+    match the oracle teacher-forced with the GPU's tokens."""
+    from test_gpu_decode import _multi_vs_single
+    cfg = MOE_SMALL
+    _multi_vs_single(cfg, gen.dense_weights(cfg), build_moe, cfg.prefill, 6, "moe_small multi-step",
+                     rel_tol=LOGIT_REL_L2_MXFP4)
