@@ -338,11 +338,19 @@ def run_decode(args, cfg):
         win = torch.tensor([int(t) for t in gen.prompt_tokens(cfg, 4)], dtype=torch.int32, device=dev)
         wl = torch.empty((4, cfg.vocab), dtype=torch.float32, device=dev)
         wa = torch.zeros(4, dtype=torch.int32, device=dev)
-        for _ in range(3):
-            dm.verify(win, cfg.prefill, wl, wa)
-        ms_win = timed(stream, lambda i: dm.verify(win, cfg.prefill, wl, wa), max(5, args.steps // 4))
-        if dm.status() != 0:
-            raise RuntimeError("device status after the verify windows")
+        from memory_bound_gemv_amd import _mbg as M
+        ms_path = {}
+        for path in (M.MBG_PATH_FMA, M.MBG_PATH_MFMA):
+            M.mbg_set_verify_path(dm.ctx, path)
+            for _ in range(3):
+                dm.verify(win, cfg.prefill, wl, wa)
+            ms_path[path] = timed(stream, lambda i: dm.verify(win, cfg.prefill, wl, wa), max(5, args.steps // 4))
+            if dm.status() != 0:
+                raise RuntimeError("device status after the verify windows")
+        best = min(ms_path, key=ms_path.get)
+        M.mbg_set_verify_path(dm.ctx, best)
+        dm.verify(win, cfg.prefill, wl, wa)
+        ms_win = ms_path[best]
         distinct = []
         for li in range(cfg.n_layers):
             idx, _ = dm.routing(li)
@@ -353,6 +361,9 @@ def run_decode(args, cfg):
             "k": 4, "ms_per_window": round(ms_win, 4), "tokens_s": round(4e3 / ms_win, 1),
             "window_over_step": round(ms_win / ms_per_step, 3), "distinct_experts_per_layer": round(nd, 2),
             "bytes_per_window": wb, "achieved_GBs": round(wb / (ms_win / 1e3) / 1e9, 1),
+            "path": "mfma" if best == M.MBG_PATH_MFMA else "fma",
+            "ms_per_window_fma": round(ms_path[M.MBG_PATH_FMA], 4),
+            "ms_per_window_mfma": round(ms_path[M.MBG_PATH_MFMA], 4),
         }
 
     if args.trace:

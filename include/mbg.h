@@ -52,6 +52,10 @@ extern "C" {
 #define MBG_E_HIP -6             /* a HIP runtime call failed                */
 #define MBG_E_TIMEOUT -7         /* a device wait exceeded its deadline      */
 
+/* ------------------------------------------------- verify-window paths */
+#define MBG_PATH_FMA 0   /* k-column FMA GEMV on the vector ALU */
+#define MBG_PATH_MFMA 1  /* 16-row blocks on the matrix cores (BF16 hi + lo activations) */
+
 /* ---------------------------------------------------------------- dtypes */
 #define MBG_BF16 1
 #define MBG_FP8_E4M3 2  /* one binary32 scale per row: value = code * scale[row] */
@@ -143,6 +147,7 @@ typedef struct {
     int32_t attn_splits;      /* split-KV partitions per KV head */
     int32_t attn_local;       /* 1: a KV head's splits run on one XCD and exchange partials through its L2 */
     int32_t trace;            /* 1 while in-kernel trace stamps are on (mbg_set_trace) */
+    int32_t verify_path;      /* MBG_PATH_FMA or MBG_PATH_MFMA (mbg_set_verify_path) */
     int64_t weight_bytes_per_step; /* bytes of weights one step reads (dense/shared; MoE routed excluded) */
     int64_t workspace_bytes;
     int64_t clock_khz;        /* rate of the device clock the trace stamps count */
@@ -275,6 +280,19 @@ int mbg_query(const mbg_ctx *ctx, mbg_info *info);
  * section on the three bills: synchronisation).  MBG_E_INVALID_ARG for
  * us <= 0. */
 int mbg_set_timeout_us(mbg_ctx *ctx, int64_t us);
+
+/* How verify windows (k >= 2 columns) run the routed experts' gate/up
+ * rows: MBG_PATH_FMA multiplies every weight with each column on the vector
+ * ALU (k multiply-adds per weight); MBG_PATH_MFMA decodes 16 rows at a time
+ * to BF16 and runs v_mfma_f32_16x16x32_bf16 against the columns split into
+ * BF16 hi and lo parts (the binary32 activations to ~2^-16 relative).  The
+ * 163.com Ling-3.0-flash article (optimisation 3) finds expert activation to
+ * be what a 4-token verify window costs; the two paths are timed against
+ * each other on that window.  Single-token steps always use the FMA path,
+ * and so do configurations without routed experts.  The default is
+ * MBG_PATH_FMA.  Takes effect for later calls.  MBG_E_INVALID_ARG for another
+ * value. */
+int mbg_set_verify_path(mbg_ctx *ctx, int path);
 
 /* Per-task self-profiling.  With `on` != 0, every later step makes thread 0
  * of each workgroup record, for each task it runs, eight uint64 words: the

@@ -65,7 +65,8 @@ class mbg_config(C.Structure):
 
 class mbg_info(C.Structure):
     _fields_ = [(f, C.c_int32) for f in ("grid", "block", "n_tasks", "launches_per_step", "lm_dtype", "kv_dtype",
-                                          "expert_dtype", "attn_dtype", "attn_splits", "attn_local", "trace")] + [
+                                          "expert_dtype", "attn_dtype", "attn_splits", "attn_local", "trace",
+                                          "verify_path")] + [
         ("weight_bytes_per_step", C.c_int64), ("workspace_bytes", C.c_int64), ("clock_khz", C.c_int64),
         ("variant", C.c_char * 64)]
 
@@ -96,6 +97,7 @@ def _load():
         "mbg_query": (C.c_int, [CTX_P, C.POINTER(mbg_info)]),
         "mbg_set_timeout_us": (C.c_int, [CTX_P, C.c_int64]),
         "mbg_set_trace": (C.c_int, [CTX_P, C.c_int]),
+        "mbg_set_verify_path": (C.c_int, [CTX_P, C.c_int]),
         "mbg_read_trace": (C.c_int, [CTX_P, C.c_void_p, C.c_size_t, C.POINTER(C.c_size_t)]),
         "mbg_read_routing": (C.c_int, [CTX_P, C.c_int32, C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
         "mbg_last_error": (C.c_char_p, []),
@@ -120,7 +122,8 @@ def _load():
 _lib = _load()
 EXPORTED = ("mbg_workspace_size", "mbg_counter_bytes", "mbg_validate", "mbg_decode_init", "mbg_decode_step",
             "mbg_decode_verify", "mbg_decode_steps",
-            "mbg_get_status", "mbg_query", "mbg_set_timeout_us", "mbg_set_trace", "mbg_read_trace",
+            "mbg_get_status", "mbg_query", "mbg_set_timeout_us", "mbg_set_verify_path", "mbg_set_trace",
+            "mbg_read_trace",
             "mbg_read_routing", "mbg_last_error", "mbg_destroy",
             "mbg_lm_head_workspace_size", "mbg_lm_head", "mbg_lm_head_noalloc", "mbg_quantize_fp8_rows",
             "mbg_kv_write")
@@ -235,6 +238,14 @@ def mbg_query(ctx) -> mbg_info:
 
 def mbg_set_timeout_us(ctx, us: int) -> None:
     _check(_lib.mbg_set_timeout_us(ctx, us))
+
+
+MBG_PATH_FMA = 0
+MBG_PATH_MFMA = 1
+
+
+def mbg_set_verify_path(ctx, path: int) -> None:
+    _check(_lib.mbg_set_verify_path(ctx, path))
 
 
 def mbg_set_trace(ctx, on: bool) -> None:

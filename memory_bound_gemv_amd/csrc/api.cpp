@@ -684,6 +684,7 @@ int mbg_query(const mbg_ctx* x, mbg_info* info) {
     info->attn_splits = x->base.attn_splits;
     info->attn_local = x->base.attn_local;
     info->trace = x->trace_on;
+    info->verify_path = x->base.verify_mfma ? MBG_PATH_MFMA : MBG_PATH_FMA;
     info->clock_khz = x->wall_khz;
     info->weight_bytes_per_step = x->weight_bytes;
     info->workspace_bytes = (int64_t)x->ws_bytes;
@@ -694,6 +695,13 @@ int mbg_query(const mbg_ctx* x, mbg_info* info) {
 int mbg_set_timeout_us(mbg_ctx* x, int64_t us) {
     if (!x || us <= 0) return fail(MBG_E_INVALID_ARG, "ctx is NULL or timeout <= 0");
     x->timeout_us = us;
+    return MBG_OK;
+}
+
+int mbg_set_verify_path(mbg_ctx* x, int path) {
+    if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
+    if (path != MBG_PATH_FMA && path != MBG_PATH_MFMA) return fail(MBG_E_INVALID_ARG, "verify path %d", path);
+    x->base.verify_mfma = path == MBG_PATH_MFMA ? 1 : 0;
     return MBG_OK;
 }
 

@@ -148,6 +148,7 @@ struct StepArgs {
     int32_t ncol;
     uint32_t epoch;            // epoch of the launch's first step; step s runs with epoch + s
     int32_t nsteps;            // greedy steps in this launch (token of step s > 0 = argmax of step s - 1)
+    int32_t verify_mfma;       // k >= 2: expert gate/up rows on the matrix cores (mfma.h) instead of FMA
     int32_t attn_local;        // 1: the splits of an attention group run on one XCD (workgroup b on XCD b % 8)
                                //    and exchange partials and arrivals through that XCD's L2
     uint64_t deadline_ticks;   // s_memrealtime ticks a wait may take

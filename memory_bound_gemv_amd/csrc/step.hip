@@ -32,6 +32,7 @@
 
 #include "gemv.h"
 #include "layout.h"
+#include "mfma.h"
 #include "ops.h"
 
 namespace mbg {
@@ -1420,16 +1421,45 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
         const uint8_t* sb = e < E ? egs + (size_t)e * kMatScales : sgs + (size_t)(e - E) * kMatScales;
         return GRow{gp(reinterpret_cast<const uint4*>(cb + row * (H / 2))), gp(sb + row * (H / 32))};
     };
+    MBG_GLOBAL float* hb = gp(a->hbuf);
+    const int ld = a->hb_ld;
+    if constexpr (NC >= 2) {
+        if (a->verify_mfma) {
+            // matrix-core tile: 16 rows (8 units) per instruction block
+            MBG_LDS u32x4* bprep = reinterpret_cast<MBG_LDS u32x4*>(xs + NC * H);
+            mfma_prep_b<F_MXFP4, NC, H>(xs, H, bprep, wave, kWaves, lane);
+            MfmaStream<F_MXFP4, NC, H, H / 128> ms(2 * nunits, lane);
+            auto outb = [&](int b, const float (&d)[4]) {
+                const int n = lane & 15, j = lane >> 4;
+                if (n >= NC) return;
+#pragma unroll
+                for (int p = 0; p < 2; ++p) {
+                    const int iu = 8 * b + 2 * j + p;   // rows 2 iu (gate) and 2 iu + 1 (up)
+                    if (iu >= nunits) continue;
+                    const int u = u0 + wave + kWaves * iu;
+                    const float gv = d[2 * p], uv = d[2 * p + 1];
+                    stc(hb + (size_t)n * ld + u, R.wt[u / MF][n] * (gv / (1.0f + expf(-gv)) * uv));
+                }
+            };
+            ms.run(rowf, bprep, outb);
+            stamp(1);
+            if (tile == 0 && (int)threadIdx.x < NC * a->top_k) {  // routing record of this step
+                const int c = threadIdx.x / a->top_k, k = threadIdx.x - c * a->top_k;
+                const size_t o = ((size_t)layer * a->ncol + c) * a->top_k + k;
+                gp(a->route_idx)[o] = R.sel[c][k];
+                gp(a->route_w)[o] = R.selw[c][k];
+            }
+            release_counter(a, ctr_index(layer, PH_GATEUP));
+            return true;
+        }
+    }
     // a wave's rows (about 14 of 1.3 KiB for the routed model) are issued at
     // once: the rows are only known after routing, so nothing was prefetched
-    // before the wait, and with a chunk of 4 rows in flight per wave the
-    // stream is bound by memory latency
+    // before the wait
     using RS = RowStream<F_MXFP4, NC, H / 32, (NC <= 2 ? 8 : 4)>;
     RS st(2 * nunits, lane);
     typename RS::Buf A, B;
     st.issue(A, 0, rowf);
-    MBG_GLOBAL float* hb = gp(a->hbuf);
-    const int ld = a->hb_ld;
     float gate[NC];
     auto out = [&](int rr, const float (&s)[NC]) {
         if ((rr & 1) == 0) {
@@ -1809,7 +1839,11 @@ const void* MBG_CAT(step_kernel_shape_, MBG_STEP_SHAPE)(const StepVariant& v, in
         // rows or the combine's group sums, whichever is larger
         const int merge_bytes = kWaves * attn_heads(v.group) * (v.head_dim + kPartPad) * 4;
         const int red_bytes = kAttnRingBytes + (merge_bytes > kThreads * 16 ? merge_bytes : kThreads * 16);
-        const int moe_bytes = v.moe ? ncol * kSlotsPerPass * v.moe_ffn * 4 : 0;
+        int moe_bytes = v.moe ? ncol * kSlotsPerPass * v.moe_ffn * 4 : 0;
+        if (v.moe && ncol >= 2) {   // matrix-core expert gate/up: activations plus prepared B operands
+            const int mb = ncol * v.hidden * 4 + (v.hidden / 32) * kWave * 16;
+            if (mb > moe_bytes) moe_bytes = mb;
+        }
         int m = xs_bytes > red_bytes ? xs_bytes : red_bytes;
         *lds_bytes_out = m > moe_bytes ? m : moe_bytes;
     }

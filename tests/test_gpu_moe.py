@@ -122,8 +122,11 @@ def _steps(dm, om, oc, cfg, p0, toks, what):
     return outs, routed
 
 
-def _verify(dm, cfg, p0, toks, steps, what):
+def _verify(dm, cfg, p0, toks, steps, what, path=None):
     k = len(toks)
+    if path is not None:
+        _M().mbg_set_verify_path(dm.ctx, path)
+        assert dm.info().verify_path == path
     win = torch.from_numpy(np.asarray(toks, dtype=np.int32)).cuda()
     logits = torch.empty((k, cfg.vocab), dtype=torch.float32, device="cuda")
     am = torch.zeros(k, dtype=torch.int32, device="cuda")
@@ -185,6 +188,8 @@ def test_moe_full_step_and_verify():
     say("moe graded routing decisions", routed, "of", cfg.n_decode * cfg.n_layers)
     assert routed >= 8 * 42 // 2
     _verify(dm, cfg, cfg.prefill, toks[:4], steps[:4], "moe")
+    # the matrix-core expert gate/up path on the same window
+    _verify(dm, cfg, cfg.prefill, toks[:4], steps[:4], "moe mfma", path=_M().MBG_PATH_MFMA)
 
 
 def test_moe_small_multi_step_launch():
@@ -195,3 +200,35 @@ def test_moe_small_multi_step_launch():
     cfg = MOE_SMALL
     _multi_vs_single(cfg, gen.dense_weights(cfg), build_moe, cfg.prefill, 6, "moe_small multi-step",
                      rel_tol=LOGIT_REL_L2_MXFP4)
+
+
+@pytest.mark.parametrize("k", [2, 3, 4])
+def test_moe_small_verify_mfma(k):
+    """Verify window with the expert gate/up rows on the matrix cores (BF16
+    hi + lo activations): against the oracle and against k single steps,
+    and close to the FMA path's window."""
+    M = _M()
+    cfg = MOE_SMALL
+    host = gen.dense_weights(cfg)
+    toks = gen.prompt_tokens(cfg, k)
+    dm, om, oc = build_moe(cfg, host=host)
+    steps, _ = _steps(dm, om, oc, cfg, cfg.prefill, toks, f"moe_small k={k}")
+    win = torch.from_numpy(np.asarray(toks, dtype=np.int32)).cuda()
+    outs = {}
+    for path in (M.MBG_PATH_FMA, M.MBG_PATH_MFMA):
+        M.mbg_set_verify_path(dm.ctx, path)
+        logits = torch.empty((k, cfg.vocab), dtype=torch.float32, device="cuda")
+        am = torch.zeros(k, dtype=torch.int32, device="cuda")
+        dm.verify(win, cfg.prefill, logits, am)
+        torch.cuda.synchronize()
+        outs[path] = (logits.cpu().numpy(), am.cpu().numpy())
+    assert dm.status() == 0
+    g, amh = outs[M.MBG_PATH_MFMA]
+    for j in range(k):
+        step_g, ref = steps[j]
+        compare_logits(g[j], ref, rel_tol=LOGIT_REL_L2_MXFP4, what=f"mfma verify col {j} vs oracle")
+        d = float(np.max(np.abs(g[j] - step_g)))
+        assert d < 2e-3, f"mfma verify col {j} vs step: max abs {d}"
+        d2 = float(np.max(np.abs(g[j] - outs[M.MBG_PATH_FMA][0][j])))
+        assert d2 < 2e-3, f"mfma vs fma col {j}: max abs {d2}"
+        check_argmax(int(amh[j]), g[j], ref, what=f"mfma verify col {j}")
