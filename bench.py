@@ -49,10 +49,11 @@ def traffic_file(name: str) -> str:
     return os.path.join(ROOT, "profiles", f"{name}_traffic.txt")
 
 
-def stored_traffic(name: str):
+def stored_traffic(name: str, steps_per_launch: int = 1):
     """HBM bytes per launch from the committed counter summary (FETCH_SIZE +
     WRITE_SIZE, each scaled by a plain-copy calibration), or None when the
-    summary is missing or was taken on other kernel sources."""
+    summary is missing, was taken on other kernel sources or on launches of
+    another number of steps."""
     from memory_bound_gemv_amd.build import source_digest
     path = traffic_file(name)
     if not os.path.exists(path):
@@ -64,6 +65,8 @@ def stored_traffic(name: str):
                 k, v = line.split(":", 1)
                 fields[k.strip()] = v.strip()
     if fields.get("source_digest") != source_digest():
+        return None
+    if int(fields.get("steps_per_launch", "1")) != steps_per_launch:
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -268,28 +271,34 @@ def run_decode(args, cfg):
     step_bytes = wbytes + kv_avg
     single = {"tokens_s": round(tok_s, 2), "ms_per_step": round(ms_per_step, 4), "launches_per_token": 1}
     launches_per_token = 1.0
-    G = args.multi_step
+    G = min(args.multi_step, cfg.n_decode, args.steps)
     if G > 1:
-        # G greedy steps per launch (positions prefill .. prefill + G - 1), the
-        # next launch's first token read on the device from the previous
-        # launch's last argmax (two token buffers used in turn)
-        G = min(G, cfg.n_decode)
+        # G greedy steps per launch (positions prefill .. prefill + G - 1);
+        # each launch reads its first token on the device from the previous
+        # launch's last argmax (two token buffers used in turn).  Exactly
+        # args.steps steps are timed: the last launch takes the remainder.
         tk = [torch.zeros(G, dtype=torch.int32, device=dev) for _ in range(2)]
         tk[1][G - 1] = int(gen.prompt_tokens(cfg, 1)[0])
-        launch = lambda i: dm.steps(tk[(i + 1) % 2][G - 1:], G, cfg.prefill, None, tk[i % 2])
+        sizes = [G] * (args.steps // G) + ([args.steps % G] if args.steps % G else [])
+        last = [G - 1]   # index of the previous launch's last argmax in its buffer
+
+        def launch(i, g=G):
+            dm.steps(tk[(i + 1) % 2][last[0]:], g, cfg.prefill, None, tk[i % 2])
+            last[0] = g - 1
+
         for i in range(max(1, args.warmup // G)):
             launch(i)
-        n_launch = max(1, args.steps // G)
-        ms_launch = timed(stream, launch, n_launch)
+        ms_total = timed(stream, lambda i: launch(i, sizes[i]), len(sizes)) * len(sizes)
         if dm.status() != 0:
             raise RuntimeError("device status after the multi-step launches")
-        multi_tok_s = G * 1e3 / ms_launch
-        if multi_tok_s > tok_s:
-            tok_s, ms_per_step, launches_per_token = multi_tok_s, ms_launch / G, 1.0 / G
-        kv_avg = float(np.mean([algorithmic_bytes(cfg, cfg.prefill + i)[1] for i in range(G)]))
+        ms_per_step = ms_total / args.steps
+        tok_s = 1e3 / ms_per_step
+        launches_per_token = len(sizes) / args.steps
+        kv_avg = float(np.mean([algorithmic_bytes(cfg, cfg.prefill + i)[1] for s_ in sizes for i in range(s_)]))
         step_bytes = wbytes + kv_avg
+    spl = max(G, 1)   # steps per (full) launch of the timed configuration
     achieved = step_bytes / (ms_per_step / 1e3) / 1e9
-    traffic = stored_traffic(f"step_kernel_{args.workload}")
+    traffic = stored_traffic(f"step_kernel_{args.workload}", spl)
 
     out = {
         "metric": METRIC,
@@ -310,7 +319,7 @@ def run_decode(args, cfg):
             "kv_dtype": cfg.kv_dtype, "accumulate": "fp32",
             "global_batch": 1, "seq_len": cfg.prefill, "parallelism": "none (1 GPU)",
             "kernel": info.variant.decode(), "grid": info.grid, "launches_per_step": round(launches_per_token, 4),
-            "steps_per_launch": round(1 / launches_per_token),
+            "steps_per_launch": spl,
         },
         "roofline": {
             "bound": "hbm",
@@ -321,14 +330,16 @@ def run_decode(args, cfg):
             "traffic": traffic,
         },
         "bytes_per_step": {"weights": wbytes, "kv_avg": round(kv_avg), "total": round(step_bytes)},
+        "ms_per_launch": round(ms_per_step * spl, 4),
         "single_step_launches": single,
         "bound_tokens_s": round(PEAK_HBM_GBS * 1e9 / step_bytes, 1),
         "wall_tokens_s": round(args.steps / wall, 2),
         "setup_s": round(t_gen, 1),
     }
     if traffic is not None:
-        # beta: bytes moved per algorithmic byte (the KV history is counted as read once)
-        beta = (traffic - kv_avg) / wbytes
+        # beta: bytes moved per algorithmic weight byte (the KV history is
+        # counted as read once); traffic covers the steps of one launch
+        beta = (traffic / spl - kv_avg) / wbytes
         out["beta"] = round(beta, 4)
         out["bound_tokens_s_measured_beta"] = round(PEAK_HBM_GBS * 1e9 / (beta * wbytes + kv_avg), 1)
 

@@ -113,14 +113,6 @@ __device__ __forceinline__ float group16_sum(float v) {
     v += dpp_f<0x140>(v);  // row_mirror: lane i <-> 15-i
     return v;
 }
-template <int N>
-__device__ __forceinline__ float group_sum(float v) {
-    static_assert(N == 4 || N == 8 || N == 16, "group size");
-    if constexpr (N == 4) return group4_sum(v);
-    else if constexpr (N == 8) return group8_sum(v);
-    else return group16_sum(v);
-}
-
 // Values of the two 16-lane rows of each row pair (rows 0/1 and 2/3) and of
 // the two 32-lane halves, exchanged by the gfx950 permlane swaps (plain VALU,
 // no LDS round trip).  Swapping a register with itself leaves in every lane
@@ -146,6 +138,20 @@ __device__ __forceinline__ float wave_sum(float v) {
     v = a + b;
     wave_halves(v, a, b);
     return a + b;
+}
+
+// Sum within aligned groups of N lanes (4 .. 64), the same tree as above.
+template <int N>
+__device__ __forceinline__ float group_sum(float v) {
+    static_assert(N == 4 || N == 8 || N == 16 || N == 32 || N == 64, "group size");
+    if constexpr (N == 4) return group4_sum(v);
+    else if constexpr (N == 8) return group8_sum(v);
+    else if constexpr (N == 16) return group16_sum(v);
+    else if constexpr (N == 32) {
+        float a, b;
+        row_pair(group16_sum(v), a, b);
+        return a + b;
+    } else return wave_sum(v);
 }
 
 // Whole-wavefront maximum, identical in every lane.

@@ -288,4 +288,149 @@ struct RowStream {
     }
 };
 
+// Segmented variant for rows whose 16-byte vectors do not fill whole 64-lane
+// columns (2560-wide rows are 80 vectors in MXFP4 and 160 in FP8: with one
+// row per wave instruction a quarter or a half of the lanes of the last
+// column idle, yet every instruction costs the whole wave).  A wavefront
+// works on P = 64 / LPR rows at once, LPR lanes per row; lane t of a row
+// reads its vectors t, t + LPR, ... (NVL = NV / LPR of them, LPR * 16
+// contiguous bytes per row and instruction), so every lane does useful work
+// in every instruction.  Rows are streamed in chunks of RG row groups (RG * P
+// rows) with two chunk buffers in registers, as above; a row's lane sums are
+// combined within its LPR lanes by the same order-fixed tree.
+//
+// row(rr) is called with this lane's row (rows past the end are clamped to
+// the last one, so every lane loads a valid address); with RSC, GRow::scale
+// points at the row's binary32 scale, which is loaded with the row and
+// applied to its sums.  out(rr, sums) is called by every lane, rr being the
+// lane's own row (possibly >= nrows: the caller masks) and sums its row's
+// results, the same in all LPR lanes of the row.
+// Lanes per row for a row of NV vectors: the widest group (64 .. 4 lanes)
+// that divides it.
+template <int NV>
+constexpr int seg_lanes() {
+    return NV % 64 == 0 ? 64 : NV % 32 == 0 ? 32 : NV % 16 == 0 ? 16 : NV % 8 == 0 ? 8 : 4;
+}
+
+template <int F, int NC, int NV, int LPR, int RG, bool RSC = false>
+struct SegStream {
+    static constexpr int P = kWave / LPR;
+    static constexpr int NVL = NV / LPR;
+    static constexpr int E = FmtInfo<F>::kEPV;
+    static constexpr int kRowsPerChunk = RG * P;
+    static_assert(kWave % LPR == 0 && NV % LPR == 0, "lanes per row divide the wave and the row");
+
+    struct Buf {
+        uint4 w[RG][NVL];
+        uint32_t s[RG][F == F_MXFP4 ? NVL : 1];
+        float rs[RG];
+    };
+
+    int nrows, t, p;
+
+    __device__ __forceinline__ SegStream(int nrows_, int lane) : nrows(nrows_), t(lane % LPR), p(lane / LPR) {}
+
+    __device__ __forceinline__ int chunks() const { return (nrows + kRowsPerChunk - 1) / kRowsPerChunk; }
+
+    template <class RowFn>
+    __device__ __forceinline__ void issue(Buf& b, int c, RowFn& row) const {
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            const int rr = (c * RG + g) * P + p;
+            const GRow gr = row(rr < nrows ? rr : nrows - 1);
+#pragma unroll
+            for (int j = 0; j < NVL; ++j) {
+                b.w[g][j] = ld_stream_g(gr.data + t + LPR * j);
+                if constexpr (F == F_MXFP4) b.s[g][j] = gr.scale[t + LPR * j];
+            }
+            if constexpr (RSC) b.rs[g] = *reinterpret_cast<const MBG_GLOBAL float*>(gr.scale);
+        }
+    }
+
+    template <class OutFn>
+    __device__ __forceinline__ void compute(const Buf& b, int c, const lds_f32* xs, int ldx, OutFn& out) const {
+        float acc[RG][NC][2];
+#pragma unroll
+        for (int g = 0; g < RG; ++g)
+#pragma unroll
+            for (int q = 0; q < NC; ++q) acc[g][q][0] = acc[g][q][1] = 0.f;
+        // activation slices: all NC columns held at once for NC <= 2 (read
+        // once per vector for all RG row groups); for wider windows one
+        // column at a time, re-read per row group, to bound live registers
+        constexpr int XC = NC <= 2 ? NC : 1;
+#pragma unroll
+        for (int j = 0; j < NVL; ++j) {
+            const int k = (t + LPR * j) * E;
+            float xv[XC][E];
+            auto load_x = [&](int slot, int q) {
+#pragma unroll
+                for (int e = 0; e < E; e += 4) {
+                    const f32x4 v = *reinterpret_cast<const MBG_LDS f32x4*>(xs + q * ldx + k + e);
+                    xv[slot][e] = v[0];
+                    xv[slot][e + 1] = v[1];
+                    xv[slot][e + 2] = v[2];
+                    xv[slot][e + 3] = v[3];
+                }
+            };
+            if constexpr (XC == NC) {
+#pragma unroll
+                for (int q = 0; q < NC; ++q) load_x(q, q);
+            }
+#pragma unroll
+            for (int g = 0; g < RG; ++g) {
+                float wf[E];
+                decode16<F>(b.w[g][j], b.s[g][F == F_MXFP4 ? j : 0], wf);
+#pragma unroll
+                for (int q = 0; q < NC; ++q) {
+                    if constexpr (XC != NC) load_x(0, q);
+                    const int xq = XC == NC ? q : 0;
+#pragma unroll
+                    for (int e = 0; e < E; e += 2) {
+                        acc[g][q][0] = fmaf(wf[e], xv[xq][e], acc[g][q][0]);
+                        acc[g][q][1] = fmaf(wf[e + 1], xv[xq][e + 1], acc[g][q][1]);
+                    }
+                }
+            }
+            // wider windows: keep the scheduler from hoisting later vectors'
+            // LDS reads (their registers would spill)
+            if constexpr (NC > 1) __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int g = 0; g < RG; ++g) {
+            float sums[NC];
+#pragma unroll
+            for (int q = 0; q < NC; ++q) {
+                sums[q] = group_sum<LPR>(acc[g][q][0] + acc[g][q][1]);
+                if constexpr (RSC) sums[q] *= b.rs[g];
+            }
+            out((c * RG + g) * P + p, sums);
+        }
+    }
+
+    // Before the caller's input wait: issue up to `pre` (0 .. 2) chunks into
+    // a (chunk 0) and b (chunk 1).  Returns how many; pass it to run().
+    template <class RowFn>
+    __device__ __forceinline__ int prefetch(Buf& a, Buf& b, RowFn& row, int pre) const {
+        const int n = min(min(pre, 2), chunks());
+        if (n > 0) issue(a, 0, row);
+        if (n > 1) issue(b, 1, row);
+        return n;
+    }
+
+    template <class RowFn, class OutFn>
+    __device__ __forceinline__ void run(Buf& a, Buf& b, RowFn& row, const lds_f32* xs, int ldx, OutFn& out,
+                                        int issued = 0) const {
+        const int nch = chunks();
+        if (nch == 0) return;
+        if (issued < 1) issue(a, 0, row);
+        for (int c = 0; c < nch; c += 2) {
+            if (c + 1 < nch && !(c == 0 && issued >= 2)) issue(b, c + 1, row);
+            compute(a, c, xs, ldx, out);
+            if (c + 1 >= nch) break;
+            if (c + 2 < nch) issue(a, c + 2, row);
+            compute(b, c + 1, xs, ldx, out);
+        }
+    }
+};
+
 }  // namespace mbg

@@ -43,19 +43,33 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
     const int nrows = r0 < r1 ? (r1 - 1 - r0) / 4 + 1 : 0;
     const MBG_GLOBAL uint4* W = gp(reinterpret_cast<const uint4*>(a.w));
     const MBG_GLOBAL uint8_t* Ws = gp(reinterpret_cast<const uint8_t*>(a.wscale));   // MXFP4: E8M0 [V][H/32]
+    // rows that do not fill whole 64-lane vector columns (FP8 and MXFP4
+    // rows of 2560, ...) go through the segmented stream for one or two
+    // columns, the FP8 row scale loaded with its row
+    constexpr bool kSeg = NC <= 2 && NV % kWave != 0;
+    constexpr int SLPR = seg_lanes<NV>();
+    constexpr int LPR = kSeg ? SLPR : kWave;   // lanes that share a row
+    const MBG_GLOBAL float* fsc = gp(reinterpret_cast<const float*>(a.wscale));   // FP8: [V]
     auto rowf = [&](int rr) -> GRow {
         const size_t row = (size_t)(r0 + 4 * rr);
-        return GRow{W + row * NV, F == F_MXFP4 ? Ws + row * NV : nullptr};
+        const MBG_GLOBAL uint8_t* sp = F == F_MXFP4 ? Ws + row * NV
+                                       : F == F_FP8 ? reinterpret_cast<const MBG_GLOBAL uint8_t*>(fsc + row)
+                                                    : nullptr;
+        return GRow{W + row * NV, sp};
     };
+    using SS = SegStream<F, NC, NV, SLPR, (NC == 1 && NV / SLPR <= 8 ? 2 : 1), F == F_FP8>;
     using RS = RowStream<F, NC, NV>;
+    SS ss(nrows, lane);
     RS st(nrows, lane);
+    typename SS::Buf SA, SB;
     typename RS::Buf A, B;
-    st.issue(A, 0, rowf);  // weights do not depend on x: start streaming first
+    // weights do not depend on x: start streaming first
+    int pre = 0;
+    if constexpr (kSeg) pre = ss.prefetch(SA, SB, rowf, 1);
+    else st.issue(A, 0, rowf);
 
     RowScales rsc;
-    if constexpr (F == F_FP8)
-        rsc.load(gp(reinterpret_cast<const float*>(a.wscale)), nrows, lane,
-                 [&](int rr) { return (size_t)(r0 + 4 * rr); });
+    if constexpr (F == F_FP8 && !kSeg) rsc.load(fsc, nrows, lane, [&](int rr) { return (size_t)(r0 + 4 * rr); });
     const MBG_GLOBAL float* x = gp(a.x);
     for (int i = threadIdx.x; i < NC * H; i += blockDim.x) xs[i] = x[i];
     __syncthreads();
@@ -64,19 +78,28 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) best[c] = 0ull;
     MBG_GLOBAL float* logits = a.logits ? gp(a.logits) : nullptr;
+    // rr: this lane's row (wave-uniform for the one-row stream); s: its sums
     auto out = [&](int rr, const float (&s)[NC]) {
+        if (rr >= nrows) return;
         const uint32_t r = (uint32_t)(r0 + 4 * rr);
         float sc = 1.0f;
-        if constexpr (F == F_FP8) sc = rsc.get(rr, r);
+        if constexpr (F == F_FP8 && !kSeg) sc = rsc.get(rr, r);
+        const int t = lane % LPR;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const float v = s[c] * sc;
-            if (logits != nullptr && lane == c) logits[(size_t)c * a.V + r] = v;
+            if (logits != nullptr && t == c) logits[(size_t)c * a.V + r] = v;
             const unsigned long long k = argmax_key(v, r);
             best[c] = k > best[c] ? k : best[c];
         }
     };
-    st.run(A, B, rowf, xs, H, out);
+    if constexpr (kSeg) {
+        ss.run(SA, SB, rowf, xs, H, out, pre);
+#pragma unroll
+        for (int c = 0; c < NC; ++c) best[c] = wave_max_u64(best[c]);   // lanes held their own rows' best
+    } else {
+        st.run(A, B, rowf, xs, H, out);
+    }
 
     if (lane == 0) {
 #pragma unroll

@@ -1455,30 +1455,53 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
     }
     // a wave's rows (about 14 of 1.3 KiB for the routed model) are issued at
     // once: the rows are only known after routing, so nothing was prefetched
-    // before the wait
-    using RS = RowStream<F_MXFP4, NC, H / 32, (NC <= 2 ? 8 : 4)>;
-    RS st(2 * nunits, lane);
-    typename RS::Buf A, B;
-    st.issue(A, 0, rowf);
-    float gate[NC];
-    auto out = [&](int rr, const float (&s)[NC]) {
-        if ((rr & 1) == 0) {
+    // before the wait.  Rows are 80 vectors: for one or two columns the
+    // segmented stream keeps every lane busy, and a unit's gate and up rows
+    // (rr = 2 iu, 2 iu + 1) sit in neighbouring lane groups; wider windows
+    // keep one row per instruction (the segmented buffers would spill)
+    if constexpr (NC <= 2) {
+        constexpr int LPR = seg_lanes<H / 32>();
+        using SS = SegStream<F_MXFP4, NC, H / 32, LPR, (NC == 1 ? 2 : 1)>;
+        static_assert(SS::P % 2 == 0, "a unit's two rows share a wave instruction");
+        SS st(2 * nunits, lane);
+        typename SS::Buf A, B;
+        auto out = [&](int rr, const float (&s)[NC]) {
+            const int t = lane % LPR;
+            float gv = 0.f, uv = 0.f;
 #pragma unroll
-            for (int c = 0; c < NC; ++c) gate[c] = s[c];
-            return;
-        }
-        if (lane >= NC) return;
-        const int c = lane;
-        float gv = 0.f, uv = 0.f;
+            for (int c = 0; c < NC; ++c) {
+                const float other = xor_lanes<LPR>(s[c]);   // the partner row's sums
+                if (c == t) { gv = s[c]; uv = other; }
+            }
+            const int iu = rr >> 1;
+            if ((rr & 1) || t >= NC || iu >= nunits) return;
+            const int u = u0 + wave + kWaves * iu;
+            stc(hb + (size_t)t * ld + u, R.wt[u / MF][t] * (gv / (1.0f + expf(-gv)) * uv));
+        };
+        st.run(A, B, rowf, xs, H, out);
+    } else {
+        using RS = RowStream<F_MXFP4, NC, H / 32, 4>;
+        RS st(2 * nunits, lane);
+        typename RS::Buf A, B;
+        st.issue(A, 0, rowf);
+        float gate[NC];
+        auto out = [&](int rr, const float (&s)[NC]) {
+            if ((rr & 1) == 0) {
 #pragma unroll
-        for (int cc = 0; cc < NC; ++cc)
-            if (cc == c) { gv = gate[cc]; uv = s[cc]; }
-        const int u = u0 + wave + kWaves * (rr >> 1);
-        const int slot = u / MF;
-        const float w = R.wt[slot][c];
-        stc(hb + (size_t)c * ld + u, w * (gv / (1.0f + expf(-gv)) * uv));
-    };
-    st.run(A, B, rowf, xs, H, out);
+                for (int c = 0; c < NC; ++c) gate[c] = s[c];
+                return;
+            }
+            if (lane >= NC) return;
+            const int c = lane;
+            float gv = 0.f, uv = 0.f;
+#pragma unroll
+            for (int cc = 0; cc < NC; ++cc)
+                if (cc == c) { gv = gate[cc]; uv = s[cc]; }
+            const int u = u0 + wave + kWaves * (rr >> 1);
+            stc(hb + (size_t)c * ld + u, R.wt[u / MF][c] * (gv / (1.0f + expf(-gv)) * uv));
+        };
+        st.run(A, B, rowf, xs, H, out);
+    }
     stamp(1);
     if (tile == 0 && (int)threadIdx.x < NC * a->top_k) {  // routing record of this step
         const int c = threadIdx.x / a->top_k, k = threadIdx.x - c * a->top_k;
@@ -1628,37 +1651,69 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     const int r0 = (int)tile * per + wave, r1 = min(V, (int)tile * per + per);
     const int nrows = r0 < r1 ? (r1 - 1 - r0) / kWaves + 1 : 0;
     const MBG_GLOBAL uint4* W = gp(reinterpret_cast<const uint4*>(a->lm_head));
-    auto rowf = [&](int rr) -> GRow { return GRow{W + (size_t)(r0 + kWaves * rr) * (H / E), nullptr}; };
-    using RS = RowStream<F, NC, H / E>;
-    RS st(nrows, lane);
+    const MBG_GLOBAL float* lsc = gp(a->lm_scale);
+    // rows that do not fill whole 64-lane vector columns (FP8 rows of 2560
+    // are 160 vectors): up to two columns the segmented stream (two rows
+    // per instruction, the row's FP8 scale loaded with it); wider windows
+    // one row per instruction (registers)
+    constexpr int NV = H / E;
+    constexpr bool kSeg = NC <= 2 && NV % kWave != 0;
+    constexpr int SLPR = seg_lanes<NV>();
+    constexpr int LPR = kSeg ? SLPR : kWave;   // lanes that share a row
+    auto rowf = [&](int rr) -> GRow {
+        const size_t r = (size_t)(r0 + kWaves * rr);
+        return GRow{W + r * NV, F == F_FP8 ? reinterpret_cast<const MBG_GLOBAL uint8_t*>(lsc + r) : nullptr};
+    };
+    using SS = SegStream<F, NC, NV, SLPR, (NC == 1 && NV / SLPR <= 8 ? 2 : 1), F == F_FP8>;
+    using RS = RowStream<F, NC, NV>;
+    SS ss(nrows, lane);
+    RS rs(nrows, lane);
+    typename SS::Buf SA, SB;
     typename RS::Buf A, B;
+    const int pre_kib = a->gemv_pre;
     int pre = 0;
+    auto do_prefetch = [&]() {
+        if constexpr (kSeg) pre = ss.prefetch(SA, SB, rowf, (pre_kib * 1024 + SS::kRowsPerChunk * NV * 16 - 1) /
+                                                                (SS::kRowsPerChunk * NV * 16));
+        else pre = rs.prefetch(A, B, rowf, gemv_pre_rows<RS>(pre_kib));
+    };
     const bool early = wave != 0 || a->poll_wave_prefetch;   // the polling wave may hold its loads back
-    if (early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));
-    RowScales rsc;   // FP8 rows: their scales, requested before the wait
-    if constexpr (F == F_FP8) rsc.load(gp(a->lm_scale), nrows, lane, [&](int rr) { return (size_t)(r0 + kWaves * rr); });
+    if (early) do_prefetch();
+    RowScales rsc;   // FP8 rows of the one-row stream: their scales, requested before the wait
+    if constexpr (F == F_FP8 && !kSeg)
+        rsc.load(lsc, nrows, lane, [&](int rr) { return (size_t)(r0 + kWaves * rr); });
     if (!wait_counter(a, wctr, wneed)) return false;
     dma_input(a, a->xres, NC * H, xs);
     norm_in_place<NC, H>(a, a->final_norm, xs);
-    if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
+    if (!early) do_prefetch();   // after the input loads, not ahead of them
     stamp(0);
     unsigned long long best[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) best[c] = 0ull;
     MBG_GLOBAL float* logits = a->logits ? gp(a->logits) + (size_t)cur_step() * NC * a->vocab : nullptr;
+    // rr: this lane's row (wave-uniform for the one-row stream); s: its sums
     auto out = [&](int rr, const float (&s)[NC]) {
+        if (rr >= nrows) return;
         const uint32_t r = (uint32_t)(r0 + kWaves * rr);
         float sc = 1.0f;
-        if constexpr (F == F_FP8) sc = rsc.get(rr, r);
+        if constexpr (F == F_FP8 && !kSeg) sc = rsc.get(rr, r);
+        const int t = lane % LPR;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
             const float v = s[c] * sc;
-            if (logits != nullptr && lane == c) logits[(size_t)c * V + r] = v;
+            if (logits != nullptr && t == c) logits[(size_t)c * V + r] = v;
             const unsigned long long k = ((unsigned long long)ordered_key32(v) << 32) | (0xFFFFFFFFu - r);
             best[c] = k > best[c] ? k : best[c];
         }
     };
-    st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
+    if constexpr (kSeg) {
+        ss.run(SA, SB, rowf, xs, H, out, pre);
+        // lanes hold the best of their own rows
+#pragma unroll
+        for (int c = 0; c < NC; ++c) best[c] = wave_max_u64(best[c]);
+    } else {
+        rs.run(A, B, rowf, xs, H, out, rs.finish_prefetch(A, B, rowf, pre));
+    }
     stamp(1);
     if (lane == 0) {
 #pragma unroll
