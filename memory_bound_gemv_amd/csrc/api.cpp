@@ -441,9 +441,12 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     const uint32_t tiles_attn = (uint32_t)(c.n_kv_heads * head_groups * S);
     // Attention placement: workgroup b runs on XCD b % 8 (the dispatcher
     // deals workgroups round-robin over the 8 XCDs; the kernel checks it).
-    // When every group's splits fit on one XCD, group gg goes to XCD gg % 8
-    // and its splits exchange partials and arrivals through that XCD's L2
-    // instead of device-coherent memory.  Each group's block of partial rows
+    // When every group's splits fit on one XCD, XCD x takes the NG / 8
+    // consecutive groups x NG / 8 .. (x + 1) NG / 8 - 1: their splits
+    // exchange partials and arrivals through that XCD's L2 instead of
+    // device-coherent memory, and head groups of one KV head (consecutive
+    // group numbers) share the XCD, whose L2 then serves their common
+    // history after the first read.  Each group's block of partial rows
     // must then be whole 128-byte lines: (heads per task x splits) % 8 == 0.
     // The kernels for BF16 caches carry this path (the FP8-cache kernels,
     // meant for long contexts, are built without it).  Long contexts keep
@@ -462,7 +465,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
         if (!a.attn_local) return wg < (int)tiles_attn ? wg : -1;
         const int x = wg % 8, slot = wg / 8;
         if (slot >= (NG / 8) * S) return -1;
-        return ((slot / S) * 8 + x) * S + slot % S;
+        return (x * (NG / 8) + slot / S) * S + slot % S;
     };
 
     // task lists
