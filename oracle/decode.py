@@ -19,6 +19,10 @@ Where the pages are silent the plainest reading is taken:
   * query head h reads KV head floor(h * Hkv / Hq);
   * attention is causal softmax(q.k / sqrt(d)) over positions [0, pos],
     including the K/V just written at pos, read back in cache precision;
+  * a sliding-window layer of window W ("Muse Spark Open" article, section
+    on how the model is split: layers attending over the last 2,048 tokens)
+    attends the W most recent positions, [max(0, pos - W + 1), pos], its
+    own included;
   * SwiGLU: W_down (silu(W_gate x) * (W_up x)), silu(z) = z / (1 + e^-z);
   * MoE: p = softmax(W_router x); the top-k of p (lower index wins ties)
     are renormalised to sum to 1; the shared expert is added with weight 1;
@@ -86,6 +90,12 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray) -> np.ndarray:
         p = softmax(s)
         out[h] = p @ v[:, g, :]
     return out
+
+
+def window_start(pos: int, window: int) -> int:
+    """First position a token at `pos` attends in a layer of window W
+    (0 = global): the W most recent positions, its own included."""
+    return max(0, pos - window + 1) if window > 0 else 0
 
 
 def silu(z: np.ndarray) -> np.ndarray:
@@ -272,6 +282,10 @@ class OracleModel:
             self._w[key] = out
         return out
 
+    def window(self, li: int) -> int:
+        w = getattr(self.cfg, "layer_window", ())
+        return int(w[li]) if w else 0
+
     # -- one layer ---------------------------------------------------------
     def _ffn(self, li: int, xn: np.ndarray) -> np.ndarray:
         cfg = self.cfg
@@ -307,7 +321,8 @@ class OracleModel:
             k = rope(k, pos, cfg.rope_theta)
             cache.store(li, pos, k, v)
             kc, vc = cache.read(li, pos + 1, dt)
-            o = attention(q, kc, vc).reshape(-1)
+            lo = window_start(pos, self.window(li))
+            o = attention(q, kc[lo:], vc[lo:]).reshape(-1)
             x = x + self.w(f"l{li}.wo") @ o
             xn = rmsnorm(x, self.w(f"l{li}.ffn_norm"), eps)
             x = x + self._ffn(li, xn)
@@ -316,6 +331,7 @@ class OracleModel:
         return self.w("lm_head") @ xn
 
     def verify(self, cache: OracleCache, tokens, pos: int) -> np.ndarray:
-        """Verify window: token j at position pos + j sees [0, pos + j],
-        the window's earlier tokens included.  Returns logits [k][vocab]."""
+        """Verify window: token j at position pos + j sees [0, pos + j] (in a
+        sliding-window layer the last W of them), the window's earlier
+        tokens included.  Returns logits [k][vocab]."""
         return np.stack([self.step(cache, int(t), pos + j) for j, t in enumerate(tokens)])

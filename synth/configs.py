@@ -58,6 +58,11 @@ class DecodeConfig:
     k_max: int = 4                # widest verify window
     norm_gains: str = "ones"      # RMSNorm gains: "ones" (the configured 1.0) or
                                   # "random" (1 + 0.1 N(0, 1) per element, distinct per norm)
+    layer_window: tuple = ()      # per-layer attention window W (0 = global); () = all global
+
+    def window(self, layer: int) -> int:
+        """Attention window of `layer`: position p attends [max(0, p - W + 1), p]; 0 = global."""
+        return int(self.layer_window[layer]) if self.layer_window else 0
 
     @property
     def max_pos(self) -> int:

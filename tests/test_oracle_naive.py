@@ -158,20 +158,22 @@ class Naive:
             self.K[li][pos] = [cache_round(kh[g], cfg.kv_dtype, sk[g]) for g in range(Hkv)]
             self.V[li][pos] = [cache_round(vh[g], cfg.kv_dtype, sv[g]) for g in range(Hkv)]
             att = []
+            win = cfg.layer_window[li] if cfg.layer_window else 0
+            first = pos - win + 1 if win > 0 and pos - win + 1 > 0 else 0   # the last `win` positions
             for h in range(Hq):
                 g = h * Hkv // Hq
                 sc = []
-                for t in range(pos + 1):
+                for t in range(first, pos + 1):
                     kt = self.K[li][t][g]
                     sc.append(sum(a * b for a, b in zip(qh[h], kt)) / math.sqrt(d))
                 m = max(sc)
                 w = [math.exp(s - m) for s in sc]
                 z = sum(w)
                 o = [0.0] * d
-                for t in range(pos + 1):
+                for i, t in enumerate(range(first, pos + 1)):
                     vt = self.V[li][t][g]
                     for j in range(d):
-                        o[j] += w[t] / z * vt[j]
+                        o[j] += w[i] / z * vt[j]
                 att.extend(o)
             y = matvec(self.W[f"l{li}.wo"], att)
             x = [a + b for a, b in zip(x, y)]
@@ -200,8 +202,8 @@ TINY_MOE = DecodeConfig(name="naive_moe", n_layers=2, hidden=32, n_q_heads=4, n_
                         moe_ffn=32, prefill=3, n_decode=3, weight_sigma=0.3, lm_dtype="fp8")
 
 
-def _run(cfg, kv_dtype="bf16", lm_fp8=False, gains="ones"):
-    cfg = cfg.with_(kv_dtype=kv_dtype, norm_gains=gains)
+def _run(cfg, kv_dtype="bf16", lm_fp8=False, gains="ones", windows=()):
+    cfg = cfg.with_(kv_dtype=kv_dtype, norm_gains=gains, layer_window=tuple(windows))
     T = gen.dense_weights(cfg)
     if gains == "random":
         # three distinct non-unit gain vectors per layer plus the final one
@@ -257,6 +259,17 @@ def test_naive_dense_random_gains_fp8_kv():
 
 def test_naive_moe_random_gains():
     _run(TINY_MOE, lm_fp8=True, gains="random")
+
+
+@pytest.mark.parametrize("windows", [(3, 0), (1, 6), (2, 2)])
+def test_naive_sliding_window(windows):
+    """Sliding-window layers (the Muse Spark Open article, section on how
+    the model is split): the brute-force loops attend the last W positions."""
+    _run(TINY_DENSE, windows=windows)
+
+
+def test_naive_sliding_window_moe_fp8_kv():
+    _run(TINY_MOE, kv_dtype="fp8", windows=(2, 0))
 
 
 def _first_step(cfg, T):
