@@ -37,6 +37,9 @@ WORKLOADS = {
     "longctx": "dense 2B decoder (as dense2b) with an FP8-e4m3 KV cache (power-of-two per-head scales) prefilled "
                "N(0,1) to 200,000 positions in 64-token pages under a shuffled page table, batch 1, greedy decode "
                "at positions 200000..200063",
+    "longctx_swa": "long-context workload (as longctx: FP8 KV at 200,000 positions, shuffled pages) with "
+                   "sliding-window layers: layers 4i..4i+2 attend over the last 2,048 positions, layer 4i+3 "
+                   "globally, batch 1, greedy decode at positions 200000..200063",
     "moe": "routed decoder: 42 layers, hidden 2560, 32 query / 4 KV heads of 128, 512 MXFP4 experts top-8 + 1 "
            "shared (moe_ffn 768), BF16 attention/router, FP8 LM head over vocab 157184, BF16 KV prefilled to 2048 "
            "positions, batch 1, greedy decode at positions 2048..2055",
@@ -83,7 +86,8 @@ def algorithmic_bytes(cfg, pos: int) -> tuple[int, int]:
     BF16 FFN matrices, routed layers the BF16 router plus the top-k and
     shared experts a token reads (MXFP4: half a byte per weight plus one
     E8M0 byte per 32).  KV: K and V of positions [0, pos] for every layer and
-    KV head (the step's own K/V included), 2 bytes (BF16) or 1 (FP8)."""
+    KV head (the step's own K/V included; a sliding-window layer only its
+    last W positions), 2 bytes (BF16) or 1 (FP8)."""
     H, d = cfg.hidden, cfg.head_dim
     attn = 2 * (2 * H + (cfg.n_q_heads + 2 * cfg.n_kv_heads) * d * H + H * cfg.n_q_heads * d)
     if cfg.is_moe:
@@ -94,7 +98,9 @@ def algorithmic_bytes(cfg, pos: int) -> tuple[int, int]:
     lm = cfg.vocab * H + 4 * cfg.vocab if cfg.lm_dtype == "fp8" else 2 * cfg.vocab * H
     w = cfg.n_layers * (attn + ffn) + 2 * H + 2 * H + lm
     kv_el = 1 if cfg.kv_dtype == "fp8" else 2
-    kv = (pos + 1) * cfg.n_layers * 2 * cfg.n_kv_heads * d * kv_el
+    # a sliding-window layer of window W reads its last W positions
+    span = sum(min(pos + 1, cfg.window(li)) if cfg.window(li) > 0 else pos + 1 for li in range(cfg.n_layers))
+    kv = span * 2 * cfg.n_kv_heads * d * kv_el
     return w, kv
 
 
@@ -458,14 +464,15 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="moe", choices=["moe", "dense2b", "longctx", "lmhead"],
+    ap.add_argument("--workload", default="moe", choices=["moe", "dense2b", "longctx", "longctx_swa", "lmhead"],
                     help="moe (default: the routed 42-layer model), dense2b, longctx (FP8 KV at 200K "
-                         "positions) or lmhead (the LM-head GEMV alone)")
+                         "positions), longctx_swa (the same with sliding-window layers) or lmhead (the "
+                         "LM-head GEMV alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="moe: skip the 4-token verify-window timing")
     ap.add_argument("--multi-step", type=int, default=8,
-                    help="also time launches of this many greedy steps each (1: single-step launches only); "
-                         "the faster of the two is the headline value")
+                    help="steps per launch of the headline timing (1: single-step launches only); "
+                         "single-step launches are timed beside it")
     ap.add_argument("--lm-dtype", default="fp8", choices=["bf16", "fp8"], help="lmhead: weight format")
     ap.add_argument("--k", type=int, default=1, help="lmhead: activation columns (1..4)")
     ap.add_argument("--trace", default="",

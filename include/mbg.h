@@ -132,6 +132,15 @@ typedef struct {
     int32_t page_size;
     int32_t max_pos;  /* KV capacity in positions */
     int32_t k_max;    /* widest verify window, 1..4 */
+    /* Sliding-window layers: host array [n_layers], read during init only,
+     * or NULL (every layer global).  layer_window[l] = W > 0: the token at
+     * position p attends positions [max(0, p - W + 1), p] (its own and the
+     * W - 1 before it); 0: [0, p].  The "Muse Spark Open" article (section
+     * on how the model is split) describes 46 of 62 layers attending over
+     * the last 2,048 tokens and 16 global layers; which layers are which is
+     * the caller's.  The cache still holds every position; a windowed layer
+     * reads only its window.  Negative values: MBG_E_INVALID_ARG. */
+    const int32_t *layer_window;
 } mbg_config;
 
 /* What an initialised context runs (the 163.com Ling-3.0-flash article,

@@ -60,7 +60,7 @@ class mbg_config(C.Structure):
     _fields_ = [(f, C.c_int32) for f in ("n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "ffn",
                                           "vocab", "n_experts", "top_k", "n_shared", "moe_ffn")] + [
         ("rope_theta", C.c_float), ("rms_eps", C.c_float), ("page_size", C.c_int32), ("max_pos", C.c_int32),
-        ("k_max", C.c_int32)]
+        ("k_max", C.c_int32), ("layer_window", C.POINTER(C.c_int32))]
 
 
 class mbg_info(C.Structure):
@@ -147,9 +147,17 @@ def _ptr(x):
 # --------------------------------------------------------------------------- marshalling helpers
 
 def make_config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_experts=0, top_k=0,
-                n_shared=0, moe_ffn=0, rope_theta=1e4, rms_eps=1e-6, page_size=64, max_pos=1, k_max=1):
-    return mbg_config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_experts, top_k, n_shared,
-                      moe_ffn, rope_theta, rms_eps, page_size, max_pos, k_max)
+                n_shared=0, moe_ffn=0, rope_theta=1e4, rms_eps=1e-6, page_size=64, max_pos=1, k_max=1,
+                layer_window=None):
+    """layer_window: per-layer attention windows (0 = global) or None.  The
+    returned struct keeps the array alive (``_keep``)."""
+    cfg = mbg_config(n_layers, hidden, n_q_heads, n_kv_heads, head_dim, ffn, vocab, n_experts, top_k, n_shared,
+                     moe_ffn, rope_theta, rms_eps, page_size, max_pos, k_max, None)
+    if layer_window is not None:
+        arr = (C.c_int32 * n_layers)(*[int(w) for w in layer_window])
+        cfg.layer_window = C.cast(arr, C.POINTER(C.c_int32))
+        cfg._keep = arr
+    return cfg
 
 
 def make_tensor(data, dtype, rows, cols, n=1, scale=None) -> mbg_tensor:

@@ -150,6 +150,9 @@ int check_config(const mbg_config* c) {
     }
     if (c->page_size <= 0 || c->max_pos <= 0) return fail(MBG_E_INVALID_ARG, "config: page_size/max_pos");
     if (c->k_max < 1 || c->k_max > 4) return fail(MBG_E_UNSUPPORTED, "config: k_max %d (1..4)", c->k_max);
+    if (c->layer_window)
+        for (int l = 0; l < c->n_layers; ++l)
+            if (c->layer_window[l] < 0) return fail(MBG_E_INVALID_ARG, "config: layer_window[%d] = %d", l, c->layer_window[l]);
     if (!(c->rope_theta > 0.f) || !(c->rms_eps >= 0.f)) return fail(MBG_E_INVALID_ARG, "config: rope_theta/rms_eps");
     return MBG_OK;
 }
@@ -526,6 +529,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
         p.sg_scales = (const uint8_t*)L.sh_gate_up.scale;
         p.sd_codes = (const uint8_t*)L.sh_down.data;
         p.sd_scales = (const uint8_t*)L.sh_down.scale;
+        p.window = c.layer_window ? c.layer_window[l] : 0;
         per_step += 2 * ((int64_t)c.hidden * 2 + (int64_t)(c.n_q_heads + 2 * c.n_kv_heads) * c.head_dim * c.hidden +
                          (int64_t)c.hidden * c.n_q_heads * c.head_dim + 3 * (int64_t)c.ffn * c.hidden);
         if (moe) {  // router plus the top_k + shared experts a single token reads (codes and E8M0 scales)

@@ -81,6 +81,8 @@ struct LayerPtrs {
     const uint8_t* sg_scales;
     const uint8_t* sd_codes;   // shared experts down [S][H][M/2]
     const uint8_t* sd_scales;
+    int32_t window;            // attention window W (0: global): position p reads [p - W + 1, p]
+    int32_t pad_;
 };
 
 // Everything the persistent kernel reads, by value.

@@ -718,10 +718,15 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const int qh0 = g * S::GQ + (gg - g * HG) * GH;   // first query head of the task
     const int pos = cur_pos(), ncol = a->ncol, page_size = a->page_size;
     const int n_tok = pos + ncol;
+    // sliding-window layer: column c attends [max(0, pos + c - W + 1), pos + c];
+    // the splits cover [lo_al, n_tok), lo_al = column 0's first position
+    // rounded down to a workgroup token slot
+    const int W = ((CLayer*)a->layers + layer)->window;
+    const int lo_al = W > 0 ? max(0, pos - W + 1) / NS * NS : 0;
     // split length: a whole number of workgroup token slots, so that every
     // wave instruction's TPI positions start TPI-aligned and sit in one page
-    const int T = ((n_tok + S_ - 1) / S_ + NS - 1) / NS * NS;
-    const int t0 = s * T;
+    const int T = ((n_tok - lo_al + S_ - 1) / S_ + NS - 1) / NS * NS;
+    const int t0 = lo_al + s * T;
     const int t1 = min(t0 + T, n_tok);
     const int th = min(t1, pos);                    // history: [t0, th)
     const int tl = lane / LPT;                      // token of this lane within an instruction
@@ -802,6 +807,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const bool empty = t0 >= t1;
     for (int col = 0; col < ncol && !empty; ++col) {
         const int te = min(t1, pos + col + 1);
+        const int tlo = W > 0 ? pos + col - W + 1 : 0;   // this column's first position (may be < 0)
         float q[GH][EPC];
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
@@ -832,7 +838,8 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
                 const u32x4 vv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src + kUnitBytes);
                 K[u] = make_uint4(kv4.x, kv4.y, kv4.z, kv4.w);
                 V[u] = make_uint4(vv4.x, vv4.y, vv4.z, vv4.w);
-                valid[u] = tok_of(c * NUB + u) < th;
+                const int tk = tok_of(c * NUB + u);
+                valid[u] = tk < th && tk >= tlo;
             }
             st.template fold<NUB>(q, K, V, valid, ksc);
             if (c + NB < nch) {
@@ -844,7 +851,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         // positions written this step, up to this column's own
         if (has_new) {
             const uint4 K[1] = {Kn}, V[1] = {Vn};
-            const bool valid[1] = {tl < ncol && tn < te};
+            const bool valid[1] = {tl < ncol && tn < te && tn >= tlo};
             st.template fold<1>(q, K, V, valid, ksc);
         }
         if constexpr (KVF == F_FP8) {
@@ -930,9 +937,9 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     }
     __syncthreads();
     if (!s_last) return true;
-    // Combine: softmax over [0, pos + col] = weights exp2(m_s - M) on the
+    // Combine: softmax over the column's positions = weights exp2(m_s - M) on the
     // split partials, normalised by their weighted sum.
-    const int nsv = min(S_, (n_tok + T - 1) / T);   // splits that wrote partials
+    const int nsv = min(S_, (n_tok - lo_al + T - 1) / T);   // splits that wrote partials
     const int nch_ = ncol * GH;                      // (column, head) rows
     constexpr int HDV = HD / 4;                      // 16-byte vectors of o
     constexpr int RV = HDV + 1;                      // vectors of a partial row: o, then (m, l, pad)

@@ -154,7 +154,8 @@ class DeviceModel:
 
         self.mcfg = M.make_config(cfg.n_layers, H, cfg.n_q_heads, cfg.n_kv_heads, d, cfg.ffn, cfg.vocab,
                                   cfg.n_experts, cfg.top_k, cfg.n_shared, cfg.moe_ffn, cfg.rope_theta,
-                                  cfg.rms_eps, cfg.page_size, cfg.max_pos, self.k_max)
+                                  cfg.rms_eps, cfg.page_size, cfg.max_pos, self.k_max,
+                                  layer_window=list(cfg.layer_window) if cfg.layer_window else None)
         self.ws_bytes = M.mbg_workspace_size(self.mcfg)
         self.ws = torch.zeros(self.ws_bytes // 4 + 64, dtype=torch.int32, device=self.device)
         self.ctr_bytes = M.mbg_counter_bytes(self.mcfg)

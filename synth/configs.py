@@ -106,4 +106,10 @@ MOE = DecodeConfig(
 LONGCTX = DENSE2B.with_(name="longctx", kv_dtype="fp8", prefill=200000,
                         n_decode=64, shuffled_pages=True)
 
-CONFIGS = {c.name: c for c in (TINY, DENSE2B, LMHEAD, MOE, LONGCTX)}
+# The long-context workload with sliding-window layers: three of every four
+# layers attend over the last 2,048 positions, the fourth globally (the
+# Muse Spark Open article's model has 46 such layers of 62).
+LONGCTX_SWA = LONGCTX.with_(name="longctx_swa",
+                            layer_window=tuple(0 if li % 4 == 3 else 2048 for li in range(LONGCTX.n_layers)))
+
+CONFIGS = {c.name: c for c in (TINY, DENSE2B, LMHEAD, MOE, LONGCTX, LONGCTX_SWA)}

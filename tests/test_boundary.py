@@ -48,6 +48,9 @@ def test_validate_config_errors(M):
     assert M.mbg_validate(_cfg(M, ffn=0)) == M.MBG_E_UNSUPPORTED
     assert M.mbg_validate(_cfg(M, n_experts=8, top_k=9, moe_ffn=64)) == M.MBG_E_UNSUPPORTED
     assert M.mbg_validate(_cfg(M, n_experts=8, top_k=2, moe_ffn=48)) == M.MBG_E_UNSUPPORTED
+    assert M.mbg_validate(_cfg(M, layer_window=[0, 2048])) == 0
+    assert M.mbg_validate(_cfg(M, layer_window=[1, 0])) == 0
+    assert M.mbg_validate(_cfg(M, layer_window=[5, -1])) == M.MBG_E_INVALID_ARG
     M.mbg_validate(_cfg(M, head_dim=96))
     assert "head_dim 96" in M.mbg_last_error()
 
