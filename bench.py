@@ -115,6 +115,19 @@ def window_bytes(cfg, pos: int, k: int, n_distinct: float) -> int:
     return w + kv
 
 
+def batch_bytes(cfg, positions, n_distinct: float) -> int:
+    """Mean algorithmic bytes of a batch step whose columns sit at the given
+    positions (a list of per-step position lists): every weight once (routed
+    layers: the union of the columns' experts, n_distinct per layer on
+    average) plus each column's own KV."""
+    w, _ = algorithmic_bytes(cfg, 0)
+    if cfg.is_moe:
+        expert = 3 * cfg.moe_ffn * cfg.hidden * 17 // 32
+        w += int(round(cfg.n_layers * (n_distinct - cfg.top_k) * expert))
+    kv = [sum(algorithmic_bytes(cfg, p)[1] for p in ps) for ps in positions]
+    return int(w + sum(kv) / len(kv))
+
+
 def fp8_pow2_scales(cfg, device, block=1 << 16):
     """Per (layer, KV head, K or V) power-of-two scale 2^ceil(log2(amax / 448))
     over the float32 prefill draws."""
@@ -133,14 +146,23 @@ def fp8_pow2_scales(cfg, device, block=1 << 16):
     return sc
 
 
-def build_device_model(cfg, host, dev, k_max=1):
-    """The workload on the device: weights, prefilled KV cache, context."""
+def batch_prefill_lens(cfg, n_seqs):
+    """Prefill lengths of the batch sequences: sequence b holds
+    prefill * (1 - b / (2 n_seqs)) positions (sequence 0 the full prefill)."""
+    return [cfg.prefill - (b * cfg.prefill) // (2 * n_seqs) for b in range(n_seqs)]
+
+
+def build_device_model(cfg, host, dev, k_max=1, n_seqs=1):
+    """The workload on the device: weights, prefilled KV cache, context.
+    n_seqs > 1: that many sequences on disjoint pages of one pool, prefilled
+    to batch_prefill_lens."""
     import torch
 
     from memory_bound_gemv_amd import _mbg as M
     from memory_bound_gemv_amd.device_model import DeviceModel
     from synth import gen
-    pt = gen.page_table(cfg)
+    pt = gen.page_table(cfg) if n_seqs == 1 else gen.batch_page_table(cfg, n_seqs)
+    lens = batch_prefill_lens(cfg, n_seqs)
     if cfg.is_moe:
         E, S, H, Mf, V = cfg.n_experts, cfg.n_shared, cfg.hidden, cfg.moe_ffn, cfg.vocab
         u8 = dict(dtype=torch.uint8, device=dev)
@@ -169,13 +191,15 @@ def build_device_model(cfg, host, dev, k_max=1):
     for li in range(cfg.n_layers):
         if cfg.kv_dtype == "fp8":
             blk = 1 << 16
-            for p0 in range(0, cfg.prefill, blk):
-                n = min(blk, cfg.prefill - p0)
-                dm.kv_write(li, p0, gen.kv_prefill_f32_device(cfg, li, 0, p0, n, dev),
-                            gen.kv_prefill_f32_device(cfg, li, 1, p0, n, dev))
+            for b, T in enumerate(lens):
+                for p0 in range(0, T, blk):
+                    n = min(blk, T - p0)
+                    dm.kv_write(li, p0, gen.kv_prefill_f32_device(cfg, li, 0, p0, n, dev),
+                                gen.kv_prefill_f32_device(cfg, li, 1, p0, n, dev), seq=b)
         else:
             k, v = gen.kv_prefill_bf16(cfg, li)
-            dm.prefill_bf16(li, k, v)
+            for b, T in enumerate(lens):
+                dm.prefill_bf16(li, k[:T], v[:T], seq=b)
     dm.init()
     return dm
 
@@ -247,7 +271,8 @@ def run_decode(args, cfg):
     t_gen = time.perf_counter()
     host = gen.dense_weights(cfg)
     k_win = 4 if cfg.is_moe and not args.no_verify else 1
-    dm = build_device_model(cfg, host, dev, k_max=k_win)
+    n_batch = args.batch if cfg.kv_dtype == "bf16" else 1
+    dm = build_device_model(cfg, host, dev, k_max=max(k_win, n_batch), n_seqs=n_batch)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     info = dm.info()
@@ -383,6 +408,34 @@ def run_decode(args, cfg):
             "ms_per_window_mfma": round(ms_path[M.MBG_PATH_MFMA], 4),
         }
 
+    if n_batch > 1:
+        # n_batch independent sequences per step, each at its own position
+        # (sequence b from batch_prefill_lens(b), positions cycled over
+        # n_decode slots like the single-sequence steps)
+        lens = batch_prefill_lens(cfg, n_batch)
+        seqs = list(range(n_batch))
+        btok = torch.tensor([int(t) for t in gen.prompt_tokens(cfg, n_batch)], dtype=torch.int32, device=dev)
+        bam = torch.zeros(n_batch, dtype=torch.int32, device=dev)
+        bpos = lambda i: [L + (i % n_slots) for L in lens]
+        for i in range(max(3, args.warmup // 4)):
+            dm.batch(btok, seqs, bpos(i), None, bam)
+        ms_b = timed(stream, lambda i: dm.batch(btok, seqs, bpos(i), None, bam), max(8, args.steps // 4))
+        if dm.status() != 0:
+            raise RuntimeError("device status after the batch steps")
+        nd = 1.0
+        if cfg.is_moe:
+            dm.batch(btok, seqs, bpos(0), None, bam)
+            nd = float(np.mean([len(np.unique(dm.routing(li)[0][:n_batch])) for li in range(cfg.n_layers)]))
+        bb = batch_bytes(cfg, [bpos(i) for i in range(n_slots)], nd)
+        out["batch"] = {
+            "n": n_batch, "prefill_lens": lens, "ms_per_step": round(ms_b, 4),
+            "tokens_s": round(n_batch * 1e3 / ms_b, 1),
+            "tokens_s_over_batch1": round(n_batch * 1e3 / ms_b / out["value"], 3),
+            "distinct_experts_per_layer": round(nd, 2) if cfg.is_moe else None,
+            "bytes_per_step": bb, "achieved_GBs": round(bb / (ms_b / 1e3) / 1e9, 1),
+            "frac": round(bb / (ms_b / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+        }
+
     if args.trace:
         from memory_bound_gemv_amd import _mbg as M
         M.mbg_set_trace(dm.ctx, True)
@@ -470,6 +523,8 @@ def main():
                          "LM-head GEMV alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="moe: skip the 4-token verify-window timing")
+    ap.add_argument("--batch", type=int, default=4,
+                    help="also time steps of this many independent sequences (BF16-KV workloads; 1: skip)")
     ap.add_argument("--multi-step", type=int, default=8,
                     help="steps per launch of the headline timing (1: single-step launches only); "
                          "single-step launches are timed beside it")

@@ -108,8 +108,11 @@ typedef struct {
  *     [n_layers][n_pages][2 (K, V)][n_kv_heads][page_size][head_dim]
  * elements of `dtype` (MBG_BF16 or MBG_FP8_E4M3).  Position t of a layer
  * lives in physical page page_table[t / page_size], slot t % page_size.
- * page_table (device int32 [ceil(max_pos / page_size)]) maps logical to
- * physical pages; the identity table is a contiguous cache.  scales (device
+ * page_table (device int32 [n_seqs][ceil(max_pos / page_size)]) maps
+ * logical to physical pages, one row per sequence (n_seqs 0 counts as 1);
+ * the identity table is a contiguous cache.  Sequence 0 is the one that
+ * mbg_decode_step/_steps/_verify extend; mbg_decode_batch names the rows it
+ * uses.  Rows must not share a physical page that either writes.  scales (device
  * float [n_layers][n_kv_heads][2], FP8 only, NULL for BF16) give
  * value = decode(code) * scale per (layer, KV head, K or V).  Paged FP8 KV
  * with a per-head scale is what the wmrh.cn Kimi-K3 long-context report
@@ -122,6 +125,7 @@ typedef struct {
     void *pool;
     const int32_t *page_table;
     const float *scales;
+    int32_t n_seqs;   /* page-table rows (sequences sharing the pool); 0 or 1: one */
 } mbg_kv;
 
 typedef struct {
@@ -246,6 +250,22 @@ int mbg_decode_step(mbg_ctx *ctx, const int32_t *d_token, int32_t pos,
 int mbg_decode_verify(mbg_ctx *ctx, const int32_t *d_tokens, int32_t k, int32_t pos,
                       float *d_logits, int32_t *d_argmax);
 
+/* Batch of n independent sequences (1 <= n <= k_max) in one launch: column
+ * i decodes token d_tokens[i] of sequence seq[i] (a page-table row, host
+ * int32 [n], all distinct, each in [0, n_seqs)) at position pos[i] (host
+ * int32 [n], each in [0, max_pos)): it writes its K/V at pos[i] in its own
+ * pages and attends [0, pos[i]] of its own cache only (its window in a
+ * sliding-window layer).  Each weight byte is read once for all n columns,
+ * as in a verify window; routed layers read the union of the columns'
+ * experts.  The "Muse Spark Open" article (section on what would change the
+ * result, first item) names batch > 1 as the next step: more tokens in
+ * flight give a throughput figure a serving team can use.  Writes logits
+ * [n][vocab] (may be NULL) and argmax [n].  Errors: MBG_E_RANGE for n, a
+ * sequence or a position out of range; MBG_E_INVALID_ARG for NULL pointers
+ * or a repeated sequence; otherwise as mbg_decode_step. */
+int mbg_decode_batch(mbg_ctx *ctx, const int32_t *d_tokens, int32_t n, const int32_t *seq,
+                     const int32_t *pos, float *d_logits, int32_t *d_argmax);
+
 /* n_steps greedy decode steps (1 .. 4096) in ONE kernel launch: step s runs
  * at pos + s; step 0 reads its token at d_token[0], step s > 0 takes the
  * argmax of step s - 1 on the device, and the persistent kernel moves from
@@ -290,7 +310,7 @@ int mbg_query(const mbg_ctx *ctx, mbg_info *info);
  * us <= 0. */
 int mbg_set_timeout_us(mbg_ctx *ctx, int64_t us);
 
-/* How verify windows (k >= 2 columns) run the routed experts' gate/up
+/* How verify windows and batches (k >= 2 columns) run the routed experts' gate/up
  * rows: MBG_PATH_FMA multiplies every weight with each column on the vector
  * ALU (k multiply-adds per weight); MBG_PATH_MFMA decodes 16 rows at a time
  * to BF16 and runs v_mfma_f32_16x16x32_bf16 against the columns split into

@@ -53,7 +53,7 @@ class mbg_weights(C.Structure):
 
 class mbg_kv(C.Structure):
     _fields_ = [("dtype", C.c_int32), ("n_pages", C.c_int32), ("pool", C.c_void_p),
-                ("page_table", C.c_void_p), ("scales", C.c_void_p)]
+                ("page_table", C.c_void_p), ("scales", C.c_void_p), ("n_seqs", C.c_int32)]
 
 
 class mbg_config(C.Structure):
@@ -93,6 +93,8 @@ def _load():
         "mbg_decode_step": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
         "mbg_decode_verify": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
         "mbg_decode_steps": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
+        "mbg_decode_batch": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
+                                       C.c_void_p, C.c_void_p]),
         "mbg_get_status": (C.c_int, [CTX_P]),
         "mbg_query": (C.c_int, [CTX_P, C.POINTER(mbg_info)]),
         "mbg_set_timeout_us": (C.c_int, [CTX_P, C.c_int64]),
@@ -121,7 +123,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("mbg_workspace_size", "mbg_counter_bytes", "mbg_validate", "mbg_decode_init", "mbg_decode_step",
-            "mbg_decode_verify", "mbg_decode_steps",
+            "mbg_decode_verify", "mbg_decode_steps", "mbg_decode_batch",
             "mbg_get_status", "mbg_query", "mbg_set_timeout_us", "mbg_set_verify_path", "mbg_set_trace",
             "mbg_read_trace",
             "mbg_read_routing", "mbg_last_error", "mbg_destroy",
@@ -183,10 +185,10 @@ def make_layer(**tensors) -> mbg_layer:
     return lay
 
 
-def make_kv(dtype, n_pages, pool, page_table, scales=None) -> mbg_kv:
+def make_kv(dtype, n_pages, pool, page_table, scales=None, n_seqs=1) -> mbg_kv:
     if isinstance(dtype, str):
         dtype = DTYPES[dtype]
-    return mbg_kv(dtype, n_pages, _ptr(pool), _ptr(page_table), _ptr(scales))
+    return mbg_kv(dtype, n_pages, _ptr(pool), _ptr(page_table), _ptr(scales), n_seqs)
 
 
 # --------------------------------------------------------------------------- the C-ABI, same names
@@ -232,6 +234,13 @@ def mbg_decode_verify(ctx, tokens, k: int, pos: int, logits, argmax) -> None:
 
 def mbg_decode_steps(ctx, token, n_steps: int, pos: int, logits, argmax) -> None:
     _check(_lib.mbg_decode_steps(ctx, _ptr(token), n_steps, pos, _ptr(logits), _ptr(argmax)))
+
+
+def mbg_decode_batch(ctx, tokens, n: int, seq, pos, logits, argmax) -> None:
+    """seq, pos: host sequences of n ints (page-table rows, positions)."""
+    sq = (C.c_int32 * n)(*[int(v) for v in seq])
+    ps = (C.c_int32 * n)(*[int(v) for v in pos])
+    _check(_lib.mbg_decode_batch(ctx, _ptr(tokens), n, sq, ps, _ptr(logits), _ptr(argmax)))
 
 
 def mbg_get_status(ctx) -> int:

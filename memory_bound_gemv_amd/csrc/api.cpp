@@ -211,6 +211,7 @@ struct mbg_ctx {
     int n_tasks;
     int trace_on;
     int last_ncol;   // columns of the last step/verify call (0: none yet)
+    int n_seqs;      // page-table rows (sequences)
     void* uc;        // the caller's uncached counter block
     size_t uc_bytes;
     void* ws_zero;   // start of the workspace region that starts at zero (argmax keys, head counters)
@@ -248,6 +249,7 @@ int mbg_validate(const mbg_config* c, const mbg_weights* w, const mbg_kv* kv) {
             return fail(MBG_E_UNSUPPORTED, "kv: dtype %d (BF16 or FP8 E4M3)", kv->dtype);
         if (!kv->pool || !kv->page_table) return fail(MBG_E_INVALID_ARG, "kv: pool/page_table is NULL");
         if (kv->n_pages <= 0) return fail(MBG_E_INVALID_ARG, "kv: n_pages %d", kv->n_pages);
+        if (kv->n_seqs < 0) return fail(MBG_E_INVALID_ARG, "kv: n_seqs %d", kv->n_seqs);
         if (kv->dtype == MBG_FP8_E4M3 && !kv->scales)
             return fail(MBG_E_DTYPE_MISMATCH, "kv: FP8 cache without per-head scales");
         if (kv->dtype == MBG_BF16 && kv->scales)
@@ -323,18 +325,20 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     HIP_TRY(hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev));
     if (!coop) return fail(MBG_E_UNSUPPORTED, "device does not support cooperative launches");
 
-    // page table entries must address the pool
+    // page table entries (every sequence's row) must address the pool
     const int n_lpages = (c.max_pos + c.page_size - 1) / c.page_size;
+    const int n_seqs = std::max(1, (int)kv->n_seqs);
     {
-        std::vector<int32_t> pt(n_lpages);
-        HIP_TRY(hipMemcpy(pt.data(), kv->page_table, sizeof(int32_t) * n_lpages, hipMemcpyDeviceToHost));
-        for (int i = 0; i < n_lpages; ++i)
+        std::vector<int32_t> pt((size_t)n_seqs * n_lpages);
+        HIP_TRY(hipMemcpy(pt.data(), kv->page_table, sizeof(int32_t) * pt.size(), hipMemcpyDeviceToHost));
+        for (size_t i = 0; i < pt.size(); ++i)
             if (pt[i] < 0 || pt[i] >= kv->n_pages)
-                return fail(MBG_E_RANGE, "page_table[%d] = %d outside [0, %d)", i, pt[i], kv->n_pages);
+                return fail(MBG_E_RANGE, "page_table[%zu] = %d outside [0, %d)", i, pt[i], kv->n_pages);
     }
 
     mbg_ctx* x = new mbg_ctx();
     x->cfg = c;
+    x->cfg.layer_window = nullptr;   // the caller's array is read during init only
     x->stream = s;
     x->epoch = 0;
     x->wall_khz = wall_khz;
@@ -585,6 +589,9 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.page_table = kv->page_table;
     a.kv_scales = kv->scales;
     a.kv_layer_stride = (int64_t)kv->n_pages * 2 * c.n_kv_heads * c.page_size * c.head_dim;
+    a.pt_stride = n_lpages;
+    a.batch = 0;
+    x->n_seqs = n_seqs;
 
     hipError_t e = launch_fill_u32((uint32_t*)base, plan.zero_bytes / 4, 0u, s);
     if (e == hipSuccess) e = launch_fill_u32((uint32_t*)uc, plan.uc_bytes / 4, 0u, s);
@@ -605,14 +612,21 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     return MBG_OK;
 }
 
+// Columns of a batch of independent sequences (mbg_decode_batch).
+struct BatchCols {
+    int n = 0;
+    int32_t seq[4] = {0, 0, 0, 0};
+    int32_t pos[4] = {0, 0, 0, 0};
+};
+
 static int launch_step(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t pos, float* d_logits,
-                       int32_t* d_argmax, int32_t nsteps = 1) {
+                       int32_t* d_argmax, int32_t nsteps = 1, const BatchCols* batch = nullptr) {
     if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
     if (!d_tokens || !d_argmax) return fail(MBG_E_INVALID_ARG, "tokens/argmax is NULL");
     if (k < 1 || k > x->cfg.k_max) return fail(MBG_E_RANGE, "k %d outside [1, %d]", k, x->cfg.k_max);
     if (nsteps < 1 || nsteps > kMaxStepsPerLaunch)
         return fail(MBG_E_RANGE, "n_steps %d outside [1, %d]", nsteps, kMaxStepsPerLaunch);
-    const int64_t span = (int64_t)k + nsteps - 1;
+    const int64_t span = batch ? 1 : (int64_t)k + nsteps - 1;   // a batch's positions were checked per column
     if (pos < 0 || (int64_t)pos + span > x->cfg.max_pos)
         return fail(MBG_E_RANGE, "positions %d..%lld outside [0, %d)", pos, (long long)(pos + span - 1),
                     x->cfg.max_pos);
@@ -623,6 +637,13 @@ static int launch_step(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t p
     a.pos = pos;
     a.ncol = k;
     a.nsteps = nsteps;
+    if (batch) {
+        a.batch = 1;
+        for (int i = 0; i < 4; ++i) {
+            a.bseq[i] = i < batch->n ? batch->seq[i] : 0;
+            a.bpos[i] = i < batch->n ? batch->pos[i] : 0;
+        }
+    }
     a.epoch = x->epoch + 1;
     x->epoch += (uint32_t)nsteps;
     a.deadline_ticks = (uint64_t)x->timeout_us * (uint64_t)x->wall_khz / 1000ull;
@@ -647,6 +668,26 @@ int mbg_decode_verify(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t po
 int mbg_decode_steps(mbg_ctx* x, const int32_t* d_token, int32_t n_steps, int32_t pos, float* d_logits,
                      int32_t* d_argmax) {
     return launch_step(x, d_token, 1, pos, d_logits, d_argmax, n_steps);
+}
+
+int mbg_decode_batch(mbg_ctx* x, const int32_t* d_tokens, int32_t n, const int32_t* seq, const int32_t* pos,
+                     float* d_logits, int32_t* d_argmax) {
+    if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
+    if (!seq || !pos) return fail(MBG_E_INVALID_ARG, "seq/pos is NULL");
+    if (n < 1 || n > x->cfg.k_max) return fail(MBG_E_RANGE, "n %d outside [1, %d]", n, x->cfg.k_max);
+    BatchCols b;
+    for (int i = 0; i < n; ++i) {
+        if (seq[i] < 0 || seq[i] >= x->n_seqs)
+            return fail(MBG_E_RANGE, "seq[%d] = %d outside [0, %d)", i, seq[i], x->n_seqs);
+        if (pos[i] < 0 || pos[i] >= x->cfg.max_pos)
+            return fail(MBG_E_RANGE, "pos[%d] = %d outside [0, %d)", i, pos[i], x->cfg.max_pos);
+        for (int j = 0; j < i; ++j)
+            if (seq[j] == seq[i]) return fail(MBG_E_INVALID_ARG, "sequence %d appears twice", seq[i]);
+        b.seq[i] = seq[i];
+        b.pos[i] = pos[i];
+    }
+    b.n = n;
+    return launch_step(x, d_tokens, n, pos[0], d_logits, d_argmax, 1, &b);
 }
 
 int mbg_get_status(mbg_ctx* x) {

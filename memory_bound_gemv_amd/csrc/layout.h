@@ -115,9 +115,16 @@ struct StepArgs {
     // KV cache
     int32_t kv_dtype;
     void* kv_pool;
-    const int32_t* page_table;
+    const int32_t* page_table;  // [n_seqs][pt_stride]
     const float* kv_scales;
     int64_t kv_layer_stride;  // elements per layer = n_pages * 2 * Hkv * page * d
+    int32_t pt_stride;        // page-table entries per sequence
+    // batch of independent sequences (batch != 0): column c runs at position
+    // bpos[c] of page-table row bseq[c]; otherwise column c runs at pos + c
+    // of row 0 (one sequence: a step or a verify window)
+    int32_t batch;
+    int32_t bpos[4];
+    int32_t bseq[4];
     // workspace
     const Task* tasks;
     const uint32_t* task_off;  // [grid + 1]

@@ -60,12 +60,27 @@ __shared__ uint64_t s_twait;  // trace: when the current task's wait was satisfi
 
 // The step a workgroup is running within a launch of several greedy steps:
 // its epoch (the launch epoch plus the step index) and position.
-__shared__ uint32_t s_ep;
-__shared__ int32_t s_pos, s_step;
-__device__ __forceinline__ uint32_t cur_epoch() { return __builtin_amdgcn_readfirstlane(s_ep); }
-__device__ __forceinline__ int cur_pos() { return __builtin_amdgcn_readfirstlane(s_pos); }
-__device__ __forceinline__ int cur_step() { return __builtin_amdgcn_readfirstlane(s_step); }
-__device__ __forceinline__ uint32_t token_ctr_index(CArgs* a) { return (uint32_t)a->n_layers * PH_COUNT; }
+// One step's view of the launch: the argument block (a->field reads it)
+// plus the step this pass runs - its counter epoch, its first position and
+// its index within the launch.  The ops take it by value, so the three stay
+// in scalar registers (read from LDS at every wait they cost ~1 us per
+// layer on the dense 2B step).
+struct Ctx {
+    CArgs* args;
+    uint32_t epoch;   // counter epoch of this step (launch epoch + step)
+    int32_t pos;      // position of column 0
+    int32_t step;     // index of the step within the launch
+    __device__ __forceinline__ CArgs* operator->() const { return args; }
+};
+// Position of column c and the page-table row it uses: consecutive
+// positions of sequence 0 (a step or a verify window) or, in a batch of
+// independent sequences, the column's own position and row.
+__device__ __forceinline__ int col_pos(Ctx a, int c) { return a->batch ? a->bpos[c] : a.pos + c; }
+__device__ __forceinline__ const MBG_CONST int32_t* col_ptab(Ctx a, int c) {
+    const MBG_CONST int32_t* p = (const MBG_CONST int32_t*)a->page_table;
+    return a->batch ? p + (size_t)a->bseq[c] * a->pt_stride : p;
+}
+__device__ __forceinline__ uint32_t token_ctr_index(Ctx a) { return (uint32_t)a->n_layers * PH_COUNT; }
 
 // Cross-workgroup data (residual stream, q, new K/V, attention partials and
 // output, FFN hidden) is written and read with device-coherent accesses
@@ -153,7 +168,7 @@ __device__ __forceinline__ void sload_counter(const uint32_t* lines, const uint3
 // Wait until counter `idx` (the sum of its kCtrLines lines) reaches
 // epoch * need (mod 2^32).  Wave 0 polls; the other waves wait at the
 // barrier.  Returns false when the launch is aborting.
-__device__ __forceinline__ bool wait_until(CArgs* a, uint32_t idx, uint32_t target) {
+__device__ __forceinline__ bool wait_until(Ctx a, uint32_t idx, uint32_t target) {
     __shared__ int s_ok;
     if (threadIdx.x < kWave) {
         const int lane = threadIdx.x;
@@ -186,13 +201,13 @@ __device__ __forceinline__ bool wait_until(CArgs* a, uint32_t idx, uint32_t targ
     return s_ok != 0;
 }
 
-__device__ __forceinline__ bool wait_counter(CArgs* a, uint32_t idx, uint32_t need) {
-    return wait_until(a, idx, cur_epoch() * need);
+__device__ __forceinline__ bool wait_counter(Ctx a, uint32_t idx, uint32_t need) {
+    return wait_until(a, idx, a.epoch * need);
 }
 
 // Make this workgroup's stores visible at device scope, then count the task
 // on this workgroup's line of the counter.
-__device__ __forceinline__ void release_counter(CArgs* a, uint32_t idx) {
+__device__ __forceinline__ void release_counter(Ctx a, uint32_t idx) {
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));  // vmcnt(0): this wave's stores have completed
     __syncthreads();
     if (threadIdx.x == 0) {
@@ -203,10 +218,10 @@ __device__ __forceinline__ void release_counter(CArgs* a, uint32_t idx) {
 
 // Token id of column c, clamped into [0, vocab); a clamp raises the range
 // flag (reported by mbg_get_status) and the step completes normally.
-__device__ __forceinline__ int token_of(CArgs* a, int c) {
+__device__ __forceinline__ int token_of(Ctx a, int c) {
     // the first step reads the caller's token; a later step of the same
     // launch reads the previous step's argmax (written this launch)
-    const int st = cur_step();
+    const int st = a.step;
     int t = st == 0 ? gp(a->tokens)[c]
                     : (int)__hip_atomic_load(gp(a->argmax) + (size_t)(st - 1) * a->ncol + c, __ATOMIC_RELAXED,
                                              __HIP_MEMORY_SCOPE_AGENT);
@@ -222,7 +237,7 @@ __device__ __forceinline__ int token_of(CArgs* a, int c) {
 // squares in a fixed order (per thread over its quads, then the wave tree,
 // then the four waves in order).
 template <int NC, int H, class Src4>
-__device__ __forceinline__ void load_normed(CArgs* a, Src4 src4, const uint16_t* gain, lds_f32* xs) {
+__device__ __forceinline__ void load_normed(Ctx a, Src4 src4, const uint16_t* gain, lds_f32* xs) {
     __shared__ float red[kWaves * 4];
     static_assert(H % 4 == 0, "hidden size");
     constexpr int NV = H / 4;
@@ -299,7 +314,7 @@ __device__ __forceinline__ void load_plain(const float* src, lds_f32* xs) {
 // multiple of 256), copied by wave 0 alone with device-coherent LDS DMA:
 // wave 0 is the polling wave and has no weight loads in flight, so the copy
 // does not queue behind the other waves' prefetch.  Ends with a barrier.
-__device__ __forceinline__ void dma_input(CArgs* a, const float* src, int n, lds_f32* xs) {
+__device__ __forceinline__ void dma_input(Ctx a, const float* src, int n, lds_f32* xs) {
     if (!a->wave0_input) {   // every wave copies its share through registers
         const rsrc_t r = make_rsrc(src);
         for (int j = threadIdx.x; j < n / 4; j += kThreads)
@@ -318,7 +333,7 @@ __device__ __forceinline__ void dma_input(CArgs* a, const float* src, int n, lds
 // xs[c][i] (already in LDS) *= 1 / sqrt(mean_i xs[c][i]^2 + eps) * gain[i]:
 // the same per-thread quads and reduction order as load_normed.
 template <int NC, int H>
-__device__ __forceinline__ void norm_in_place(CArgs* a, const uint16_t* gain, lds_f32* xs) {
+__device__ __forceinline__ void norm_in_place(Ctx a, const uint16_t* gain, lds_f32* xs) {
     __shared__ float red[kWaves * 4];
     constexpr int NV = H / 4;
     constexpr int PER = (NV + kThreads - 1) / kThreads;
@@ -386,7 +401,7 @@ __device__ __forceinline__ int gemv_pre_rows(int kib) {
     return (kib * 1024 + RS::kRowBytes - 1) / RS::kRowBytes;
 }
 template <class RS>
-__device__ __forceinline__ int gemv_pre_rows(CArgs* a) {
+__device__ __forceinline__ int gemv_pre_rows(Ctx a) {
     return gemv_pre_rows<RS>(a->gemv_pre);
 }
 
@@ -422,7 +437,7 @@ struct ResidPre {
 // ------------------------------------------------------------------ QKV
 
 template <int NC, class S>
-__device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+__device__ __forceinline__ bool op_qkv(Ctx a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                     lds_f32* xs) {
     constexpr int HD = S::HD, HALF = HD / 2, H = S::H;
     const int lane = lane_id();
@@ -466,7 +481,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
             const int pu = idx / NC, c = idx - pu * NC;
             const int u = gw + nw * pu;
             const int hh = u / HALF;
-            if (hh < Hq + Hkv) cs_pre[it] = rcs[(size_t)(cur_pos() + c) * HALF + (u - hh * HALF)];
+            if (hh < Hq + Hkv) cs_pre[it] = rcs[(size_t)col_pos(a, c) * HALF + (u - hh * HALF)];
             if (S::KVF == F_FP8 && hh >= Hq) {
                 const int kv = hh < Hq + Hkv ? 0 : 1;
                 const int gh = kv == 0 ? hh - Hq : hh - Hq - Hkv;
@@ -474,11 +489,10 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
             }
         }
     }
-    // the pages of the window's positions (scalar loads)
-    const MBG_CONST int32_t* ptab_s = (const MBG_CONST int32_t*)a->page_table;
+    // the pages of the columns' positions (scalar loads)
     int page_c[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) page_c[c] = ptab_s[(cur_pos() + c) / a->page_size];
+    for (int c = 0; c < NC; ++c) page_c[c] = col_ptab(a, c)[col_pos(a, c) / a->page_size];
     if (!wait_counter(a, wctr, wneed)) return false;
     if (layer == 0) {
         int tok[NC];
@@ -515,7 +529,7 @@ __device__ __forceinline__ bool op_qkv(CArgs* a, uint32_t layer, uint32_t tile, 
         const int u = gw + nw * pu;
         const int hh = u / HALF;
         const int i = u - hh * HALF;
-        const int p = cur_pos() + c;
+        const int p = col_pos(a, c);
         if (hh < Hq + Hkv) {
             const float cs = cs_pre[it][0], sn = cs_pre[it][1];
             const float y0 = x0 * cs - x1 * sn;
@@ -692,7 +706,7 @@ __device__ __forceinline__ void wait_chunks(int k) {
 // wave's LDS ring (global_load_lds_dwordx4); up to kAttnBufs chunks are
 // requested before the task waits for this step's q and new K/V.
 template <int NC, class S>
-__device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+__device__ __forceinline__ bool op_attn(Ctx a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                         lds_f32* smem) {
     constexpr int HD = S::HD, KVF = S::KVF;
     constexpr int GH = attn_heads(S::GQ);    // query heads per task
@@ -716,30 +730,43 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const int s = (int)tile - gg * S_;
     const int g = gg / HG;
     const int qh0 = g * S::GQ + (gg - g * HG) * GH;   // first query head of the task
-    const int pos = cur_pos(), ncol = a->ncol, page_size = a->page_size;
-    const int n_tok = pos + ncol;
-    // sliding-window layer: column c attends [max(0, pos + c - W + 1), pos + c];
-    // the splits cover [lo_al, n_tok), lo_al = column 0's first position
-    // rounded down to a workgroup token slot
+    const int pos = a.pos, ncol = a->ncol, page_size = a->page_size;
+    // One sequence: column c at pos + c shares the history [0, pos) and sees
+    // the window's earlier tokens.  A batch: column c at bpos[c] of its own
+    // sequence sees [0, bpos[c]] of that sequence only; the splits then
+    // cover the widest column and each column streams its own history.
+    const bool batch = a->batch != 0;
+    int pmin = pos, pmax = pos + ncol - 1;
+    if (batch) {
+        pmin = pmax = a->bpos[0];
+        for (int c = 1; c < ncol; ++c) {
+            pmin = min(pmin, (int)a->bpos[c]);
+            pmax = max(pmax, (int)a->bpos[c]);
+        }
+    }
+    const int n_tok = pmax + 1;
+    // sliding-window layer: a column at p attends [max(0, p - W + 1), p];
+    // the splits cover [lo_al, n_tok), lo_al = the lowest column's first
+    // position rounded down to a workgroup token slot
     const int W = ((CLayer*)a->layers + layer)->window;
-    const int lo_al = W > 0 ? max(0, pos - W + 1) / NS * NS : 0;
+    const int lo_al = W > 0 ? max(0, pmin - W + 1) / NS * NS : 0;
     // split length: a whole number of workgroup token slots, so that every
     // wave instruction's TPI positions start TPI-aligned and sit in one page
     const int T = ((n_tok - lo_al + S_ - 1) / S_ + NS - 1) / NS * NS;
     const int t0 = lo_al + s * T;
     const int t1 = min(t0 + T, n_tok);
-    const int th = min(t1, pos);                    // history: [t0, th)
+    int th = min(t1, batch ? (int)a->bpos[0] : pos);   // history of column 0: [t0, th)
     const int tl = lane / LPT;                      // token of this lane within an instruction
     const int cidx = lane % LPT;                    // 16-byte slice of the row
-    const int nu = th > t0 ? (th - t0 + NS - 1) / NS : 0;   // units per wave
-    const int nch = (nu + NUB - 1) / NUB;
-    const bool resident = nch <= NB;                // whole history stays in LDS
+    int nu = th > t0 ? (th - t0 + NS - 1) / NS : 0;   // units per wave
+    int nch = (nu + NUB - 1) / NUB;
+    const bool resident = !batch && nch <= NB;      // whole (shared) history stays in LDS
     const size_t layer_off = (size_t)layer * a->kv_layer_stride;
     const MBG_GLOBAL uint8_t* pool = gp(reinterpret_cast<const uint8_t*>(a->kv_pool));
     MBG_LDS uint8_t* ring = reinterpret_cast<MBG_LDS uint8_t*>(smem) + wave * kAttnWaveBytes;
 
     auto tok_of = [&](int i) { return t0 + (i * kWaves + wave) * TPI + tl; };
-    const MBG_CONST int32_t* ptab_s = (const MBG_CONST int32_t*)a->page_table;
+    const MBG_CONST int32_t* ptab_s = col_ptab(a, 0);   // the streamed column's page table
     const size_t lane_off = (size_t)tl * HD * EB + (size_t)cidx * 16;
     // Request chunk c of history into ring buffer b: NUB units, each one K and
     // one V instruction.  A unit's TPI positions share a page, so its page is
@@ -757,7 +784,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
             const size_t vstep = (size_t)Hkv * page_size * HD * EB;   // K -> V of the same page
             const MBG_GLOBAL uint8_t* kp = pool + el * EB + lane_off;
             MBG_LDS uint8_t* dst = ring + (b * NUB + u) * 2 * kUnitBytes;
-            if (tb + TPI > a->pos) {   // rows this launch writes (an earlier step's K/V): coherent loads
+            if (!batch && tb + TPI > a->pos) {   // rows this launch writes (an earlier step's K/V): coherent loads
                 lds_dma16_coh(kp, (MBG_LDS void*)dst);
                 lds_dma16_coh(kp + vstep, (MBG_LDS void*)(dst + kUnitBytes));
             } else {
@@ -767,7 +794,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         }
     };
 
-    const int npre = min(nch, NB);
+    int npre = min(nch, NB);
     // the polling wave (0) may hold its loads back until its wait is over
     const int early = (wave != 0 || a->poll_wave_prefetch) ? min(npre, a->attn_pre) : 0;
     for (int c = 0; c < early; ++c) issue_chunk(c, c);
@@ -775,7 +802,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     // positions this step writes, the FP8 scales
     int page_new[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) page_new[c] = ptab_s[(pos + c) / page_size];
+    for (int c = 0; c < NC; ++c) page_new[c] = col_ptab(a, c)[col_pos(a, c) / page_size];
     const MBG_CONST float* kvs = (const MBG_CONST float*)a->kv_scales;
     const float ksc = KVF == F_FP8 ? kvs[((size_t)layer * Hkv + g) * 2 + 0] : 1.f;
     const float vsc = KVF == F_FP8 ? kvs[((size_t)layer * Hkv + g) * 2 + 1] : 1.f;
@@ -783,14 +810,17 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     for (int c = early; c < npre; ++c) issue_chunk(c, c);
     // the positions written this step (at most ncol of them, folded by wave 0
     // after the history): requested now, read coherently
-    const bool has_new = wave == 0 && t1 > pos;   // wave-uniform
-    const int tn = max(t0, pos) + tl;             // this lane's position
+    // (one sequence: lane group tl holds position max(t0, pos) + tl; a batch:
+    // lane group tl holds column tl's own new position)
+    const bool has_new = wave == 0 && (batch || t1 > pos);   // wave-uniform
+    const int tn = batch ? (tl < ncol ? (int)a->bpos[tl] : -1) : max(t0, pos) + tl;   // this lane's position
+    const bool ld_new = has_new && tl < ncol && tn >= t0 && tn < t1;
     uint4 Kn = make_uint4(0, 0, 0, 0), Vn = make_uint4(0, 0, 0, 0);
-    if (has_new && tl < ncol && tn < t1) {
+    if (ld_new) {
         int page = page_new[0];
 #pragma unroll
         for (int c = 1; c < NC; ++c)
-            if (tn - pos == c) page = page_new[c];
+            if ((batch ? tl : tn - pos) == c) page = page_new[c];
         const size_t el =
             layer_off + ((((size_t)page * 2) * Hkv + g) * page_size + (tn - (tn / page_size) * page_size)) * HD;
         const MBG_GLOBAL uint8_t* kp = pool + el * EB + (size_t)cidx * 16;
@@ -806,8 +836,9 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
     const bool local = KVF == F_BF16 && a->attn_local != 0;
     const bool empty = t0 >= t1;
     for (int col = 0; col < ncol && !empty; ++col) {
-        const int te = min(t1, pos + col + 1);
-        const int tlo = W > 0 ? pos + col - W + 1 : 0;   // this column's first position (may be < 0)
+        const int pc = batch ? (int)a->bpos[col] : pos + col;   // this column's position
+        const int te = min(t1, pc + 1);
+        const int tlo = W > 0 ? pc - W + 1 : 0;   // this column's first position (may be < 0)
         float q[GH][EPC];
 #pragma unroll
         for (int h = 0; h < GH; ++h) {
@@ -823,6 +854,13 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         Lane st;
         st.init();
         if (col > 0 && !resident) {  // stream the history again for this column
+            if (batch) {   // its own sequence's history and pages
+                th = min(t1, pc);
+                ptab_s = col_ptab(a, col);
+                nu = th > t0 ? (th - t0 + NS - 1) / NS : 0;
+                nch = (nu + NUB - 1) / NUB;
+                npre = min(nch, NB);
+            }
             __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // earlier ring reads are done
             for (int c = 0; c < npre; ++c) issue_chunk(c, c);
         }
@@ -851,7 +889,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         // positions written this step, up to this column's own
         if (has_new) {
             const uint4 K[1] = {Kn}, V[1] = {Vn};
-            const bool valid[1] = {tl < ncol && tn < te && tn >= tlo};
+            const bool valid[1] = {batch ? ld_new && tl == col : tl < ncol && tn < te && tn >= tlo};
             st.template fold<1>(q, K, V, valid, ksc);
         }
         if constexpr (KVF == F_FP8) {
@@ -933,7 +971,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
         else
             old = __hip_atomic_fetch_add(gp(a->head_ctr) + ((size_t)layer * Hkv * HG + gg) * kLineU32, 1u,
                                          __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old + 1u == cur_epoch() * (uint32_t)S_);
+        s_last = (old + 1u == a.epoch * (uint32_t)S_);
     }
     __syncthreads();
     if (!s_last) return true;
@@ -1043,7 +1081,7 @@ __device__ __forceinline__ bool op_attn(CArgs* a, uint32_t layer, uint32_t tile,
 // --------------------------------------------------- plain row GEMVs
 
 template <int NC, class S>
-__device__ __forceinline__ bool op_oproj(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+__device__ __forceinline__ bool op_oproj(Ctx a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                       lds_f32* xs) {
     constexpr int H = S::H, K = S::QD;
     const int lane = lane_id(), wave = wave_id();
@@ -1098,7 +1136,7 @@ __device__ __forceinline__ bool op_oproj(CArgs* a, uint32_t layer, uint32_t tile
 }
 
 template <int NC, class S>
-__device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+__device__ __forceinline__ bool op_gateup(Ctx a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                        lds_f32* xs) {
     constexpr int H = S::H, F = S::F;
     const int lane = lane_id(), wave = wave_id();
@@ -1147,7 +1185,7 @@ __device__ __forceinline__ bool op_gateup(CArgs* a, uint32_t layer, uint32_t til
 }
 
 template <int NC, class S>
-__device__ __forceinline__ bool op_down(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+__device__ __forceinline__ bool op_down(Ctx a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                      lds_f32* xs) {
     constexpr int H = S::H, F = S::F;
     const int lane = lane_id(), wave = wave_id();
@@ -1247,7 +1285,7 @@ __device__ __forceinline__ uint32_t ordered_key32(float f) {
 // Inlined: as a called function the argument block would reach it through a
 // vector register, and every field read would become a vector memory load.
 template <int NC>
-__device__ __forceinline__ void route_slots(CArgs* a, uint32_t layer) {
+__device__ __forceinline__ void route_slots(Ctx a, uint32_t layer) {
     RouteLds& R = s_route;
     const int E = a->n_experts, K = a->top_k;
     const int lane = lane_id(), wave = wave_id();
@@ -1341,13 +1379,13 @@ __device__ __forceinline__ void route_slots(CArgs* a, uint32_t layer) {
     }
     if (threadIdx.x == 0) {
         R.layer = layer;
-        R.epoch = cur_epoch();
+        R.epoch = a.epoch;
     }
     __syncthreads();
 }
 
 template <int NC, class S>
-__device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+__device__ __forceinline__ bool op_router(Ctx a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                        lds_f32* xs) {
     constexpr int H = S::H;
     const int lane = lane_id(), wave = wave_id();
@@ -1370,7 +1408,7 @@ __device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t til
     norm_in_place<NC, H>(a, L->ffn_norm, xs);
     if (threadIdx.x == 0) {
         s_xs_layer = layer;
-        s_xs_epoch = cur_epoch();
+        s_xs_epoch = a.epoch;
     }
     if (!early) pre = st.prefetch(A, B, rowf, gemv_pre_rows<RS>(a));   // after the input loads, not ahead of them
     stamp(0);
@@ -1387,7 +1425,7 @@ __device__ __forceinline__ bool op_router(CArgs* a, uint32_t layer, uint32_t til
 }
 
 template <int NC, class S>
-__device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+__device__ __forceinline__ bool op_expgu(Ctx a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                       lds_f32* xs) {
     constexpr int H = S::H, MF = S::MF;
     const int lane = lane_id(), wave = wave_id();
@@ -1395,7 +1433,7 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
     // the input (the stream after the output projection) is complete before
     // the router is: load and normalise it first, then wait for the logits;
     // a workgroup whose router task of this layer left it in LDS keeps it
-    if (!(s_xs_layer == layer && s_xs_epoch == cur_epoch())) {
+    if (!(s_xs_layer == layer && s_xs_epoch == a.epoch)) {
         if (!wait_counter(a, ctr_index(layer, PH_OPROJ), a->tiles_o)) return false;
         dma_input(a, a->xres, NC * H, xs);
         norm_in_place<NC, H>(a, L->ffn_norm, xs);
@@ -1521,7 +1559,7 @@ __device__ __forceinline__ bool op_expgu(CArgs* a, uint32_t layer, uint32_t tile
 }
 
 template <int NC, class S>
-__device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
+__device__ __forceinline__ bool op_expdown(Ctx a, uint32_t layer, uint32_t tile, uint32_t wctr, uint32_t wneed,
                                         lds_f32* xs) {
     constexpr int H = S::H, MF = S::MF;
     constexpr int VPS = MF / 32;                     // 16-byte vectors per slot segment of a row
@@ -1564,7 +1602,7 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
     };
     // this workgroup's expert gate/up task of the layer left the routing in
     // LDS: then the first pass's weights are requested before the wait
-    const bool have_route = R.layer == layer && R.epoch == cur_epoch();
+    const bool have_route = R.layer == layer && R.epoch == a.epoch;
     if (have_route) issue_pass(0, min(kSlotsPerPass, R.nslots));
     // the residual after this layer's output projection (final since this
     // workgroup's expert gate/up wait)
@@ -1646,7 +1684,7 @@ __device__ __forceinline__ bool op_expdown(CArgs* a, uint32_t layer, uint32_t ti
 // --------------------------------------------------------------- LM head
 
 template <int NC, class S, int F>
-__device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr, uint32_t wneed, lds_f32* xs) {
+__device__ __forceinline__ bool op_lmhead(Ctx a, uint32_t tile, uint32_t wctr, uint32_t wneed, lds_f32* xs) {
     constexpr int H = S::H;
     constexpr int E = FmtInfo<F>::kEPV;
     __shared__ unsigned long long wbest[kWaves * 4];
@@ -1697,7 +1735,7 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     unsigned long long best[NC];
 #pragma unroll
     for (int c = 0; c < NC; ++c) best[c] = 0ull;
-    MBG_GLOBAL float* logits = a->logits ? gp(a->logits) + (size_t)cur_step() * NC * a->vocab : nullptr;
+    MBG_GLOBAL float* logits = a->logits ? gp(a->logits) + (size_t)a.step * NC * a->vocab : nullptr;
     // rr: this lane's row (wave-uniform for the one-row stream); s: its sums
     auto out = [&](int rr, const float (&s)[NC]) {
         if (rr >= nrows) return;
@@ -1739,14 +1777,14 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
     __syncthreads();
     if (threadIdx.x == 0) {
         const uint32_t old = __hip_atomic_fetch_add(gp(a->lm_ctr), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        s_last = (old + 1u == cur_epoch() * a->tiles_lm);
+        s_last = (old + 1u == a.epoch * a->tiles_lm);
     }
     __syncthreads();
     if (s_last && threadIdx.x < NC) {
         const int c = threadIdx.x;
         const unsigned long long k = __hip_atomic_load(keys + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         // device-coherent: the next step of a multi-step launch reads it as its token
-        __hip_atomic_store(gp(a->argmax) + (size_t)cur_step() * NC + c,
+        __hip_atomic_store(gp(a->argmax) + (size_t)a.step * NC + c,
                            (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(keys + c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1760,35 +1798,30 @@ __device__ __forceinline__ bool op_lmhead(CArgs* a, uint32_t tile, uint32_t wctr
 template <int NC, class S>
 __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
     (void)args;
-    CArgs* a = (CArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+    CArgs* ka = (CArgs*)__builtin_amdgcn_kernarg_segment_ptr();
     extern __shared__ __align__(16) float smem_raw[];
     lds_f32* smem = (lds_f32*)smem_raw;
     const uint32_t b = blockIdx.x;
-    const MBG_CONST uint32_t* off = (const MBG_CONST uint32_t*)a->task_off;
-    const MBG_CONST u32x4* tasks = (const MBG_CONST u32x4*)a->tasks;
+    const MBG_CONST uint32_t* off = (const MBG_CONST uint32_t*)ka->task_off;
+    const MBG_CONST u32x4* tasks = (const MBG_CONST u32x4*)ka->tasks;
     const uint32_t end = off[b + 1];
-    MBG_GLOBAL unsigned long long* trace = a->trace ? gp(a->trace) : nullptr;
+    MBG_GLOBAL unsigned long long* trace = ka->trace ? gp(ka->trace) : nullptr;
     if (threadIdx.x == 0) {
         s_stamp[2] = s_stamp[3] = 0;
         s_route.epoch = 0;   // no routing held yet (epochs start at 1)
         s_xs_epoch = 0;      // no router input held yet
-        if (S::KVF == F_BF16 && a->attn_local) {   // the attention placement assumes workgroup b runs on XCD b % 8
+        if (S::KVF == F_BF16 && ka->attn_local) {   // the attention placement assumes workgroup b runs on XCD b % 8
             uint32_t xcc;
             asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
-            if ((xcc & 0xFu) != (blockIdx.x & 7u)) latch_error(a->status, kStatusPlacement);
+            if ((xcc & 0xFu) != (blockIdx.x & 7u)) latch_error(ka->status, kStatusPlacement);
         }
     }
-    const int nsteps = a->nsteps;
+    const int nsteps = ka->nsteps;
     for (int step = 0; step < nsteps; ++step) {
-    if (threadIdx.x == 0) {
-        s_ep = a->epoch + (uint32_t)step;
-        s_pos = a->pos + step;
-        s_step = step;
-    }
-    __syncthreads();
+    const Ctx a{ka, ka->epoch + (uint32_t)step, ka->pos + step, step};
     // a later step of the launch starts when the previous step's argmax (its
     // token) is written
-    if (step > 0 && !wait_until(a, token_ctr_index(a), a->epoch + (uint32_t)(step - 1))) {
+    if (step > 0 && !wait_until(a, token_ctr_index(a), a.epoch - 1u)) {
         __builtin_amdgcn_s_waitcnt(0);
         return;
     }

@@ -144,12 +144,14 @@ class DeviceModel:
         el = torch.int16 if kv_dtype == "bf16" else torch.uint8
         self.pool = torch.zeros((cfg.n_layers, self.n_pages, 2, cfg.n_kv_heads, cfg.page_size, d), dtype=el,
                                 device=self.device)
+        # one row per sequence (a 1-D table is the one sequence 0)
         self.page_table_host = np.asarray(page_table, dtype=np.int32)
+        self.n_seqs = self.page_table_host.shape[0] if self.page_table_host.ndim == 2 else 1
         self.page_table = torch.from_numpy(self.page_table_host).to(self.device)
         self.kv_scales = None
         if kv_dtype == "fp8":
             self.kv_scales = torch.as_tensor(np.asarray(kv_scales, dtype=np.float32)).to(self.device).contiguous()
-        self.kv = M.make_kv(kv_dtype, self.n_pages, self.pool, self.page_table, self.kv_scales)
+        self.kv = M.make_kv(kv_dtype, self.n_pages, self.pool, self.page_table, self.kv_scales, self.n_seqs)
         self.kv_dtype = kv_dtype
 
         self.mcfg = M.make_config(cfg.n_layers, H, cfg.n_q_heads, cfg.n_kv_heads, d, cfg.ffn, cfg.vocab,
@@ -164,8 +166,12 @@ class DeviceModel:
         self.ctx = None
 
     # ------------------------------------------------------------------ KV prefill
-    def prefill_bf16(self, layer: int, k_bits: np.ndarray, v_bits: np.ndarray) -> None:
-        """Place logical BF16 K/V [T][Hkv][d] of positions [0, T) into the pages."""
+    def _row(self, seq: int) -> torch.Tensor:
+        return self.page_table[seq] if self.page_table.dim() == 2 else self.page_table
+
+    def prefill_bf16(self, layer: int, k_bits: np.ndarray, v_bits: np.ndarray, seq: int = 0) -> None:
+        """Place logical BF16 K/V [T][Hkv][d] of positions [0, T) of sequence
+        `seq` into its pages."""
         cfg = self.cfg
         T = k_bits.shape[0]
         P = cfg.page_size
@@ -175,7 +181,7 @@ class DeviceModel:
             full[:T] = src
             blk = torch.from_numpy(full.view(np.int16)).to(self.device)
             blk = blk.view(npg, P, cfg.n_kv_heads, cfg.head_dim).permute(0, 2, 1, 3)
-            phys = self.page_table[:npg].long()
+            phys = self._row(seq)[:npg].long()
             if T % P:  # keep slots of the last page beyond T untouched
                 last = phys[-1]
                 keep = self.pool[layer, last, which, :, T % P:, :].clone()
@@ -183,9 +189,12 @@ class DeviceModel:
             if T % P:
                 self.pool[layer, last, which, :, T % P:, :] = keep
 
-    def kv_write(self, layer: int, pos0: int, k: torch.Tensor, v: torch.Tensor) -> None:
-        """Quantising write through the library (cache dtype rounding)."""
-        M.mbg_kv_write(self.mcfg, self.kv, layer, pos0, k.shape[0], k, v, self.stream.cuda_stream)
+    def kv_write(self, layer: int, pos0: int, k: torch.Tensor, v: torch.Tensor, seq: int = 0) -> None:
+        """Quantising write through the library (cache dtype rounding) into
+        sequence `seq`'s pages."""
+        kv = self.kv if seq == 0 else M.make_kv(self.kv_dtype, self.n_pages, self.pool, self._row(seq),
+                                                self.kv_scales)
+        M.mbg_kv_write(self.mcfg, kv, layer, pos0, k.shape[0], k, v, self.stream.cuda_stream)
 
     # ------------------------------------------------------------------ decode
     def init(self) -> None:
@@ -210,6 +219,11 @@ class DeviceModel:
 
     def verify(self, tokens: torch.Tensor, pos: int, logits, argmax) -> None:
         M.mbg_decode_verify(self.ctx, tokens, tokens.numel(), pos, logits, argmax)
+
+    def batch(self, tokens: torch.Tensor, seq, pos, logits, argmax) -> None:
+        """One step of len(seq) independent sequences: column i is token
+        tokens[i] of sequence seq[i] at position pos[i]."""
+        M.mbg_decode_batch(self.ctx, tokens, len(seq), seq, pos, logits, argmax)
 
     def status(self) -> int:
         return M.mbg_get_status(self.ctx)

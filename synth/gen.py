@@ -211,6 +211,19 @@ def page_table(cfg: DecodeConfig, shuffled: bool | None = None) -> np.ndarray:
     return _rng(PAGE_SEED, n).permutation(n).astype(np.int32)
 
 
+def batch_page_table(cfg: DecodeConfig, n_seqs: int, shuffled: bool | None = None) -> np.ndarray:
+    """Page tables of n_seqs sequences sharing one pool, int32
+    [n_seqs][n_pages]: disjoint physical pages (a permutation of
+    n_seqs * n_pages when shuffled, else consecutive blocks)."""
+    if shuffled is None:
+        shuffled = cfg.shuffled_pages
+    n = cfg.n_pages
+    phys = np.arange(n_seqs * n, dtype=np.int32)
+    if shuffled:
+        phys = _rng(PAGE_SEED + 1, n_seqs * n).permutation(n_seqs * n).astype(np.int32)
+    return phys.reshape(n_seqs, n)
+
+
 # ---------------------------------------------------------------------------
 # Counter-based draws (MXFP4 experts)
 # ---------------------------------------------------------------------------

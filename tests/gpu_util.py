@@ -72,40 +72,48 @@ def fp8_kv_scales(cfg, block: int = 1 << 16):
     return sc
 
 
-def build_dense(cfg, shuffled=None, kv_dtype=None, kv_scales=None, k_max=None, host=None, block=1 << 16):
+def build_dense(cfg, shuffled=None, kv_dtype=None, kv_scales=None, k_max=None, host=None, block=1 << 16,
+                prefill_lens=None):
     """(DeviceModel, OracleModel, OracleCache) with identical weights and prefill.
 
     BF16 caches take their prefill as BF16 draws placed directly in both
     caches.  FP8 caches take float32 draws (made on the GPU) that each side
     rounds into its own cache: the library through mbg_kv_write, the oracle
-    through its codec."""
+    through its codec.  prefill_lens (one length per sequence, each at most
+    cfg.prefill) builds several sequences on disjoint pages; the third item
+    is then a list of oracle caches, sequence b holding the first
+    prefill_lens[b] prefill positions."""
     import torch
     from memory_bound_gemv_amd.device_model import DeviceModel
     kv_dtype = kv_dtype or cfg.kv_dtype
     host = host if host is not None else gen.dense_weights(cfg)
-    pt = gen.page_table(cfg, shuffled)
+    lens = [cfg.prefill] if prefill_lens is None else list(prefill_lens)
+    pt = gen.page_table(cfg, shuffled) if prefill_lens is None else gen.batch_page_table(cfg, len(lens), shuffled)
     if kv_dtype == "fp8" and kv_scales is None:
         kv_scales = fp8_kv_scales(cfg, block)
     dm = DeviceModel(cfg, host, pt, kv_dtype=kv_dtype, kv_scales=kv_scales, k_max=k_max)
     om = OracleModel(cfg, host)
-    oc = OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim, kv_dtype)
-    if kv_dtype == "fp8":
-        oc.scales = np.asarray(kv_scales, dtype=np.float32).reshape(cfg.n_layers, cfg.n_kv_heads, 2)
+    ocs = [OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim, kv_dtype) for _ in lens]
+    for oc in ocs:
+        if kv_dtype == "fp8":
+            oc.scales = np.asarray(kv_scales, dtype=np.float32).reshape(cfg.n_layers, cfg.n_kv_heads, 2)
     if cfg.prefill:
         for li in range(cfg.n_layers):
             k, v = gen.kv_prefill_bf16(cfg, li)
-            if kv_dtype == "bf16":
-                dm.prefill_bf16(li, k, v)
-                oc.k[li][:cfg.prefill] = k
-                oc.v[li][:cfg.prefill] = v
-            else:
-                for p0 in range(0, cfg.prefill, block):
-                    n = min(block, cfg.prefill - p0)
-                    k = gen.kv_prefill_f32_device(cfg, li, 0, p0, n, "cuda")
-                    v = gen.kv_prefill_f32_device(cfg, li, 1, p0, n, "cuda")
-                    dm.kv_write(li, p0, k, v)
-                    oc.prefill_f32(li, p0, k.cpu().numpy(), v.cpu().numpy())
-                torch.cuda.synchronize()
+            for b, (T, oc) in enumerate(zip(lens, ocs)):
+                if kv_dtype == "bf16":
+                    dm.prefill_bf16(li, k[:T], v[:T], seq=b)
+                    oc.k[li][:T] = k[:T]
+                    oc.v[li][:T] = v[:T]
+                else:
+                    for p0 in range(0, T, block):
+                        n = min(block, T - p0)
+                        kd = gen.kv_prefill_f32_device(cfg, li, 0, p0, n, "cuda")
+                        vd = gen.kv_prefill_f32_device(cfg, li, 1, p0, n, "cuda")
+                        dm.kv_write(li, p0, kd, vd, seq=b)
+                        oc.prefill_f32(li, p0, kd.cpu().numpy(), vd.cpu().numpy())
+                    torch.cuda.synchronize()
+    oc = ocs[0] if prefill_lens is None else ocs
     dm.init()
     return dm, om, oc
 
@@ -133,7 +141,7 @@ def device_experts(cfg, device="cuda"):
     return out
 
 
-def build_moe(cfg, shuffled=None, k_max=None, host=None, cache_experts=True):
+def build_moe(cfg, shuffled=None, k_max=None, host=None, cache_experts=True, prefill_lens=None):
     """(DeviceModel, OracleModel, OracleCache) of a routed model: BF16
     attention/router weights, MXFP4 experts (drawn on the device for the
     library, regenerated per expert on the host for the oracle), FP8 LM head
@@ -144,7 +152,8 @@ def build_moe(cfg, shuffled=None, k_max=None, host=None, cache_experts=True):
     from memory_bound_gemv_amd.device_model import DeviceModel
     from oracle import quantize_fp8_rows
     host = host if host is not None else gen.dense_weights(cfg)
-    pt = gen.page_table(cfg, shuffled)
+    lens = [cfg.prefill] if prefill_lens is None else list(prefill_lens)
+    pt = gen.page_table(cfg, shuffled) if prefill_lens is None else gen.batch_page_table(cfg, len(lens), shuffled)
     V, H = cfg.vocab, cfg.hidden
     lm_bf16 = torch.from_numpy(np.ascontiguousarray(host["lm_head"]).view(np.int16)).cuda()
     lm_codes = torch.empty((V, H), dtype=torch.uint8, device="cuda")
@@ -155,11 +164,13 @@ def build_moe(cfg, shuffled=None, k_max=None, host=None, cache_experts=True):
     dm = DeviceModel(cfg, host, pt, lm_fp8=(lm_codes, lm_scales), experts=experts, k_max=k_max)
     om = OracleModel(cfg, host, experts=lambda l, e, w: gen.expert_mxfp4(cfg, l, e, w),
                      lm_fp8=quantize_fp8_rows(host["lm_head"]), cache_experts=cache_experts)
-    oc = OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim, "bf16")
+    ocs = [OracleCache(cfg.n_layers, cfg.max_pos, cfg.n_kv_heads, cfg.head_dim, "bf16") for _ in lens]
     for li in range(cfg.n_layers if cfg.prefill else 0):
         k, v = gen.kv_prefill_bf16(cfg, li)
-        dm.prefill_bf16(li, k, v)
-        oc.k[li][:cfg.prefill] = k
-        oc.v[li][:cfg.prefill] = v
+        for b, (T, oc) in enumerate(zip(lens, ocs)):
+            dm.prefill_bf16(li, k[:T], v[:T], seq=b)
+            oc.k[li][:T] = k[:T]
+            oc.v[li][:T] = v[:T]
+    oc = ocs[0] if prefill_lens is None else ocs
     dm.init()
     return dm, om, oc
