@@ -216,9 +216,16 @@ int mbg_validate(const mbg_config *cfg, const mbg_weights *w, const mbg_kv *kv);
  *     not be freed before the process ends once a kernel has read it, so
  *     a caller reuses it for later contexts.  One context per block.
  * The weights, KV pool, workspace and counter block must outlive the
- * context.  Errors: as mbg_validate, MBG_E_WORKSPACE (workspace or counter
- * block missing, small or misaligned), MBG_E_RANGE (a page-table entry
- * outside the pool), MBG_E_HIP. */
+ * context.  Tuning overrides read from the environment here (defaults are
+ * the measured best; the "Muse Spark Open" article's prefetch bill is what
+ * they trade): MBG_GEMV_PREFETCH, MBG_GU_PREFETCH, MBG_DOWN_PREFETCH (KiB
+ * of weight rows a GEMV wavefront requests before its dependency wait,
+ * 0..64; defaults 16, 24, 32), MBG_ATTN_PREFETCH (history ring chunks an
+ * attention wave requests before its wait, 0..4), MBG_ATTN_LOCAL=0 (keep
+ * the attention splits of a head group off a single XCD's L2).  Results do
+ * not depend on them.  Errors: as mbg_validate, MBG_E_WORKSPACE (workspace
+ * or counter block missing, small or misaligned), MBG_E_RANGE (a
+ * page-table entry outside the pool), MBG_E_HIP. */
 int mbg_decode_init(const mbg_config *cfg, const mbg_weights *w, const mbg_kv *kv,
                     void *d_workspace, size_t workspace_bytes, void *d_counters, size_t counter_bytes,
                     void *stream, mbg_ctx **out);

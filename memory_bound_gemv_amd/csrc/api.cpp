@@ -369,8 +369,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.max_pos = c.max_pos;
 
     // kernels, LDS, occupancy -> grid
-    int wg_per_cu = 1;
-    if (const char* e = getenv("MBG_WG_PER_CU")) wg_per_cu = atoi(e) > 0 ? atoi(e) : 1;
+    const int wg_per_cu = 1;   // the kernel's registers allow one 4-wave workgroup per CU
     for (int k = 1; k <= c.k_max; ++k) {
         x->fn[k] = step_kernel_for(v, k, &x->lds[k]);
         if (!x->fn[k]) {
@@ -431,8 +430,8 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     S = std::max(1, std::min(S, kMaxSplits));
     S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 128)));   // >= ~128 positions per split
     a.attn_splits = S;
-    // prefetch defaults chosen by measurement on the dense 2B step (the
-    // environment variables below override them for tuning runs)
+    // prefetch defaults chosen by measurement on the dense 2B step; the
+    // environment overrides documented at mbg_decode_init replace them
     a.gemv_pre = 16;
     a.gu_pre = 24;     // dense gate/up and down: deeper than the other phases
     a.down_pre = 32;   // (same-box A/B: +0.9 % on the dense step; 32 for gate/up was slower)
@@ -442,8 +441,6 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     if (const char* e = getenv("MBG_GEMV_PREFETCH")) a.gemv_pre = std::max(0, std::min(64, atoi(e)));
     if (const char* e = getenv("MBG_GU_PREFETCH")) a.gu_pre = std::max(0, std::min(64, atoi(e)));
     if (const char* e = getenv("MBG_DOWN_PREFETCH")) a.down_pre = std::max(0, std::min(64, atoi(e)));
-    if (const char* e = getenv("MBG_POLL_WAVE_PREFETCH")) a.poll_wave_prefetch = atoi(e) != 0;
-    if (const char* e = getenv("MBG_WAVE0_INPUT")) a.wave0_input = atoi(e) != 0;
     if (const char* e = getenv("MBG_ATTN_PREFETCH")) a.attn_pre = std::max(0, std::min(kAttnBufsHost, atoi(e)));
     const uint32_t tiles_attn = (uint32_t)(c.n_kv_heads * head_groups * S);
     // Attention placement: workgroup b runs on XCD b % 8 (the dispatcher
