@@ -335,3 +335,35 @@ class OracleModel:
         sliding-window layer the last W of them), the window's earlier
         tokens included.  Returns logits [k][vocab]."""
         return np.stack([self.step(cache, int(t), pos + j) for j, t in enumerate(tokens)])
+
+
+# ---------------------------------------------------------------------------
+# Speculative round
+# ---------------------------------------------------------------------------
+
+
+def spec_round(target, tcache, draft, dcache, token: int, pos: int, k: int):
+    """One greedy speculative round (163.com Ling-3.0-flash article,
+    optimisation 3: a draft proposes tokens, the target checks the 4-token
+    window in one pass and keeps the prefix it agrees with).
+
+    The draft (any model with .step(cache, token, pos) -> logits) runs k
+    greedy steps from `token` at pos .. pos + k - 1; the window is `token`
+    and its first k - 1 proposals (the k-th step only extends the draft's
+    cache).  The target verifies the window at pos; am[j] is its argmax after
+    window[j].  Draft token j + 1 is accepted while am[j] == window[j + 1];
+    with m accepted the round emits am[0 .. m] and the next round starts from
+    am[m] at pos + m + 1.  Returns (emitted, next_pos, next_token, window,
+    target window logits)."""
+    window = [int(token)]
+    t = int(token)
+    for s in range(k):
+        t = argmax_lower_index(draft.step(dcache, t, pos + s))
+        window.append(t)
+    logits = target.verify(tcache, window[:k], pos)
+    am = [argmax_lower_index(v) for v in logits]
+    m = 0
+    while m < k - 1 and am[m] == window[m + 1]:
+        m += 1
+    return am[:m + 1], pos + m + 1, am[m], window, logits
+
