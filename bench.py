@@ -204,6 +204,26 @@ def build_device_model(cfg, host, dev, k_max=1, n_seqs=1):
     return dm
 
 
+def build_draft_model(cfg, host, dev, target):
+    """A 1-layer early-exit draft for speculative rounds: the target's layer
+    0 with its embedding, final norm and LM head (the same device tensors
+    for the experts and the FP8 head), its own KV cache prefilled like the
+    target's layer 0."""
+    from memory_bound_gemv_amd.device_model import DeviceModel
+    from synth import gen
+    dcfg = cfg.with_(n_layers=1)
+    keep = {k: v for k, v in host.items() if not k.startswith("l") or k.startswith("l0.") or k == "lm_head"}
+    if cfg.is_moe:
+        dm = DeviceModel(dcfg, keep, gen.page_table(dcfg), lm_fp8=(target.lm_codes, target.lm_scales),
+                         experts=target.experts[:1], device=dev)
+    else:
+        dm = DeviceModel(dcfg, keep, gen.page_table(dcfg), device=dev)
+    k, v = gen.kv_prefill_bf16(cfg, 0)
+    dm.prefill_bf16(0, k, v)
+    dm.init()
+    return dm
+
+
 def _threads():
     from threadpoolctl import threadpool_info
     return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
@@ -272,7 +292,8 @@ def run_decode(args, cfg):
     host = gen.dense_weights(cfg)
     k_win = 4 if cfg.is_moe and not args.no_verify else 1
     n_batch = args.batch if cfg.kv_dtype == "bf16" else 1
-    dm = build_device_model(cfg, host, dev, k_max=max(k_win, n_batch), n_seqs=n_batch)
+    k_spec = 4 if args.spec and cfg.kv_dtype == "bf16" else 1
+    dm = build_device_model(cfg, host, dev, k_max=max(k_win, n_batch, k_spec), n_seqs=n_batch)
     torch.cuda.synchronize()
     t_gen = time.perf_counter() - t_gen
     info = dm.info()
@@ -408,6 +429,36 @@ def run_decode(args, cfg):
             "ms_per_window_mfma": round(ms_path[M.MBG_PATH_MFMA], 4),
         }
 
+    if args.spec and cfg.kv_dtype == "bf16" and dm.k_max >= 4:
+        # speculative rounds (k = 4): 1-layer early-exit draft, verify and
+        # on-device acceptance, two launches per round; one round from a
+        # fixed state repeated (the workload's position budget holds only a
+        # few rounds), its acceptance read back
+        ddm = build_draft_model(cfg, host, dev, dm)
+        s0 = torch.zeros(12, dtype=torch.int32, device=dev)
+        s0[0] = cfg.prefill
+        s0[4] = int(gen.prompt_tokens(cfg, 1)[0])
+        s1 = torch.zeros_like(s0)
+        emit = torch.zeros(16, dtype=torch.int32, device=dev)
+        tk4 = torch.zeros(4, dtype=torch.int32, device=dev)
+        tk4[0] = int(s0[4].item())
+        am4 = torch.zeros(4, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            dm.spec_round(ddm, 4, s0, s1, emit)
+        ms_round = timed(stream, lambda i: dm.spec_round(ddm, 4, s0, s1, emit), max(8, args.steps // 8))
+        ms_draft = timed(stream, lambda i: ddm.steps(tk4, 4, cfg.prefill, None, am4), max(8, args.steps // 8))
+        if dm.status() != 0 or ddm.status() != 0:
+            raise RuntimeError("device status after the speculative rounds")
+        m = int(s1[2].item())
+        out["spec_round"] = {
+            "k": 4, "draft": "1 layer (the target's layer 0, embedding, final norm and LM head)",
+            "ms_per_round": round(ms_round, 4), "ms_draft_4_steps": round(ms_draft, 4),
+            "accepted_this_round": m, "tokens_s_at_this_acceptance": round((m + 1) * 1e3 / ms_round, 1),
+            "tokens_s_full_acceptance": round(4e3 / ms_round, 1),
+            "note": "random weights: acceptance measures nothing; the round's cost is what is measured",
+        }
+        ddm.close()
+
     if n_batch > 1:
         # n_batch independent sequences per step, each at its own position
         # (sequence b from batch_prefill_lens(b), positions cycled over
@@ -523,6 +574,8 @@ def main():
                          "LM-head GEMV alone)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-verify", action="store_true", help="moe: skip the 4-token verify-window timing")
+    ap.add_argument("--no-spec", dest="spec", action="store_false",
+                    help="skip the speculative-round timing (BF16-KV workloads)")
     ap.add_argument("--batch", type=int, default=4,
                     help="also time steps of this many independent sequences (BF16-KV workloads; 1: skip)")
     ap.add_argument("--multi-step", type=int, default=8,

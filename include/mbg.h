@@ -273,6 +273,49 @@ int mbg_decode_verify(mbg_ctx *ctx, const int32_t *d_tokens, int32_t k, int32_t 
 int mbg_decode_batch(mbg_ctx *ctx, const int32_t *d_tokens, int32_t n, const int32_t *seq,
                      const int32_t *pos, float *d_logits, int32_t *d_argmax);
 
+/* Speculative decoding state, in device memory (int32 words): the position
+ * of window[0]; tokens emitted, draft tokens accepted and rounds run so
+ * far; the window: window[0] is the last emitted token, window[1 .. k] the
+ * draft's tokens of the round (written by mbg_spec_round). */
+typedef struct {
+    int32_t pos;
+    int32_t n_emitted;
+    int32_t n_accepted;
+    int32_t n_rounds;
+    int32_t window[8];
+} mbg_spec_state;
+
+/* One speculative round, enqueued as two launches on the shared stream with
+ * no host round trip (163.com Ling-3.0-flash article, optimisation 3: a
+ * draft proposes 3 tokens, the target verifies the 4-token window in one
+ * pass, and the agreeing prefix is accepted; the "Muse Spark Open" article
+ * runs draft, verify and accept as one graph per step).
+ *   1. draft: k greedy steps of the draft context (any model with the same
+ *      vocabulary, e.g. one layer sharing the target's embedding and LM
+ *      head) from state.window[0] at state.pos, its tokens into
+ *      state.window[1 .. k];
+ *   2. target: the verify window state.window[0 .. k-1] at state.pos, then,
+ *      on the device, greedy prefix acceptance: with am[j] the target's
+ *      argmax after window[j], draft token j + 1 is accepted while
+ *      am[j] == window[j + 1]; with m accepted the round appends
+ *      am[0 .. m] to d_emit (int32 [emit_cap], at state.n_emitted) and
+ *      writes *d_next: pos + m + 1, window[0] = am[m], the counters + (m + 1),
+ *      + m, + 1.
+ * Both contexts read the position on the device, so rounds chain: round
+ * r + 1 takes round r's d_next as its d_state.  The emitted tokens are
+ * those of greedy decoding of the target whatever the draft proposes; the
+ * draft's quality only sets how many come per round.  d_logits (may be
+ * NULL): the window's target logits [k][vocab].  k in [2, target k_max];
+ * d_state and d_next are distinct mbg_spec_state buffers (device); both
+ * contexts must have been initialised on the same stream.  A position out of
+ * range (state.pos + k > max_pos of either context) ends the launch and
+ * makes the next mbg_get_status of that context return MBG_E_RANGE; more
+ * emitted tokens than emit_cap are dropped and flagged the same way.
+ * Errors here: MBG_E_INVALID_ARG (NULL, shared buffers, different streams
+ * or vocabularies), MBG_E_RANGE (k), MBG_E_HIP. */
+int mbg_spec_round(mbg_ctx *target, mbg_ctx *draft, int32_t k, int32_t *d_state, int32_t *d_next,
+                   int32_t *d_emit, int32_t emit_cap, float *d_logits);
+
 /* n_steps greedy decode steps (1 .. 4096) in ONE kernel launch: step s runs
  * at pos + s; step 0 reads its token at d_token[0], step s > 0 takes the
  * argmax of step s - 1 on the device, and the persistent kernel moves from

@@ -95,6 +95,8 @@ def _load():
         "mbg_decode_steps": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.c_int32, C.c_void_p, C.c_void_p]),
         "mbg_decode_batch": (C.c_int, [CTX_P, C.c_void_p, C.c_int32, C.POINTER(C.c_int32), C.POINTER(C.c_int32),
                                        C.c_void_p, C.c_void_p]),
+        "mbg_spec_round": (C.c_int, [CTX_P, CTX_P, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                     C.c_void_p]),
         "mbg_get_status": (C.c_int, [CTX_P]),
         "mbg_query": (C.c_int, [CTX_P, C.POINTER(mbg_info)]),
         "mbg_set_timeout_us": (C.c_int, [CTX_P, C.c_int64]),
@@ -123,7 +125,7 @@ def _load():
 
 _lib = _load()
 EXPORTED = ("mbg_workspace_size", "mbg_counter_bytes", "mbg_validate", "mbg_decode_init", "mbg_decode_step",
-            "mbg_decode_verify", "mbg_decode_steps", "mbg_decode_batch",
+            "mbg_decode_verify", "mbg_decode_steps", "mbg_decode_batch", "mbg_spec_round",
             "mbg_get_status", "mbg_query", "mbg_set_timeout_us", "mbg_set_verify_path", "mbg_set_trace",
             "mbg_read_trace",
             "mbg_read_routing", "mbg_last_error", "mbg_destroy",
@@ -241,6 +243,15 @@ def mbg_decode_batch(ctx, tokens, n: int, seq, pos, logits, argmax) -> None:
     sq = (C.c_int32 * n)(*[int(v) for v in seq])
     ps = (C.c_int32 * n)(*[int(v) for v in pos])
     _check(_lib.mbg_decode_batch(ctx, _ptr(tokens), n, sq, ps, _ptr(logits), _ptr(argmax)))
+
+
+# mbg_spec_state: int32 words pos, n_emitted, n_accepted, n_rounds, window[8]
+SPEC_STATE_WORDS = 12
+
+
+def mbg_spec_round(target, draft, k: int, state, next_state, emit, emit_cap: int, logits=None) -> None:
+    _check(_lib.mbg_spec_round(target, draft, k, _ptr(state), _ptr(next_state), _ptr(emit), emit_cap,
+                               _ptr(logits)))
 
 
 def mbg_get_status(ctx) -> int:

@@ -369,7 +369,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.max_pos = c.max_pos;
 
     // kernels, LDS, occupancy -> grid
-    const int wg_per_cu = 1;   // the kernel's registers allow one 4-wave workgroup per CU
+    int wg_per_cu = 1;   // one 4-wave workgroup per CU (the kernel uses every register of a SIMD)
     for (int k = 1; k <= c.k_max; ++k) {
         x->fn[k] = step_kernel_for(v, k, &x->lds[k]);
         if (!x->fn[k]) {
@@ -616,14 +616,27 @@ struct BatchCols {
     int32_t pos[4] = {0, 0, 0, 0};
 };
 
+// A speculative round's launch: position on the device, acceptance outputs.
+struct SpecLaunch {
+    const int32_t* dpos = nullptr;
+    const int32_t* cur = nullptr;
+    int32_t* next = nullptr;
+    int32_t* emit = nullptr;
+    int32_t cap = 0;
+};
+
 static int launch_step(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t pos, float* d_logits,
-                       int32_t* d_argmax, int32_t nsteps = 1, const BatchCols* batch = nullptr) {
+                       int32_t* d_argmax, int32_t nsteps = 1, const BatchCols* batch = nullptr,
+                       const SpecLaunch* spec = nullptr) {
     if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
     if (!d_tokens || !d_argmax) return fail(MBG_E_INVALID_ARG, "tokens/argmax is NULL");
     if (k < 1 || k > x->cfg.k_max) return fail(MBG_E_RANGE, "k %d outside [1, %d]", k, x->cfg.k_max);
     if (nsteps < 1 || nsteps > kMaxStepsPerLaunch)
         return fail(MBG_E_RANGE, "n_steps %d outside [1, %d]", nsteps, kMaxStepsPerLaunch);
-    const int64_t span = batch ? 1 : (int64_t)k + nsteps - 1;   // a batch's positions were checked per column
+    // a batch's positions were checked per column; a device-resident
+    // position is checked by the kernel
+    const int64_t span = batch ? 1 : (int64_t)k + nsteps - 1;
+    if (spec) pos = 0;
     if (pos < 0 || (int64_t)pos + span > x->cfg.max_pos)
         return fail(MBG_E_RANGE, "positions %d..%lld outside [0, %d)", pos, (long long)(pos + span - 1),
                     x->cfg.max_pos);
@@ -634,6 +647,13 @@ static int launch_step(mbg_ctx* x, const int32_t* d_tokens, int32_t k, int32_t p
     a.pos = pos;
     a.ncol = k;
     a.nsteps = nsteps;
+    if (spec) {
+        a.dpos = spec->dpos;
+        a.spec_cur = spec->cur;
+        a.spec_next = spec->next;
+        a.spec_emit = spec->emit;
+        a.spec_emit_cap = spec->cap;
+    }
     if (batch) {
         a.batch = 1;
         for (int i = 0; i < 4; ++i) {
@@ -687,6 +707,33 @@ int mbg_decode_batch(mbg_ctx* x, const int32_t* d_tokens, int32_t n, const int32
     return launch_step(x, d_tokens, n, pos[0], d_logits, d_argmax, 1, &b);
 }
 
+int mbg_spec_round(mbg_ctx* target, mbg_ctx* draft, int32_t k, int32_t* d_state, int32_t* d_next, int32_t* d_emit,
+                   int32_t emit_cap, float* d_logits) {
+    if (!target || !draft) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
+    if (!d_state || !d_next || !d_emit) return fail(MBG_E_INVALID_ARG, "state/next/emit is NULL");
+    if (d_state == d_next) return fail(MBG_E_INVALID_ARG, "the next state must be another buffer");
+    if (target->stream != draft->stream) return fail(MBG_E_INVALID_ARG, "target and draft must share a stream");
+    if (target->cfg.vocab != draft->cfg.vocab) return fail(MBG_E_INVALID_ARG, "target and draft vocabularies differ");
+    if (k < 2 || k > target->cfg.k_max) return fail(MBG_E_RANGE, "k %d outside [2, %d]", k, target->cfg.k_max);
+    if (emit_cap <= 0) return fail(MBG_E_INVALID_ARG, "emit_cap %d", emit_cap);
+    int32_t* win = d_state + SPEC_WINDOW;
+    // draft: k greedy steps from window[0] at the state's position; its
+    // tokens land in window[1 .. k] (the k-th is only for the draft's own
+    // cache: with every draft accepted the next round starts after it)
+    SpecLaunch ds;
+    ds.dpos = d_state + SPEC_POS;
+    int rc = launch_step(draft, win, 1, 0, nullptr, win + 1, k, nullptr, &ds);
+    if (rc) return rc;
+    // target: the k-token window, then acceptance into the next state
+    SpecLaunch vs;
+    vs.dpos = d_state + SPEC_POS;
+    vs.cur = d_state;
+    vs.next = d_next;
+    vs.emit = d_emit;
+    vs.cap = emit_cap;
+    return launch_step(target, win, k, 0, d_logits, d_next + SPEC_WINDOW, 1, nullptr, &vs);
+}
+
 int mbg_get_status(mbg_ctx* x) {
     if (!x) return fail(MBG_E_INVALID_ARG, "ctx is NULL");
     HIP_TRY(hipStreamSynchronize(x->stream));
@@ -704,6 +751,7 @@ int mbg_get_status(mbg_ctx* x) {
         if (st == kStatusTimeout) return fail(MBG_E_TIMEOUT, "a device wait exceeded its deadline");
         if (st == kStatusPlacement)
             return fail(MBG_E_UNSUPPORTED, "workgroups are not placed on XCD blockIdx %% 8; set MBG_ATTN_LOCAL=0");
+        if (st == kStatusPosition) return fail(MBG_E_RANGE, "a speculative round's position was out of range");
         return fail(MBG_E_HIP, "device status %u", st);
     }
     if (fl != 0) {

@@ -125,6 +125,15 @@ struct StepArgs {
     int32_t batch;
     int32_t bpos[4];
     int32_t bseq[4];
+    // speculative rounds: the launch's first position is read on the device
+    // from dpos (range-checked there) instead of pos; a verify launch with
+    // spec_next set ends in greedy prefix acceptance (the LM head's last
+    // workgroup) that writes the next round's state and the emitted tokens
+    const int32_t* dpos;
+    const int32_t* spec_cur;   // this round's state (SpecState layout)
+    int32_t* spec_next;        // the next round's state, or null
+    int32_t* spec_emit;        // emitted tokens [spec_emit_cap]
+    int32_t spec_emit_cap;
     // workspace
     const Task* tasks;
     const uint32_t* task_off;  // [grid + 1]
@@ -165,11 +174,18 @@ struct StepArgs {
 };
 
 // Device status codes (positive on the device, negated at the boundary).
-// kStatusTimeout and kStatusPlacement end the launch (every wait gives up);
+// kStatusTimeout, kStatusPlacement and kStatusPosition end the launch (every wait gives up);
 // kStatusRange is a flag: the token id was clamped and the step completes.
 constexpr uint32_t kStatusTimeout = 7;
 constexpr uint32_t kStatusRange = 4;
 constexpr int kAttnLocalMaxSplitLen = 1024;    // XCD-local attention groups only up to this many positions per split
 constexpr uint32_t kStatusPlacement = 2;   // a workgroup is not on the XCD its attention placement assumes
+constexpr uint32_t kStatusPosition = 5;    // a device-resident position (speculative round) was out of range
+
+// Speculative-round state in device memory (int32 words; mbg_spec_state in
+// the public header): position of window[0], tokens emitted, draft tokens
+// accepted and rounds run so far, then the window: [0] the last emitted
+// token, [1 ..] the draft's tokens.
+enum : int { SPEC_POS = 0, SPEC_EMITTED = 1, SPEC_ACCEPTED = 2, SPEC_ROUNDS = 3, SPEC_WINDOW = 4, SPEC_WORDS = 12 };
 
 }  // namespace mbg

@@ -784,7 +784,7 @@ __device__ __forceinline__ bool op_attn(Ctx a, uint32_t layer, uint32_t tile, ui
             const size_t vstep = (size_t)Hkv * page_size * HD * EB;   // K -> V of the same page
             const MBG_GLOBAL uint8_t* kp = pool + el * EB + lane_off;
             MBG_LDS uint8_t* dst = ring + (b * NUB + u) * 2 * kUnitBytes;
-            if (!batch && tb + TPI > a->pos) {   // rows this launch writes (an earlier step's K/V): coherent loads
+            if (!batch && tb + TPI > a.pos - a.step) {   // rows this launch writes (an earlier step's K/V): coherent loads
                 lds_dma16_coh(kp, (MBG_LDS void*)dst);
                 lds_dma16_coh(kp + vstep, (MBG_LDS void*)(dst + kUnitBytes));
             } else {
@@ -1681,6 +1681,35 @@ __device__ __forceinline__ bool op_expdown(Ctx a, uint32_t layer, uint32_t tile,
     return true;
 }
 
+// ------------------------------------------------- speculative acceptance
+
+// Greedy prefix acceptance of a verify window (163.com Ling-3.0-flash
+// article, optimisation 3: the target checks the draft's tokens in one
+// pass and keeps the prefix it agrees with).  The window holds t0 (the last
+// emitted token) and the draft's d1 .. d(NC-1); am[j] is the target's argmax
+// after window[j].  Draft j + 1 is accepted while am[j] == d(j+1); with m
+// accepted, the round emits am[0 .. m] (the accepted drafts and the target's
+// own next token) and the next round starts from am[m] at pos + m + 1.  One
+// thread; the state words of this round were written by earlier launches.
+template <int NC>
+__device__ __forceinline__ void spec_accept(Ctx a, const int32_t* am) {
+    const MBG_GLOBAL int32_t* cur = gp(a->spec_cur);
+    MBG_GLOBAL int32_t* nxt = gp(a->spec_next);
+    const MBG_GLOBAL int32_t* win = cur + SPEC_WINDOW;
+    int m = 0;
+    while (m < NC - 1 && am[m] == win[m + 1]) ++m;
+    const int done = cur[SPEC_EMITTED];
+    MBG_GLOBAL int32_t* emit = gp(a->spec_emit);
+    for (int j = 0; j <= m; ++j)
+        if (done + j < a->spec_emit_cap) emit[done + j] = am[j];
+    if (done + m + 1 > a->spec_emit_cap) latch_error(a->flags, kStatusRange);
+    nxt[SPEC_POS] = a.pos + m + 1;
+    nxt[SPEC_EMITTED] = min(done + m + 1, a->spec_emit_cap);
+    nxt[SPEC_ACCEPTED] = cur[SPEC_ACCEPTED] + m;
+    nxt[SPEC_ROUNDS] = cur[SPEC_ROUNDS] + 1;
+    nxt[SPEC_WINDOW] = am[m];
+}
+
 // --------------------------------------------------------------- LM head
 
 template <int NC, class S, int F>
@@ -1780,14 +1809,19 @@ __device__ __forceinline__ bool op_lmhead(Ctx a, uint32_t tile, uint32_t wctr, u
         s_last = (old + 1u == a.epoch * a->tiles_lm);
     }
     __syncthreads();
+    __shared__ int32_t s_amax[4];
     if (s_last && threadIdx.x < NC) {
         const int c = threadIdx.x;
         const unsigned long long k = __hip_atomic_load(keys + c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const int32_t am = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
         // device-coherent: the next step of a multi-step launch reads it as its token
-        __hip_atomic_store(gp(a->argmax) + (size_t)a.step * NC + c,
-                           (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull)), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(gp(a->argmax) + (size_t)a.step * NC + c, am, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(keys + c, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_amax[c] = am;
+    }
+    if (s_last && a->spec_next) {   // wave-uniform: s_last is the workgroup's
+        __syncthreads();
+        if (threadIdx.x == 0) spec_accept<NC>(a, s_amax);
     }
     if (s_last) release_counter(a, token_ctr_index(a));   // this step's token is written
     return true;
@@ -1817,8 +1851,16 @@ __global__ void __launch_bounds__(kThreads, 1) step_kernel(StepArgs args) {
         }
     }
     const int nsteps = ka->nsteps;
+    int pos0 = ka->pos;
+    if (ka->dpos) {   // a speculative round's launch: its position is on the device
+        pos0 = *(const MBG_GLOBAL int32_t*)ka->dpos;
+        if (pos0 < 0 || pos0 > ka->max_pos - (ka->ncol + nsteps - 1)) {   // every workgroup sees the same value
+            if (threadIdx.x == 0 && blockIdx.x == 0) latch_error(ka->status, kStatusPosition);
+            return;
+        }
+    }
     for (int step = 0; step < nsteps; ++step) {
-    const Ctx a{ka, ka->epoch + (uint32_t)step, ka->pos + step, step};
+    const Ctx a{ka, ka->epoch + (uint32_t)step, pos0 + step, step};
     // a later step of the launch starts when the previous step's argmax (its
     // token) is written
     if (step > 0 && !wait_until(a, token_ctr_index(a), a.epoch - 1u)) {

@@ -225,6 +225,13 @@ class DeviceModel:
         tokens[i] of sequence seq[i] at position pos[i]."""
         M.mbg_decode_batch(self.ctx, tokens, len(seq), seq, pos, logits, argmax)
 
+    def spec_round(self, draft: "DeviceModel", k: int, state: torch.Tensor, next_state: torch.Tensor,
+                   emit: torch.Tensor, logits=None) -> None:
+        """One speculative round: `draft` proposes k tokens, this model
+        verifies the window and accepts on the device (state, next_state:
+        int32 [12] device tensors; emit: int32 device tensor)."""
+        M.mbg_spec_round(self.ctx, draft.ctx, k, state, next_state, emit, emit.numel(), logits)
+
     def status(self) -> int:
         return M.mbg_get_status(self.ctx)
 

@@ -174,3 +174,45 @@ def build_moe(cfg, shuffled=None, k_max=None, host=None, cache_experts=True, pre
     oc = ocs[0] if prefill_lens is None else ocs
     dm.init()
     return dm, om, oc
+
+
+def build_draft(cfg, host, n_layers, target_dm=None):
+    """(DeviceModel, OracleModel, OracleCache) of an early-exit draft: the
+    target's first n_layers layers with its embedding, final norm and LM
+    head (the same tensors), its cache prefilled like the target's first
+    layers.  A routed target passes its DeviceModel for the experts and the
+    FP8 LM head."""
+    import torch
+    from memory_bound_gemv_amd.device_model import DeviceModel
+    dcfg = cfg.with_(n_layers=n_layers)
+    import re
+    keep = {k: v for k, v in host.items()
+            if not re.match(r"l\d+\.", k) or int(k[1:].split(".")[0]) < n_layers}
+    pt = gen.page_table(dcfg)
+    if cfg.is_moe:
+        dm = DeviceModel(dcfg, keep, pt, lm_fp8=(target_dm.lm_codes, target_dm.lm_scales),
+                         experts=target_dm.experts[:n_layers])
+        om = OracleModel(dcfg, keep, experts=lambda l, e, w: gen.expert_mxfp4(cfg, l, e, w),
+                         lm_fp8=quantize_fp8_rows_cached(host))
+    else:
+        dm = DeviceModel(dcfg, keep, pt)
+        om = OracleModel(dcfg, keep)
+    oc = OracleCache(dcfg.n_layers, dcfg.max_pos, dcfg.n_kv_heads, dcfg.head_dim, "bf16")
+    for li in range(n_layers if cfg.prefill else 0):
+        k, v = gen.kv_prefill_bf16(cfg, li)
+        dm.prefill_bf16(li, k, v)
+        oc.k[li][:cfg.prefill] = k
+        oc.v[li][:cfg.prefill] = v
+    dm.init()
+    return dm, om, oc
+
+
+_FP8_LM = {}
+
+
+def quantize_fp8_rows_cached(host):
+    from oracle import quantize_fp8_rows
+    key = id(host["lm_head"])
+    if key not in _FP8_LM:
+        _FP8_LM[key] = quantize_fp8_rows(host["lm_head"])
+    return _FP8_LM[key]
