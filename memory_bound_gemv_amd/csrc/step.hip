@@ -1506,7 +1506,7 @@ __device__ __forceinline__ bool op_expgu(Ctx a, uint32_t layer, uint32_t tile, u
     // keep one row per instruction (the segmented buffers would spill)
     if constexpr (NC <= 2) {
         constexpr int LPR = seg_lanes<H / 32>();
-        using SS = SegStream<F_MXFP4, NC, H / 32, LPR, (NC == 1 ? 2 : 1)>;
+        using SS = SegStream<F_MXFP4, NC, H / 32, LPR, (NC == 1 ? 4 : 1)>;
         static_assert(SS::P % 2 == 0, "a unit's two rows share a wave instruction");
         SS st(2 * nunits, lane);
         typename SS::Buf A, B;
