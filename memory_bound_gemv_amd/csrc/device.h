@@ -71,10 +71,14 @@ __device__ __forceinline__ uint8_t f32_to_fp8e4m3(float f) {
 // ------------------------------------------------------------------ MXFP4
 
 // E8M0 byte -> binary32 2^(e-127) (e = 0 gives the subnormal 2^-127,
-// e = 255 NaN).
+// e = 255 NaN).  Branch-free: the two special codes are the ones for which
+// (e + 1) mod 256 <= 1, and both only add bit 22 to e << 23 (0 -> 2^-127,
+// 0x7F800000 -> quiet NaN).  A per-lane branch here would put divergent
+// control flow into every streaming loop, where it costs the load waits
+// their precision.
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
-    if (e == 255u) return __uint_as_float(0x7FC00000u);
-    return e ? __uint_as_float(e << 23) : __uint_as_float(0x00400000u);
+    const uint32_t special = ((e + 1u) & 0xFFu) <= 1u ? 0x00400000u : 0u;
+    return __uint_as_float((e << 23) | special);
 }
 
 // Eight E2M1 codes of one 32-bit word (element 2i in the low nibble of byte

@@ -176,13 +176,28 @@ struct RowStream {
 
     __device__ __forceinline__ static bool active(int j, int lane) { return !PART || j < NJ - 1 || lane < LASTN; }
 
-    // Issue rows [r0, r1) of chunk c into b.
-    template <class RowFn>
+    // Issue rows [r0, r1) of chunk c into b.  Rows past the end are skipped
+    // and so are the idle lanes of a partial last column, unless kClamp:
+    // then every load is issued, rows past the end repeating the last row
+    // and idle lanes the row's last vector (lines the same instruction or
+    // chunk already requests), so that the number of loads behind a chunk
+    // is the same on every path (what the split loop of run() needs).
+    template <bool kClamp, class RowFn>
     __device__ __forceinline__ void issue_rows(Buf& b, int c, RowFn& row, int r0, int r1) const {
 #pragma unroll
         for (int r = 0; r < RPC; ++r) {
             const int rr = c * RPC + r;
-            if (r >= r0 && r < r1 && rr < nrows) {
+            if constexpr (kClamp) {
+                if (r >= r0 && r < r1) {
+                    const GRow g = row(rr < nrows ? rr : nrows - 1);
+#pragma unroll
+                    for (int j = 0; j < NJ; ++j) {
+                        const int v = active(j, lane) ? lane + kWave * j : NV - 1;
+                        b.w[r][j] = ld_stream_g(g.data + v);
+                        if constexpr (F == F_MXFP4) b.s[r][j] = g.scale[v];
+                    }
+                }
+            } else if (r >= r0 && r < r1 && rr < nrows) {
                 const GRow g = row(rr);
 #pragma unroll
                 for (int j = 0; j < NJ; ++j) {
@@ -196,11 +211,16 @@ struct RowStream {
     }
     template <class RowFn>
     __device__ __forceinline__ void issue(Buf& b, int c, RowFn& row) const {
-        issue_rows(b, c, row, 0, RPC);
+        issue_rows<false>(b, c, row, 0, RPC);
     }
 
-    template <class OutFn>
+    // With kFence the activations, read from LDS in every chunk, are kept
+    // from being hoisted out of the chunk loop by a compiler barrier (held
+    // in registers across all compute sites of the split loop they can
+    // spill).
+    template <bool kFence = false, class OutFn>
     __device__ __forceinline__ void compute(const Buf& b, int c, const lds_f32* xs, int ldx, OutFn& out) const {
+        if constexpr (kFence) asm volatile("" ::: "memory");
         float acc[RPC][NC][2];
 #pragma unroll
         for (int r = 0; r < RPC; ++r)
@@ -256,8 +276,8 @@ struct RowStream {
     template <class RowFn>
     __device__ __forceinline__ int prefetch(Buf& a, Buf& b, RowFn& row, int pre) const {
         pre = pre < 0 ? 0 : pre > 2 * RPC ? 2 * RPC : pre;
-        issue_rows(a, 0, row, 0, pre < RPC ? pre : RPC);
-        if (pre > RPC) issue_rows(b, 1, row, 0, pre - RPC);
+        issue_rows<false>(a, 0, row, 0, pre < RPC ? pre : RPC);
+        if (pre > RPC) issue_rows<false>(b, 1, row, 0, pre - RPC);
         return pre;
     }
 
@@ -265,25 +285,55 @@ struct RowStream {
     // chunk 1 is issued (pass it to run()).
     template <class RowFn>
     __device__ __forceinline__ bool finish_prefetch(Buf& a, Buf& b, RowFn& row, int pre) const {
-        if (pre < RPC) issue_rows(a, 0, row, pre, RPC);
+        if (pre < RPC) issue_rows<false>(a, 0, row, pre, RPC);
         if (pre > RPC) {
-            issue_rows(b, 1, row, pre - RPC, RPC);
+            issue_rows<false>(b, 1, row, pre - RPC, RPC);
             return true;
         }
         return false;
     }
 
     // `a` holds chunk 0, already issued; `b` holds chunk 1 when b_issued.
-    template <class RowFn, class OutFn>
+    //
+    // kSplit: four compute sites, a chunk with the next one in flight behind
+    // it (one site per buffer) and the final chunk (one per buffer).  Where
+    // one site serves both "next chunk issued" and "no next chunk" paths
+    // (the compact loop), the compiler assumes the smaller number of loads
+    // in flight behind it and waits for the next chunk as well, so a chunk's
+    // arithmetic does not overlap the following chunk's loads; the split
+    // loop (with every load of a chunk issued, see issue_rows) waits for
+    // exactly the chunk it computes, at the price of twice the code and of
+    // repeated rows in a partial last chunk.  Callers choose: measured in the
+    // decode step, the split loop pays off with several activation columns
+    // and costs time with one (where a wave's streams are one or two chunks
+    // long and the kernel's instruction footprint grows).
+    template <bool kSplit, class RowFn, class OutFn>
     __device__ __forceinline__ void run(Buf& a, Buf& b, RowFn& row, const lds_f32* xs, int ldx, OutFn& out,
                                         bool b_issued = false) const {
         const int nch = chunks();
-        for (int c = 0; c < nch; c += 2) {
-            if (c + 1 < nch && !(c == 0 && b_issued)) issue(b, c + 1, row);
-            compute(a, c, xs, ldx, out);
-            if (c + 1 >= nch) break;
-            if (c + 2 < nch) issue(a, c + 2, row);
-            compute(b, c + 1, xs, ldx, out);
+        if constexpr (kSplit) {
+            for (int c = 0; c < nch; c += 2) {
+                if (c + 1 >= nch) {
+                    compute<true>(a, c, xs, ldx, out);
+                    break;
+                }
+                if (!(c == 0 && b_issued)) issue_rows<true>(b, c + 1, row, 0, RPC);
+                compute<true>(a, c, xs, ldx, out);
+                if (c + 2 >= nch) {
+                    compute<true>(b, c + 1, xs, ldx, out);
+                    break;
+                }
+                issue_rows<true>(a, c + 2, row, 0, RPC);
+                compute<true>(b, c + 1, xs, ldx, out);
+            }
+        } else {
+            for (int c = 0; c < nch; c += 2) {
+                if (c + 1 < nch && !(c == 0 && b_issued)) issue_rows<false>(b, c + 1, row, 0, RPC);
+                compute(a, c, xs, ldx, out);
+                if (c + 1 >= nch) break;
+                if (c + 2 < nch) issue_rows<false>(a, c + 2, row, 0, RPC);
+                compute(b, c + 1, xs, ldx, out);
+            }
         }
     }
 };
@@ -347,8 +397,10 @@ struct SegStream {
         }
     }
 
-    template <class OutFn>
+    // (kFence: as in RowStream::compute)
+    template <bool kFence = false, class OutFn>
     __device__ __forceinline__ void compute(const Buf& b, int c, const lds_f32* xs, int ldx, OutFn& out) const {
+        if constexpr (kFence) asm volatile("" ::: "memory");
         float acc[RG][NC][2];
 #pragma unroll
         for (int g = 0; g < RG; ++g)
@@ -417,18 +469,36 @@ struct SegStream {
         return n;
     }
 
-    template <class RowFn, class OutFn>
+    // kSplit: as in RowStream::run.
+    template <bool kSplit, class RowFn, class OutFn>
     __device__ __forceinline__ void run(Buf& a, Buf& b, RowFn& row, const lds_f32* xs, int ldx, OutFn& out,
                                         int issued = 0) const {
         const int nch = chunks();
         if (nch == 0) return;
         if (issued < 1) issue(a, 0, row);
-        for (int c = 0; c < nch; c += 2) {
-            if (c + 1 < nch && !(c == 0 && issued >= 2)) issue(b, c + 1, row);
-            compute(a, c, xs, ldx, out);
-            if (c + 1 >= nch) break;
-            if (c + 2 < nch) issue(a, c + 2, row);
-            compute(b, c + 1, xs, ldx, out);
+        if constexpr (kSplit) {
+            for (int c = 0; c < nch; c += 2) {
+                if (c + 1 >= nch) {
+                    compute<true>(a, c, xs, ldx, out);
+                    break;
+                }
+                if (!(c == 0 && issued >= 2)) issue(b, c + 1, row);
+                compute<true>(a, c, xs, ldx, out);
+                if (c + 2 >= nch) {
+                    compute<true>(b, c + 1, xs, ldx, out);
+                    break;
+                }
+                issue(a, c + 2, row);
+                compute<true>(b, c + 1, xs, ldx, out);
+            }
+        } else {
+            for (int c = 0; c < nch; c += 2) {
+                if (c + 1 < nch && !(c == 0 && issued >= 2)) issue(b, c + 1, row);
+                compute(a, c, xs, ldx, out);
+                if (c + 1 >= nch) break;
+                if (c + 2 < nch) issue(a, c + 2, row);
+                compute(b, c + 1, xs, ldx, out);
+            }
         }
     }
 };

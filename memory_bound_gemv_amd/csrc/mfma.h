@@ -30,6 +30,8 @@
 //     LDS read.
 #pragma once
 
+#include <type_traits>
+
 #include "gemv.h"
 
 namespace mbg {
@@ -93,13 +95,19 @@ __device__ __forceinline__ void mfma_prep_b(const lds_f32* xs, int ldx, MBG_LDS 
 // each finished block b, out(b, d) is called by every lane with d = this
 // lane's hi + lo sums: lanes with l % 16 < NC hold column l % 16 of rows
 // 16 b + 4 (l / 16) + i in d[i] (rows past nrows are to be ignored).
-template <int F, int NC, int K, int D>
+//
+// One block of loads (U per lane) is in flight: while unit u of block b is
+// consumed, unit u of block b + 1 is requested into the same registers.
+// The last block is a separate instance that requests nothing, so in the
+// main one every unit has the same number of loads behind it on every path
+// and the compiler waits for that unit alone.
+template <int F, int NC, int K>
 struct MfmaStream {
     static constexpr int EPU = MfmaFmt<F>::kElemsPerUnit;
     static constexpr int IPU = MfmaFmt<F>::kInstPerUnit;
     static constexpr int U = K / EPU;    // 16-byte loads per lane per block
     static_assert(K % EPU == 0, "row length");
-    static_assert(D >= 1 && D <= U, "ring depth");
+    static_assert(U <= 24, "a block's loads stay within the registers and the load counter");
 
     int nrows, lane;
     __device__ __forceinline__ MfmaStream(int nrows_, int lane_) : nrows(nrows_), lane(lane_) {}
@@ -107,40 +115,32 @@ struct MfmaStream {
     template <class RowFn, class OutFn>
     __device__ __forceinline__ void run(RowFn& row, const MBG_LDS u32x4* bprep, OutFn& out) const {
         const int nblocks = (nrows + 15) / 16;
-        const int total = nblocks * U;
-        if (total == 0) return;
+        if (nblocks == 0) return;
         const int r16 = lane & 15, kq = lane >> 4;
-        uint4 wv[D];
-        uint32_t sv[D];
-        // this lane's row address in the block whose items are being issued
-        // (items are issued in order, so one cached address suffices)
-        int ib = -1;
-        GRow gi{nullptr, nullptr};
-        auto issue = [&](int item, uint4& w, uint32_t& s) {
-            const int b = item / U, u = item - b * U;
-            if (b != ib) {
-                ib = b;
-                gi = row(min(16 * b + r16, nrows - 1));
-            }
+        uint4 wv[U];
+        uint32_t sv[U];
+        auto issue = [&](const GRow& g, int u) {
             const int vec = 4 * u + kq;
-            w = ld_stream_g(gi.data + vec);
-            if constexpr (F == F_MXFP4) s = gi.scale[vec];
+            wv[u] = ld_stream_g(g.data + vec);
+            if constexpr (F == F_MXFP4) sv[u] = g.scale[vec];
         };
-        // prefetch the first D items
+        auto block_row = [&](int b) { return row(min(16 * b + r16, nrows - 1)); };
+        {
+            const GRow g0 = block_row(0);
 #pragma unroll
-        for (int o = 0; o < D; ++o)
-            if (o < total) issue(o, wv[o], sv[o]);
-        f32x4m acc = {0.f, 0.f, 0.f, 0.f};
-        for (int base = 0; base < total; base += D) {
+            for (int u = 0; u < U; ++u) issue(g0, u);
+        }
+        // consume block b; with Refill, request block b + 1 unit by unit
+        auto block = [&](int b, auto refill) {
+            constexpr bool kRefill = decltype(refill)::value;
+            GRow gn{nullptr, nullptr};
+            if constexpr (kRefill) gn = block_row(b + 1);
+            f32x4m acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int o = 0; o < D; ++o) {
-                const int it = base + o;
-                if (it >= total) continue;
-                const int b = it / U, u = it - b * U;
-                // consume slot o
+            for (int u = 0; u < U; ++u) {
                 if constexpr (F == F_MXFP4) {
-                    const float sc = e8m0_to_f32(sv[o]);
-                    const uint32_t ws[4] = {wv[o].x, wv[o].y, wv[o].z, wv[o].w};
+                    const float sc = e8m0_to_f32(sv[u]);
+                    const uint32_t ws[4] = {wv[u].x, wv[u].y, wv[u].z, wv[u].w};
 #pragma unroll
                     for (int m = 0; m < 4; ++m) {
                         const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(ws[m], sc, 0);
@@ -155,28 +155,30 @@ struct MfmaStream {
                     }
                 } else {
                     const u32x4 bq = bprep[u * kWave + lane];
-                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[o]),
+                    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wv[u]),
                                                                     __builtin_bit_cast(bf16x8, bq), acc, 0, 0, 0);
                 }
-                // hi + lo of every unit, read in the basic block of the
-                // instructions that wrote the accumulator: a read placed only
-                // behind the block-end branch can follow the last matrix
-                // instruction with fewer wait states than it needs (measured:
-                // wrong rows 2 and 3 of each group of 4 when no refill load
-                // came between)
-                const bool last = u == U - 1;
-                float d[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float part = __int_as_float(
-                        __builtin_amdgcn_update_dpp(0, __float_as_int(acc[i]), 0x100 + NC, 0xF, 0xF, false));
-                    d[i] = acc[i] + part;   // row_shl:NC: the lo column of this lane's column
-                    acc[i] = last ? 0.f : acc[i];
-                }
-                // refill slot o with the item D ahead
-                if (it + D < total) issue(it + D, wv[o], sv[o]);
-                if (last) out(b, d);   // block b complete
+                if constexpr (kRefill) issue(gn, u);
             }
+            // hi + lo, read in the basic block of the matrix instructions
+            // that wrote the accumulator (a read behind a branch can follow
+            // the last one with fewer wait states than it needs: measured
+            // as wrong rows 2 and 3 of each group of 4)
+            float d[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float part = __int_as_float(
+                    __builtin_amdgcn_update_dpp(0, __float_as_int(acc[i]), 0x100 + NC, 0xF, 0xF, false));
+                d[i] = acc[i] + part;   // row_shl:NC: the lo column of this lane's column
+            }
+            out(b, d);
+        };
+        for (int b = 0;; ++b) {
+            if (b + 1 >= nblocks) {
+                block(b, std::false_type{});
+                break;
+            }
+            block(b, std::true_type{});
         }
     }
 };

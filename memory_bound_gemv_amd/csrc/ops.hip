@@ -94,11 +94,11 @@ __global__ void __launch_bounds__(256) lm_head_kernel(LmHeadArgs a) {
         }
     };
     if constexpr (kSeg) {
-        ss.run(SA, SB, rowf, xs, H, out, pre);
+        ss.template run<true>(SA, SB, rowf, xs, H, out, pre);
 #pragma unroll
         for (int c = 0; c < NC; ++c) best[c] = wave_max_u64(best[c]);   // lanes held their own rows' best
     } else {
-        st.run(A, B, rowf, xs, H, out);
+        st.template run<true>(A, B, rowf, xs, H, out);
     }
 
     if (lane == 0) {

@@ -515,7 +515,8 @@ __device__ __forceinline__ bool op_qkv(Ctx a, uint32_t layer, uint32_t tile, uin
             for (int c = 0; c < NC; ++c) res[rr * NC + c] = s[c];
         }
     };
-    st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
+    // compact loop: a wave has one or two chunks here, and the split loop (gemv.h) spills in the small model
+    st.template run<false>(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     __syncthreads();
 #pragma unroll
@@ -1129,7 +1130,8 @@ __device__ __forceinline__ bool op_oproj(Ctx a, uint32_t layer, uint32_t tile, u
         const int r = gw + nw * rr;
         stc(x + c * H + r, rp.get(rr, [&] { return resid(rr); }) + v);
     };
-    st.run(A, B, rowf, xs, K, out, st.finish_prefetch(A, B, rowf, pre));
+    // compact loop: one or two chunks per wave; the split loop spills in the small model
+    st.template run<false>(A, B, rowf, xs, K, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     release_counter(a, ctr_index(layer, PH_OPROJ));
     return true;
@@ -1178,7 +1180,9 @@ __device__ __forceinline__ bool op_gateup(Ctx a, uint32_t layer, uint32_t tile, 
         const int f = gw + nw * (rr >> 1);
         stc(hb + (size_t)c * F + f, gv / (1.0f + expf(-gv)) * uv);
     };
-    st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
+    // split loop for several columns (each chunk computed while the next is
+    // in flight); for one column the compact loop measured faster in the step
+    st.template run<(NC >= 2)>(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     release_counter(a, ctr_index(layer, PH_GATEUP));
     return true;
@@ -1222,7 +1226,8 @@ __device__ __forceinline__ bool op_down(Ctx a, uint32_t layer, uint32_t tile, ui
         const int r = gw + nw * rr;
         stc(x + c * H + r, rp.get(rr, [&] { return resid(rr); }) + v);
     };
-    st.run(A, B, rowf, xs, F, out, st.finish_prefetch(A, B, rowf, pre));
+    // split loop for several columns, compact for one (as in op_gateup)
+    st.template run<(NC >= 2)>(A, B, rowf, xs, F, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     release_counter(a, ctr_index(layer, PH_DOWN));
     return true;
@@ -1418,7 +1423,8 @@ __device__ __forceinline__ bool op_router(Ctx a, uint32_t layer, uint32_t tile, 
         for (int c = 0; c < NC; ++c)
             if (lane == c) stc(rl + (size_t)c * E + gw + nw * rr, s[c]);
     };
-    st.run(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
+    // compact loop: the split one spills in the routed kernel, and a wave has at most one chunk
+    st.template run<false>(A, B, rowf, xs, H, out, st.finish_prefetch(A, B, rowf, pre));
     stamp(1);
     release_counter(a, ctr_index(layer, PH_ROUTER));
     return true;
@@ -1473,7 +1479,7 @@ __device__ __forceinline__ bool op_expgu(Ctx a, uint32_t layer, uint32_t tile, u
             // matrix-core tile: 16 rows (8 units) per instruction block
             MBG_LDS u32x4* bprep = reinterpret_cast<MBG_LDS u32x4*>(xs + NC * H);
             mfma_prep_b<F_MXFP4, NC, H>(xs, H, bprep, wave, kWaves, lane);
-            MfmaStream<F_MXFP4, NC, H, H / 128> ms(2 * nunits, lane);
+            MfmaStream<F_MXFP4, NC, H> ms(2 * nunits, lane);
             auto outb = [&](int b, const float (&d)[4]) {
                 const int n = lane & 15, j = lane >> 4;
                 if (n >= NC) return;
@@ -1500,10 +1506,11 @@ __device__ __forceinline__ bool op_expgu(Ctx a, uint32_t layer, uint32_t tile, u
     }
     // a wave's rows (about 14 of 1.3 KiB for the routed model) are issued at
     // once: the rows are only known after routing, so nothing was prefetched
-    // before the wait.  Rows are 80 vectors: for one or two columns the
-    // segmented stream keeps every lane busy, and a unit's gate and up rows
-    // (rr = 2 iu, 2 iu + 1) sit in neighbouring lane groups; wider windows
-    // keep one row per instruction (the segmented buffers would spill)
+    // before the wait.  Rows are 80 vectors:
+    // for one or two columns the segmented stream keeps every lane busy, and
+    // a unit's gate and up rows (rr = 2 iu, 2 iu + 1) sit in neighbouring
+    // lane groups; wider windows keep one row per instruction (the segmented
+    // buffers would spill)
     if constexpr (NC <= 2) {
         constexpr int LPR = seg_lanes<H / 32>();
         using SS = SegStream<F_MXFP4, NC, H / 32, LPR, (NC == 1 ? 4 : 1)>;
@@ -1523,7 +1530,9 @@ __device__ __forceinline__ bool op_expgu(Ctx a, uint32_t layer, uint32_t tile, u
             const int u = u0 + wave + kWaves * iu;
             stc(hb + (size_t)t * ld + u, R.wt[u / MF][t] * (gv / (1.0f + expf(-gv)) * uv));
         };
-        st.run(A, B, rowf, xs, H, out);
+        // one column: a wave's rows in one chunk; two: the split loop (each
+        // chunk computed while the next is in flight)
+        st.template run<(NC >= 2)>(A, B, rowf, xs, H, out);
     } else {
         using RS = RowStream<F_MXFP4, NC, H / 32, 4>;
         RS st(2 * nunits, lane);
@@ -1545,7 +1554,8 @@ __device__ __forceinline__ bool op_expgu(Ctx a, uint32_t layer, uint32_t tile, u
             const int u = u0 + wave + kWaves * (rr >> 1);
             stc(hb + (size_t)c * ld + u, R.wt[u / MF][c] * (gv / (1.0f + expf(-gv)) * uv));
         };
-        st.run(A, B, rowf, xs, H, out);
+        // split loop: each chunk computed while the next is in flight
+        st.template run<true>(A, B, rowf, xs, H, out);
     }
     stamp(1);
     if (tile == 0 && (int)threadIdx.x < NC * a->top_k) {  // routing record of this step
@@ -1781,12 +1791,15 @@ __device__ __forceinline__ bool op_lmhead(Ctx a, uint32_t tile, uint32_t wctr, u
         }
     };
     if constexpr (kSeg) {
-        ss.run(SA, SB, rowf, xs, H, out, pre);
+        // split loop for several columns, compact for one (measured faster
+        // in the step)
+        ss.template run<(NC >= 2)>(SA, SB, rowf, xs, H, out, pre);
         // lanes hold the best of their own rows
 #pragma unroll
         for (int c = 0; c < NC; ++c) best[c] = wave_max_u64(best[c]);
     } else {
-        rs.run(A, B, rowf, xs, H, out, rs.finish_prefetch(A, B, rowf, pre));
+        // compact loop: the split one spills in the dense kernels (BF16 head rows)
+        rs.template run<false>(A, B, rowf, xs, H, out, rs.finish_prefetch(A, B, rowf, pre));
     }
     stamp(1);
     if (lane == 0) {
