@@ -60,7 +60,7 @@ constexpr int kMaxTopK = 8;
 constexpr int kMaxShared = 2;
 constexpr int kMaxSlots = 4 * kMaxTopK + kMaxShared;   // union over a 4-token window plus shared experts
 constexpr int kSlotsPerPass = 9;                 // expert-down slots whose h sits in LDS at once
-constexpr int kMaxDownRows = 4;                  // output rows one wavefront owns in the expert down
+constexpr int kMaxDownRows = 3;                  // output rows one wavefront owns in the expert down
 
 struct LayerPtrs {
     const uint16_t* attn_norm;

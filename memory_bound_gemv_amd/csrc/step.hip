@@ -1257,6 +1257,7 @@ struct RouteLds {
     int slot_exp[kMaxSlots];     // expert id; ids >= n_experts are shared experts
     uint8_t slot_of[kMaxExperts];   // slot of a selected routed expert
     float wt[kMaxSlots][4];      // weight of a slot in each column (0: not selected)
+    uint8_t cslot[4][kMaxTopK + kMaxShared];   // each column's own slots, ascending (windows of 2+)
     int sel[4][kMaxTopK];
     float selw[4][kMaxTopK];
     uint32_t layer, epoch;       // the routing these fields hold
@@ -1376,11 +1377,18 @@ __device__ __forceinline__ void route_slots(Ctx a, uint32_t layer) {
     __syncthreads();
     if ((int)threadIdx.x < NC * K) {
         const int c = threadIdx.x / K, k = threadIdx.x - c * K;
-        R.wt[R.slot_of[R.sel[c][k]]][c] = R.selw[c][k];
+        const int sl = R.slot_of[R.sel[c][k]];
+        R.wt[sl][c] = R.selw[c][k];
+        if constexpr (NC > 1) {   // rank among the column's (distinct) slots
+            int rank = 0;
+            for (int k2 = 0; k2 < K; ++k2) rank += R.slot_of[R.sel[c][k2]] < sl;
+            R.cslot[c][rank] = (uint8_t)sl;
+        }
     }
     if ((int)threadIdx.x < NC * a->n_shared) {
         const int c = threadIdx.x / a->n_shared, sh = threadIdx.x - c * a->n_shared;
         R.wt[R.nrouted + sh][c] = 1.f;
+        if constexpr (NC > 1) R.cslot[c][K + sh] = (uint8_t)(R.nrouted + sh);
     }
     if (threadIdx.x == 0) {
         R.layer = layer;
@@ -1573,9 +1581,16 @@ __device__ __forceinline__ bool op_expdown(Ctx a, uint32_t layer, uint32_t tile,
                                         lds_f32* xs) {
     constexpr int H = S::H, MF = S::MF;
     constexpr int VPS = MF / 32;                     // 16-byte vectors per slot segment of a row
-    constexpr int NV = kSlotsPerPass * VPS;          // vectors per pass
+    // One column: passes over the routing's slots in order (the 8 routed +
+    // 1 shared experts of the step in one pass).  Several columns: one pass
+    // per column over that column's own slots (its h is zero for the other
+    // experts of the window, ~70 % of a 4-token window's slot union), the
+    // next column's weights in flight while a column is computed; an expert
+    // two columns share is read twice.
+    constexpr int SPP = NC >= 2 ? kMaxTopK + kMaxShared : kSlotsPerPass;
+    constexpr int NV = SPP * VPS;                    // vectors per pass
     constexpr int NJ = (NV + kWave - 1) / kWave;
-    constexpr int XLD = kSlotsPerPass * MF;          // LDS floats per column
+    constexpr int XLD = SPP * MF;                    // LDS floats per column (one column a pass for NC >= 2)
     const int lane = lane_id(), wave = wave_id();
     CLayer* L = (CLayer*)a->layers + layer;
     const RouteLds& R = s_route;
@@ -1587,15 +1602,18 @@ __device__ __forceinline__ bool op_expdown(Ctx a, uint32_t layer, uint32_t tile,
     const uint8_t* sdc = L->sd_codes;
     const uint8_t* sds = L->sd_scales;
     constexpr size_t kMatCodes = (size_t)H * (MF / 2), kMatScales = (size_t)H * (MF / 32);
-    // every row's gathered vectors of a pass (slots s0 .. s0 + ns), all in flight at once
-    uint4 w[kMaxDownRows][NJ];
-    uint32_t sb[kMaxDownRows][NJ];
-    auto issue_pass = [&](int s0, int ns) {
+    // every row's gathered vectors of a pass, all in flight at once
+    struct PassBuf {
+        uint4 w[kMaxDownRows][NJ];
+        uint32_t sb[kMaxDownRows][NJ];
+    };
+    // pass vector v of this lane belongs to slot slot_at(v / VPS)
+    auto issue_pass = [&](PassBuf& P, int ns, auto slot_at) {
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int v = lane + kWave * j;
             const bool act = v < ns * VPS;
-            const int slot = s0 + (act ? v / VPS : 0);
+            const int slot = slot_at(act ? v / VPS : 0);
             const int vv = v - (v / VPS) * VPS;
             const int e = R.slot_exp[slot];
             const uint8_t* cb = e < E ? edc + (size_t)e * kMatCodes : sdc + (size_t)(e - E) * kMatCodes;
@@ -1604,16 +1622,22 @@ __device__ __forceinline__ bool op_expdown(Ctx a, uint32_t layer, uint32_t tile,
             for (int i = 0; i < kMaxDownRows; ++i) {
                 if (i < nrows && act) {
                     const size_t r = (size_t)(gw + nw * i);
-                    w[i][j] = ld_stream_g(gp(reinterpret_cast<const uint4*>(cb + r * (MF / 2))) + vv);
-                    sb[i][j] = gp(scb)[r * (MF / 32) + vv];
+                    P.w[i][j] = ld_stream_g(gp(reinterpret_cast<const uint4*>(cb + r * (MF / 2))) + vv);
+                    P.sb[i][j] = gp(scb)[r * (MF / 32) + vv];
                 }
             }
         }
     };
+    auto col_slot = [&](int c) { return [&R, c](int k) { return (int)R.cslot[c][k]; }; };
+    const int ncs = a->top_k + a->n_shared;          // slots of one column
+    PassBuf PA, PB;
     // this workgroup's expert gate/up task of the layer left the routing in
     // LDS: then the first pass's weights are requested before the wait
     const bool have_route = R.layer == layer && R.epoch == a.epoch;
-    if (have_route) issue_pass(0, min(kSlotsPerPass, R.nslots));
+    if (have_route) {
+        if constexpr (NC == 1) issue_pass(PA, min(SPP, R.nslots), [](int k) { return k; });
+        else issue_pass(PA, ncs, col_slot(0));
+    }
     // the residual after this layer's output projection (final since this
     // workgroup's expert gate/up wait)
     MBG_GLOBAL float* x = gp(a->xres);
@@ -1632,24 +1656,30 @@ __device__ __forceinline__ bool op_expdown(Ctx a, uint32_t layer, uint32_t tile,
     for (int i = 0; i < kMaxDownRows; ++i)
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[i][c] = 0.f;
-    for (int s0 = 0; s0 < U; s0 += kSlotsPerPass) {
-        const int ns = min(kSlotsPerPass, U - s0);
-        // h of this pass's slots -> LDS [c][slot][MF]
+    // a pass's h into LDS: column c (of cols) of slots slot_at(0 .. ns) ->
+    // xs[(c - c0) * XLD + k * MF + f]
+    auto load_h = [&](int c0, int cols, int ns, auto slot_at) {
         __syncthreads();
-        const int nvec = ns * MF / 4;
-        for (int c = 0; c < NC; ++c)
-            for (int j = threadIdx.x; j < nvec; j += kThreads)
+        constexpr int Q = MF / 4;
+        const int nvec = ns * Q;
+        for (int c = 0; c < cols; ++c)
+            for (int j = threadIdx.x; j < nvec; j += kThreads) {
+                const int k = j / Q, f4 = j - k * Q;
                 *reinterpret_cast<MBG_LDS f32x4*>(xs + c * XLD + 4 * j) =
-                    ldc4(hr, (uint32_t)(((size_t)c * ld + (size_t)s0 * MF + 4 * j) * 4));
+                    ldc4(hr, (uint32_t)(((size_t)(c0 + c) * ld + (size_t)slot_at(k) * MF + 4 * f4) * 4));
+            }
         __syncthreads();
-        if (s0 > 0 || !have_route) issue_pass(s0, ns);
+    };
+    // acc[i][c0 .. c0 + cols) += the pass's rows against LDS columns 0 .. cols
+    auto compute_pass = [&](const PassBuf& P, int ns, auto c0v, auto colsv) {
+        constexpr int c0 = decltype(c0v)::value, cols = decltype(colsv)::value;
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             const int v = lane + kWave * j;
             if (v >= ns * VPS) continue;
-            float xv[NC][32];
+            float xv[cols][32];
 #pragma unroll
-            for (int c = 0; c < NC; ++c)
+            for (int c = 0; c < cols; ++c)
 #pragma unroll
                 for (int e4 = 0; e4 < 32; e4 += 4) {
                     const f32x4 t = *reinterpret_cast<const MBG_LDS f32x4*>(xs + c * XLD + v * 32 + e4);
@@ -1662,19 +1692,43 @@ __device__ __forceinline__ bool op_expdown(Ctx a, uint32_t layer, uint32_t tile,
             for (int i = 0; i < kMaxDownRows; ++i) {
                 if (i >= nrows) continue;
                 float wf[32];
-                decode16<F_MXFP4>(w[i][j], sb[i][j], wf);
+                decode16<F_MXFP4>(P.w[i][j], P.sb[i][j], wf);
 #pragma unroll
-                for (int c = 0; c < NC; ++c) {
+                for (int c = 0; c < cols; ++c) {
                     float p0 = 0.f, p1 = 0.f;
 #pragma unroll
                     for (int e2 = 0; e2 < 32; e2 += 2) {
                         p0 = fmaf(wf[e2], xv[c][e2], p0);
                         p1 = fmaf(wf[e2 + 1], xv[c][e2 + 1], p1);
                     }
-                    acc[i][c] += p0 + p1;
+                    acc[i][c0 + c] += p0 + p1;
                 }
             }
         }
+    };
+    using C0 = std::integral_constant<int, 0>;
+    if constexpr (NC == 1) {
+        for (int s0 = 0; s0 < U; s0 += SPP) {
+            const int ns = min(SPP, U - s0);
+            auto seq = [s0](int k) { return s0 + k; };
+            load_h(0, 1, ns, seq);
+            if (s0 > 0 || !have_route) issue_pass(PA, ns, seq);
+            compute_pass(PA, ns, C0{}, std::integral_constant<int, 1>{});
+        }
+    } else {
+        if (!have_route) issue_pass(PA, ncs, col_slot(0));
+        // column c: its h into LDS (that wait has also retired its weights),
+        // then column c + 1's weights requested, then column c computed
+        auto column = [&](auto cv, PassBuf& cur, PassBuf& nxt) {
+            constexpr int c = decltype(cv)::value;
+            load_h(c, 1, ncs, col_slot(c));
+            if constexpr (c + 1 < NC) issue_pass(nxt, ncs, col_slot(c + 1));
+            compute_pass(cur, ncs, cv, std::integral_constant<int, 1>{});
+        };
+        column(C0{}, PA, PB);
+        column(std::integral_constant<int, 1>{}, PB, PA);
+        if constexpr (NC > 2) column(std::integral_constant<int, 2>{}, PA, PB);
+        if constexpr (NC > 3) column(std::integral_constant<int, 3>{}, PB, PA);
     }
     stamp(1);
 #pragma unroll
