@@ -836,127 +836,294 @@ __device__ __forceinline__ bool op_attn(Ctx a, uint32_t layer, uint32_t tile, ui
     // this group's splits share an XCD (and its L2); compiled for BF16 caches
     const bool local = KVF == F_BF16 && a->attn_local != 0;
     const bool empty = t0 >= t1;
-    for (int col = 0; col < ncol && !empty; ++col) {
-        const int pc = batch ? (int)a->bpos[col] : pos + col;   // this column's position
-        const int te = min(t1, pc + 1);
-        const int tlo = W > 0 ? pc - W + 1 : 0;   // this column's first position (may be < 0)
-        float q[GH][EPC];
-#pragma unroll
-        for (int h = 0; h < GH; ++h) {
-            const uint32_t qo = (uint32_t)((((size_t)col * Hq + qh0 + h) * HD + cidx * EPC) * 4);
-#pragma unroll
-            for (int e = 0; e < EPC; e += 4) {
-                const f32x4 t = ldc4(rq, qo + 4u * e);
-#pragma unroll
-                for (int k = 0; k < 4; ++k) q[h][e + k] = t[k] * qscale;
-            }
-        }
-        if (col == 0) stamp(0);
-        Lane st;
-        st.init();
-        if (col > 0 && !resident) {  // stream the history again for this column
-            if (batch) {   // its own sequence's history and pages
-                th = min(t1, pc);
-                ptab_s = col_ptab(a, col);
-                nu = th > t0 ? (th - t0 + NS - 1) / NS : 0;
-                nch = (nu + NUB - 1) / NUB;
-                npre = min(nch, NB);
-            }
-            __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // earlier ring reads are done
-            for (int c = 0; c < npre; ++c) issue_chunk(c, c);
-        }
-        for (int c = 0; c < nch; ++c) {
-            const int b = c & (NB - 1);
-            wait_chunks(min(nch - 1 - c, NB - 1));        // chunk c has landed
-            uint4 K[NUB], V[NUB];
-            bool valid[NUB];
-#pragma unroll
-            for (int u = 0; u < NUB; ++u) {
-                const MBG_LDS uint8_t* src = ring + (b * NUB + u) * 2 * kUnitBytes + lane * 16;
-                const u32x4 kv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src);
-                const u32x4 vv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src + kUnitBytes);
-                K[u] = make_uint4(kv4.x, kv4.y, kv4.z, kv4.w);
-                V[u] = make_uint4(vv4.x, vv4.y, vv4.z, vv4.w);
-                const int tk = tok_of(c * NUB + u);
-                valid[u] = tk < th && tk >= tlo;
-            }
-            st.template fold<NUB>(q, K, V, valid, ksc);
-            if (c + NB < nch) {
-                __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // this buffer's reads are done
-                issue_chunk(c + NB, b);
-            }
-        }
-        if (col == 0) stamp(2);
-        // positions written this step, up to this column's own
-        if (has_new) {
-            const uint4 K[1] = {Kn}, V[1] = {Vn};
-            const bool valid[1] = {batch ? ld_new && tl == col : tl < ncol && tn < te && tn >= tlo};
-            st.template fold<1>(q, K, V, valid, ksc);
-        }
-        if constexpr (KVF == F_FP8) {
-#pragma unroll
-            for (int h = 0; h < GH; ++h)
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) st.o[h][e] *= vsc;
-        }
-        // merge the token slots of a wave (lanes with the same cidx)
-        if constexpr (LPT <= 4) st.template merge_partner<4>();
-        if constexpr (LPT <= 8) st.template merge_partner<8>();
-        if constexpr (LPT <= 16) st.template merge_partner<16>();
-        st.template merge_partner<32>();
-        // then the waves, through LDS, in wave order
-        if (lane < LPT) {
+    // One sequence whose split history does not stay in the ring: the
+    // window's columns share that history, so it is streamed once and each
+    // chunk is folded into every column's state while it sits in the ring
+    // (kJoint columns at a time: all of them, except that four columns over
+    // the FP8 cache, whose lane slices are twice as wide, go in pairs, as
+    // four states would spill).  The window then reads its history once
+    // (twice) instead of once per column.  Compiled for the FP8 cache, the
+    // long-context format: in the BF16 kernels, whose histories here stay
+    // resident, the joint code's mere presence slowed the routed 4-token
+    // window by 4 % (measured), so there a window over a long history is
+    // still streamed once per column.  Otherwise one column at a time: a
+    // batch column streams its own sequence's history, and a resident
+    // history is re-read from LDS.
+    constexpr int kJoint = (KVF == F_FP8 && NC > 3) ? 2 : NC;
+    bool done_joint = false;
+    if constexpr (KVF == F_FP8 && NC >= 2) {
+        // q of column col (pre-scaled to the log2 domain)
+        auto load_q = [&](float (&q)[GH][EPC], int col) {
 #pragma unroll
             for (int h = 0; h < GH; ++h) {
-                lds_f32* r = red + ((size_t)wave * GH + h) * stride;
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) r[cidx * EPC + e] = st.o[h][e];
-                if (cidx == 0) {
-                    r[HD] = st.m[h];
-                    r[HD + 1] = st.l[h];
-                }
-            }
-        }
-        __syncthreads();
-        if (wave == 0 && lane < LPT) {
-#pragma unroll
-            for (int h = 0; h < GH; ++h) {
-                float M = red[h * stride + HD], Ls = red[h * stride + HD + 1];
-                float O[EPC];
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) O[e] = red[h * stride + cidx * EPC + e];
-                for (int w = 1; w < kWaves; ++w) {
-                    const lds_f32* r = red + ((size_t)w * GH + h) * stride;
-                    float mn, w1, w2;
-                    merge_weights(M, r[HD], mn, w1, w2);
-                    Ls = Ls * w1 + r[HD + 1] * w2;
-#pragma unroll
-                    for (int e = 0; e < EPC; ++e) O[e] = O[e] * w1 + r[cidx * EPC + e] * w2;
-                    M = mn;
-                }
-                const uint32_t row = (uint32_t)((((size_t)col * Hq + qh0 + h) * S_ + s) * stride * 4);
+                const uint32_t qo = (uint32_t)((((size_t)col * Hq + qh0 + h) * HD + cidx * EPC) * 4);
 #pragma unroll
                 for (int e = 0; e < EPC; e += 4) {
-                    f32x4 t;
-                    t[0] = O[e];
-                    t[1] = O[e + 1];
-                    t[2] = O[e + 2];
-                    t[3] = O[e + 3];
-                    if (local) stx4(rp, row + 4u * (cidx * EPC + e), t);
-                    else stc4(rp, row + 4u * (cidx * EPC + e), t);
-                }
-                if (cidx == 0) {
-                    f32x4 t;
-                    t[0] = M;
-                    t[1] = Ls;
-                    t[2] = 0.f;
-                    t[3] = 0.f;
-                    if (local) stx4(rp, row + 4u * HD, t);
-                    else stc4(rp, row + 4u * HD, t);
+                    const f32x4 t = ldc4(rq, qo + 4u * e);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) q[h][e + k] = t[k] * qscale;
                 }
             }
+        };
+        // stream the split's history chunks (the first npre already requested)
+        // through the ring; fold(K, V, tk) sees each unit's rows and positions
+        auto stream = [&](auto fold) {
+            for (int c = 0; c < nch; ++c) {
+                const int b = c & (NB - 1);
+                wait_chunks(min(nch - 1 - c, NB - 1));        // chunk c has landed
+                uint4 K[NUB], V[NUB];
+                int tk[NUB];
+#pragma unroll
+                for (int u = 0; u < NUB; ++u) {
+                    const MBG_LDS uint8_t* src = ring + (b * NUB + u) * 2 * kUnitBytes + lane * 16;
+                    const u32x4 kv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src);
+                    const u32x4 vv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src + kUnitBytes);
+                    K[u] = make_uint4(kv4.x, kv4.y, kv4.z, kv4.w);
+                    V[u] = make_uint4(vv4.x, vv4.y, vv4.z, vv4.w);
+                    tk[u] = tok_of(c * NUB + u);
+                }
+                fold(K, V, tk);
+                if (c + NB < nch) {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // this buffer's reads are done
+                    issue_chunk(c + NB, b);
+                }
+            }
+        };
+        // column col after its history: the positions written this step up to
+        // its own, the V scale, the merge of the lanes and waves, the split's
+        // partial row
+        auto finish_column = [&](Lane& st, const float (&q)[GH][EPC], int col, int tlo) {
+            const int pc = batch ? (int)a->bpos[col] : pos + col;   // this column's position
+            const int te = min(t1, pc + 1);
+            if (has_new) {
+                const uint4 K[1] = {Kn}, V[1] = {Vn};
+                const bool valid[1] = {batch ? ld_new && tl == col : tl < ncol && tn < te && tn >= tlo};
+                st.template fold<1>(q, K, V, valid, ksc);
+            }
+            if constexpr (KVF == F_FP8) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h)
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) st.o[h][e] *= vsc;
+            }
+            // merge the token slots of a wave (lanes with the same cidx)
+            if constexpr (LPT <= 4) st.template merge_partner<4>();
+            if constexpr (LPT <= 8) st.template merge_partner<8>();
+            if constexpr (LPT <= 16) st.template merge_partner<16>();
+            st.template merge_partner<32>();
+            // then the waves, through LDS, in wave order
+            if (lane < LPT) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    lds_f32* r = red + ((size_t)wave * GH + h) * stride;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) r[cidx * EPC + e] = st.o[h][e];
+                    if (cidx == 0) {
+                        r[HD] = st.m[h];
+                        r[HD + 1] = st.l[h];
+                    }
+                }
+            }
+            __syncthreads();
+            if (wave == 0 && lane < LPT) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    float M = red[h * stride + HD], Ls = red[h * stride + HD + 1];
+                    float O[EPC];
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) O[e] = red[h * stride + cidx * EPC + e];
+                    for (int w = 1; w < kWaves; ++w) {
+                        const lds_f32* r = red + ((size_t)w * GH + h) * stride;
+                        float mn, w1, w2;
+                        merge_weights(M, r[HD], mn, w1, w2);
+                        Ls = Ls * w1 + r[HD + 1] * w2;
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) O[e] = O[e] * w1 + r[cidx * EPC + e] * w2;
+                        M = mn;
+                    }
+                    const uint32_t row = (uint32_t)((((size_t)col * Hq + qh0 + h) * S_ + s) * stride * 4);
+#pragma unroll
+                    for (int e = 0; e < EPC; e += 4) {
+                        f32x4 t;
+                        t[0] = O[e];
+                        t[1] = O[e + 1];
+                        t[2] = O[e + 2];
+                        t[3] = O[e + 3];
+                        if (local) stx4(rp, row + 4u * (cidx * EPC + e), t);
+                        else stc4(rp, row + 4u * (cidx * EPC + e), t);
+                    }
+                    if (cidx == 0) {
+                        f32x4 t;
+                        t[0] = M;
+                        t[1] = Ls;
+                        t[2] = 0.f;
+                        t[3] = 0.f;
+                        if (local) stx4(rp, row + 4u * HD, t);
+                        else stc4(rp, row + 4u * HD, t);
+                    }
+                }
+            }
+            __syncthreads();
+        };
+        if (!batch && !resident && !empty) {
+            done_joint = true;
+            for (int cg = 0; cg < ncol; cg += kJoint) {
+                const int ce = min(ncol, cg + kJoint);
+                float q[kJoint][GH][EPC];
+                int tlo[kJoint];   // each column's first position (may be < 0)
+                Lane st[kJoint];
+#pragma unroll
+                for (int i = 0; i < kJoint; ++i) {
+                    if (cg + i >= ce) continue;
+                    load_q(q[i], cg + i);
+                    tlo[i] = W > 0 ? pos + cg + i - W + 1 : 0;
+                    st[i].init();
+                }
+                if (cg == 0) stamp(0);
+                if (cg > 0) {  // the next group streams the history again
+                    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // earlier ring reads are done
+                    for (int c = 0; c < npre; ++c) issue_chunk(c, c);
+                }
+                stream([&](const uint4 (&K)[NUB], const uint4 (&V)[NUB], const int (&tk)[NUB]) {
+#pragma unroll
+                    for (int i = 0; i < kJoint; ++i) {
+                        if (cg + i >= ce) continue;
+                        bool valid[NUB];
+#pragma unroll
+                        for (int u = 0; u < NUB; ++u) valid[u] = tk[u] < th && tk[u] >= tlo[i];
+                        st[i].template fold<NUB>(q[i], K, V, valid, ksc);
+                    }
+                });
+                if (cg == 0) stamp(2);
+#pragma unroll
+                for (int i = 0; i < kJoint; ++i)
+                    if (cg + i < ce) finish_column(st[i], q[i], cg + i, tlo[i]);
+            }
         }
-        __syncthreads();
+    }
+    if (!done_joint) {
+        for (int col = 0; col < ncol && !empty; ++col) {
+            const int pc = batch ? (int)a->bpos[col] : pos + col;   // this column's position
+            const int te = min(t1, pc + 1);
+            const int tlo = W > 0 ? pc - W + 1 : 0;   // this column's first position (may be < 0)
+            float q[GH][EPC];
+#pragma unroll
+            for (int h = 0; h < GH; ++h) {
+                const uint32_t qo = (uint32_t)((((size_t)col * Hq + qh0 + h) * HD + cidx * EPC) * 4);
+#pragma unroll
+                for (int e = 0; e < EPC; e += 4) {
+                    const f32x4 t = ldc4(rq, qo + 4u * e);
+#pragma unroll
+                    for (int k = 0; k < 4; ++k) q[h][e + k] = t[k] * qscale;
+                }
+            }
+            if (col == 0) stamp(0);
+            Lane st;
+            st.init();
+            if (col > 0 && !resident) {  // stream the history again for this column
+                if (batch) {   // its own sequence's history and pages
+                    th = min(t1, pc);
+                    ptab_s = col_ptab(a, col);
+                    nu = th > t0 ? (th - t0 + NS - 1) / NS : 0;
+                    nch = (nu + NUB - 1) / NUB;
+                    npre = min(nch, NB);
+                }
+                __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // earlier ring reads are done
+                for (int c = 0; c < npre; ++c) issue_chunk(c, c);
+            }
+            for (int c = 0; c < nch; ++c) {
+                const int b = c & (NB - 1);
+                wait_chunks(min(nch - 1 - c, NB - 1));        // chunk c has landed
+                uint4 K[NUB], V[NUB];
+                bool valid[NUB];
+#pragma unroll
+                for (int u = 0; u < NUB; ++u) {
+                    const MBG_LDS uint8_t* src = ring + (b * NUB + u) * 2 * kUnitBytes + lane * 16;
+                    const u32x4 kv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src);
+                    const u32x4 vv4 = *reinterpret_cast<const MBG_LDS u32x4*>(src + kUnitBytes);
+                    K[u] = make_uint4(kv4.x, kv4.y, kv4.z, kv4.w);
+                    V[u] = make_uint4(vv4.x, vv4.y, vv4.z, vv4.w);
+                    const int tk = tok_of(c * NUB + u);
+                    valid[u] = tk < th && tk >= tlo;
+                }
+                st.template fold<NUB>(q, K, V, valid, ksc);
+                if (c + NB < nch) {
+                    __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0());  // this buffer's reads are done
+                    issue_chunk(c + NB, b);
+                }
+            }
+            if (col == 0) stamp(2);
+            // positions written this step, up to this column's own
+            if (has_new) {
+                const uint4 K[1] = {Kn}, V[1] = {Vn};
+                const bool valid[1] = {batch ? ld_new && tl == col : tl < ncol && tn < te && tn >= tlo};
+                st.template fold<1>(q, K, V, valid, ksc);
+            }
+            if constexpr (KVF == F_FP8) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h)
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) st.o[h][e] *= vsc;
+            }
+            // merge the token slots of a wave (lanes with the same cidx)
+            if constexpr (LPT <= 4) st.template merge_partner<4>();
+            if constexpr (LPT <= 8) st.template merge_partner<8>();
+            if constexpr (LPT <= 16) st.template merge_partner<16>();
+            st.template merge_partner<32>();
+            // then the waves, through LDS, in wave order
+            if (lane < LPT) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    lds_f32* r = red + ((size_t)wave * GH + h) * stride;
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) r[cidx * EPC + e] = st.o[h][e];
+                    if (cidx == 0) {
+                        r[HD] = st.m[h];
+                        r[HD + 1] = st.l[h];
+                    }
+                }
+            }
+            __syncthreads();
+            if (wave == 0 && lane < LPT) {
+#pragma unroll
+                for (int h = 0; h < GH; ++h) {
+                    float M = red[h * stride + HD], Ls = red[h * stride + HD + 1];
+                    float O[EPC];
+#pragma unroll
+                    for (int e = 0; e < EPC; ++e) O[e] = red[h * stride + cidx * EPC + e];
+                    for (int w = 1; w < kWaves; ++w) {
+                        const lds_f32* r = red + ((size_t)w * GH + h) * stride;
+                        float mn, w1, w2;
+                        merge_weights(M, r[HD], mn, w1, w2);
+                        Ls = Ls * w1 + r[HD + 1] * w2;
+#pragma unroll
+                        for (int e = 0; e < EPC; ++e) O[e] = O[e] * w1 + r[cidx * EPC + e] * w2;
+                        M = mn;
+                    }
+                    const uint32_t row = (uint32_t)((((size_t)col * Hq + qh0 + h) * S_ + s) * stride * 4);
+#pragma unroll
+                    for (int e = 0; e < EPC; e += 4) {
+                        f32x4 t;
+                        t[0] = O[e];
+                        t[1] = O[e + 1];
+                        t[2] = O[e + 2];
+                        t[3] = O[e + 3];
+                        if (local) stx4(rp, row + 4u * (cidx * EPC + e), t);
+                        else stc4(rp, row + 4u * (cidx * EPC + e), t);
+                    }
+                    if (cidx == 0) {
+                        f32x4 t;
+                        t[0] = M;
+                        t[1] = Ls;
+                        t[2] = 0.f;
+                        t[3] = 0.f;
+                        if (local) stx4(rp, row + 4u * HD, t);
+                        else stc4(rp, row + 4u * HD, t);
+                    }
+                }
+            }
+            __syncthreads();
+        }
     }
     stamp(1);
     // arrival; the last split of this KV head combines all of them

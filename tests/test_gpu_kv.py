@@ -113,6 +113,37 @@ def test_dense2b_fp8_kv_steps():
     _teacher_forced(dm, om, oc, cfg, 3, "dense2b-fp8kv")
 
 
+@pytest.mark.parametrize("kv,k", [("bf16", 4), ("fp8", 3), ("fp8", 4)])
+def test_verify_window_streamed_history(kv, k):
+    """A verify window whose split histories are longer than the attention
+    ring (24,000 positions: over 512 per split), so the history streams
+    through LDS instead of staying resident there.  Over the FP8 cache the
+    window's columns fold each history chunk as it passes (all k at once, or
+    two pairs for k = 4, the second pair streaming the history again); over
+    the BF16 cache each column streams it in turn.  Every column is compared
+    with the oracle."""
+    cfg = CONFIGS["dense2b"].with_(name="dense2b", kv_dtype=kv, prefill=24000, n_decode=8,
+                                   shuffled_pages=True)
+    say("streamed-history verify", kv, k)
+    dm, om, oc = build_dense(cfg)
+    info = dm.info()
+    assert (cfg.prefill + info.attn_splits - 1) // info.attn_splits > 512, "splits must not fit the ring"
+    p0 = cfg.prefill
+    toks = [int(t) for t in gen.prompt_tokens(cfg, k)]
+    win = torch.tensor(toks, dtype=torch.int32, device="cuda")
+    logits = torch.empty((k, cfg.vocab), dtype=torch.float32, device="cuda")
+    am = torch.zeros(k, dtype=torch.int32, device="cuda")
+    dm.verify(win, p0, logits, am)
+    torch.cuda.synchronize()
+    g = logits.cpu().numpy()
+    amh = am.cpu().numpy()
+    ref = om.verify(oc, toks, p0)
+    for j in range(k):
+        compare_logits(g[j], ref[j], what=f"{kv} streamed verify col {j}")
+        check_argmax(int(amh[j]), g[j], ref[j], what=f"{kv} streamed verify col {j}")
+    assert dm.status() == 0
+
+
 @pytest.mark.parametrize("k", [2, 4])
 def test_fp8_kv_verify_window(k):
     """Verify window on the FP8-cache kernel: k tokens in one launch against
