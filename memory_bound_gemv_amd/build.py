@@ -24,18 +24,55 @@ STEP_SHAPES = 4
 SOURCES = [("step.hip", i) for i in range(STEP_SHAPES)] + [("ops.hip", None), ("api.cpp", None)]
 
 
+def _code_tokens(text: str) -> str:
+    """C/C++ source with every run of whitespace and comments turned into
+    one separator (a newline if the run holds one outside a comment, else a
+    space), string and character literals kept as written: what the
+    compiler sees, so that a comment or layout edit does not rename the
+    build."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif c.isspace() or text.startswith("//", i) or text.startswith("/*", i):
+            newline = False
+            while i < n:
+                if text[i].isspace():
+                    newline = newline or text[i] == "\n"
+                    i += 1
+                elif text.startswith("//", i):
+                    j = text.find("\n", i)
+                    i = n if j < 0 else j
+                elif text.startswith("/*", i):
+                    j = text.find("*/", i + 2)
+                    i = n if j < 0 else j + 2
+                else:
+                    break
+            out.append("\n" if newline else " ")
+        else:
+            out.append(c)
+            i += 1
+    return "".join(out)
+
+
 def source_digest() -> str:
-    """SHA-256 over the library's sources, the public header and the flags:
-    names the kernel build that a stored counter measurement belongs to."""
+    """SHA-256 over the library's sources (comments and layout aside), the
+    public header and the flags: names the kernel build that a stored
+    counter measurement belongs to."""
     h = hashlib.sha256()
     names = sorted(os.listdir(CSRC))
     for n in names:
         if n.endswith((".hip", ".cpp", ".h")):
             h.update(n.encode())
-            with open(os.path.join(CSRC, n), "rb") as f:
-                h.update(f.read())
-    with open(os.path.join(INCLUDE, "mbg.h"), "rb") as f:
-        h.update(f.read())
+            with open(os.path.join(CSRC, n), encoding="utf-8") as f:
+                h.update(_code_tokens(f.read()).encode())
+    with open(os.path.join(INCLUDE, "mbg.h"), encoding="utf-8") as f:
+        h.update(_code_tokens(f.read()).encode())
     h.update(" ".join(f for f in FLAGS if f not in (INCLUDE, CSRC)).encode())
     return h.hexdigest()[:16]
 

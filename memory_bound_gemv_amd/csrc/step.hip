@@ -1415,8 +1415,9 @@ __device__ __forceinline__ bool op_down(Ctx a, uint32_t layer, uint32_t tile, ui
 //           for all columns of a verify window (the article's observation
 //           that expert activation is the verify cost);
 //   EXPDOWN x += sum over slots of D_slot h_slot: an output row is the
-//           gather of the slots' row segments, streamed in passes of
-//           kSlotsPerPass slots whose h fits in LDS.
+//           gather of the slots' row segments, streamed in passes whose h
+//           fits in LDS: kSlotsPerPass slots of the step for one column, one
+//           pass per column over that column's own slots for a window.
 
 struct RouteLds {
     uint32_t mask[kMaxExperts / 32];
