@@ -133,7 +133,7 @@ typedef struct {
     int32_t n_experts, top_k, n_shared, moe_ffn; /* n_experts = 0: dense */
     float rope_theta; /* RoPE base; pairs (i, i + d/2) turn by pos * theta^(-2i/d) */
     float rms_eps;    /* RMSNorm: x / sqrt(mean(x^2) + eps) * g */
-    int32_t page_size;
+    int32_t page_size; /* positions per KV page: a power of two, >= 16 */
     int32_t max_pos;  /* KV capacity in positions */
     int32_t k_max;    /* widest verify window, 1..4 */
     /* Sliding-window layers: host array [n_layers], read during init only,

@@ -149,6 +149,10 @@ int check_config(const mbg_config* c) {
             return fail(MBG_E_UNSUPPORTED, "config: moe_ffn %d must be a positive multiple of 32", c->moe_ffn);
     }
     if (c->page_size <= 0 || c->max_pos <= 0) return fail(MBG_E_INVALID_ARG, "config: page_size/max_pos");
+    // an attention instruction reads up to 16 consecutive positions from one
+    // page, and the kernels index pages by shifts
+    if (c->page_size < 16 || (c->page_size & (c->page_size - 1)) != 0)
+        return fail(MBG_E_UNSUPPORTED, "config: page_size %d (a power of two, >= 16)", c->page_size);
     if (c->k_max < 1 || c->k_max > 4) return fail(MBG_E_UNSUPPORTED, "config: k_max %d (1..4)", c->k_max);
     if (c->layer_window)
         for (int l = 0; l < c->n_layers; ++l)
@@ -366,6 +370,7 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     a.rms_eps = c.rms_eps;
     a.attn_scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
     a.page_size = c.page_size;
+    a.page_shift = __builtin_ctz((unsigned)c.page_size);
     a.max_pos = c.max_pos;
 
     // kernels, LDS, occupancy -> grid

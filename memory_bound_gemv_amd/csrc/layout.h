@@ -93,6 +93,7 @@ struct StepArgs {
     float rms_eps;
     float attn_scale_log2;  // log2(e) / sqrt(head_dim)
     int32_t page_size, max_pos;
+    int32_t page_shift;     // log2(page_size) (a power of two)
     // tiling: tasks (workgroups) per phase; each wavefront of a phase owns
     // the output rows u = wave_id + n_waves * i of that phase
     uint32_t tiles_qkv, tiles_o, tiles_gu, tiles_down, tiles_lm;

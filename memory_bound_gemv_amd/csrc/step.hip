@@ -80,6 +80,7 @@ __device__ __forceinline__ const MBG_CONST int32_t* col_ptab(Ctx a, int c) {
     const MBG_CONST int32_t* p = (const MBG_CONST int32_t*)a->page_table;
     return a->batch ? p + (size_t)a->bseq[c] * a->pt_stride : p;
 }
+
 __device__ __forceinline__ uint32_t token_ctr_index(Ctx a) { return (uint32_t)a->n_layers * PH_COUNT; }
 
 // Cross-workgroup data (residual stream, q, new K/V, attention partials and
@@ -492,7 +493,7 @@ __device__ __forceinline__ bool op_qkv(Ctx a, uint32_t layer, uint32_t tile, uin
     // the pages of the columns' positions (scalar loads)
     int page_c[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) page_c[c] = col_ptab(a, c)[col_pos(a, c) / a->page_size];
+    for (int c = 0; c < NC; ++c) page_c[c] = col_ptab(a, c)[col_pos(a, c) >> a->page_shift];
     if (!wait_counter(a, wctr, wneed)) return false;
     if (layer == 0) {
         int tok[NC];
@@ -550,7 +551,7 @@ __device__ __forceinline__ bool op_qkv(Ctx a, uint32_t layer, uint32_t tile, uin
 #pragma unroll
         for (int cc = 1; cc < NC; ++cc)
             if (c == cc) page = page_c[cc];
-        const int slot = p - (p / a->page_size) * a->page_size;
+        const int slot = p & (a->page_size - 1);
         const size_t off = (size_t)layer * a->kv_layer_stride +
                            ((((size_t)page * 2 + kv) * Hkv + gh) * a->page_size + slot) * HD + i;
         if constexpr (S::KVF == F_BF16) {
@@ -769,21 +770,31 @@ __device__ __forceinline__ bool op_attn(Ctx a, uint32_t layer, uint32_t tile, ui
     auto tok_of = [&](int i) { return t0 + (i * kWaves + wave) * TPI + tl; };
     const MBG_CONST int32_t* ptab_s = col_ptab(a, 0);   // the streamed column's page table
     const size_t lane_off = (size_t)tl * HD * EB + (size_t)cidx * 16;
+    const int pshift = a->page_shift, pmask = page_size - 1;
     // Request chunk c of history into ring buffer b: NUB units, each one K and
-    // one V instruction.  A unit's TPI positions share a page, so its page is
-    // one scalar load (counted apart from the vector loads the waits count).
-    // Units past the history re-read the split's first unit, so every chunk
-    // is the same number of loads.
+    // one V instruction.  A unit's TPI positions share a page (a page is a
+    // power of two >= 16 positions and units start TPI-aligned), so its page
+    // is one scalar load (counted apart from the vector loads the waits
+    // count).  Units past the history re-read the split's first unit, so
+    // every chunk is the same number of loads.
+    // (per task: bytes of a physical page over all KV heads, K -> V within
+    // a page, and this KV head's rows in page 0 of the layer)
+    const size_t page_bytes = (size_t)2 * Hkv * page_size * HD * EB;
+    const size_t vstep = (size_t)Hkv * page_size * HD * EB;
+    const MBG_GLOBAL uint8_t* head0 = pool + (layer_off + (size_t)g * page_size * HD) * EB + lane_off;
     auto issue_chunk = [&](int c, int b) {
+        // the units' pages first (one wait for all their scalar loads)
+        int tbs[NUB], pages[NUB];
 #pragma unroll
         for (int u = 0; u < NUB; ++u) {
-            int tb = t0 + ((c * NUB + u) * kWaves + wave) * TPI;
-            tb = __builtin_amdgcn_readfirstlane(tb < th ? tb : t0);
-            const int lp = tb / page_size;
-            const int page = ptab_s[lp];
-            const size_t el = layer_off + ((((size_t)page * 2) * Hkv + g) * page_size + (tb - lp * page_size)) * HD;
-            const size_t vstep = (size_t)Hkv * page_size * HD * EB;   // K -> V of the same page
-            const MBG_GLOBAL uint8_t* kp = pool + el * EB + lane_off;
+            const int tb = t0 + ((c * NUB + u) * kWaves + wave) * TPI;
+            tbs[u] = __builtin_amdgcn_readfirstlane(tb < th ? tb : t0);
+            pages[u] = ptab_s[tbs[u] >> pshift];
+        }
+#pragma unroll
+        for (int u = 0; u < NUB; ++u) {
+            const int tb = tbs[u];
+            const MBG_GLOBAL uint8_t* kp = head0 + (size_t)pages[u] * page_bytes + (size_t)((tb & pmask) * HD * EB);
             MBG_LDS uint8_t* dst = ring + (b * NUB + u) * 2 * kUnitBytes;
             if (!batch && tb + TPI > a.pos - a.step) {   // rows this launch writes (an earlier step's K/V): coherent loads
                 lds_dma16_coh(kp, (MBG_LDS void*)dst);
@@ -803,7 +814,7 @@ __device__ __forceinline__ bool op_attn(Ctx a, uint32_t layer, uint32_t tile, ui
     // positions this step writes, the FP8 scales
     int page_new[NC];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) page_new[c] = col_ptab(a, c)[col_pos(a, c) / page_size];
+    for (int c = 0; c < NC; ++c) page_new[c] = col_ptab(a, c)[col_pos(a, c) >> pshift];
     const MBG_CONST float* kvs = (const MBG_CONST float*)a->kv_scales;
     const float ksc = KVF == F_FP8 ? kvs[((size_t)layer * Hkv + g) * 2 + 0] : 1.f;
     const float vsc = KVF == F_FP8 ? kvs[((size_t)layer * Hkv + g) * 2 + 1] : 1.f;
@@ -823,7 +834,7 @@ __device__ __forceinline__ bool op_attn(Ctx a, uint32_t layer, uint32_t tile, ui
         for (int c = 1; c < NC; ++c)
             if ((batch ? tl : tn - pos) == c) page = page_new[c];
         const size_t el =
-            layer_off + ((((size_t)page * 2) * Hkv + g) * page_size + (tn - (tn / page_size) * page_size)) * HD;
+            layer_off + ((((size_t)page * 2) * Hkv + g) * page_size + (tn & pmask)) * HD;
         const MBG_GLOBAL uint8_t* kp = pool + el * EB + (size_t)cidx * 16;
         Kn = ldc16(reinterpret_cast<const MBG_GLOBAL uint4*>(kp));
         Vn = ldc16(reinterpret_cast<const MBG_GLOBAL uint4*>(kp + (size_t)Hkv * page_size * HD * EB));

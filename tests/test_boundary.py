@@ -51,6 +51,15 @@ def test_validate_config_errors(M):
     assert M.mbg_validate(_cfg(M, layer_window=[0, 2048])) == 0
     assert M.mbg_validate(_cfg(M, layer_window=[1, 0])) == 0
     assert M.mbg_validate(_cfg(M, layer_window=[5, -1])) == M.MBG_E_INVALID_ARG
+    # KV pages: a power of two of at least 16 positions (an attention
+    # instruction reads up to 16 consecutive positions from one page)
+    for ps in (16, 32, 64, 256):
+        assert M.mbg_validate(_cfg(M, page_size=ps)) == 0, ps
+    for ps in (8, 12, 48, 96):
+        assert M.mbg_validate(_cfg(M, page_size=ps)) == M.MBG_E_UNSUPPORTED, ps
+    assert M.mbg_validate(_cfg(M, page_size=0)) == M.MBG_E_INVALID_ARG
+    M.mbg_validate(_cfg(M, page_size=48))
+    assert "page_size 48" in M.mbg_last_error()
     M.mbg_validate(_cfg(M, head_dim=96))
     assert "head_dim 96" in M.mbg_last_error()
 
