@@ -38,6 +38,8 @@
 namespace mbg {
 
 constexpr int kThreads = 256;
+constexpr int kLogThreads = 8;
+static_assert(kThreads == 1 << kLogThreads, "threads per workgroup");
 constexpr int kWaves = kThreads / kWave;
 // Upper bound of Q/K/V rows one wavefront owns in a step (pairs * 2).
 constexpr int kQkvRowsPerWave = 64;
@@ -1169,24 +1171,34 @@ __device__ __forceinline__ bool op_attn(Ctx a, uint32_t layer, uint32_t tile, ui
     lds_f32* tot = wts + nch_ * 64;                  // [nch_]: weighted sum of l
     lds_f32* accl = smem + kAttnRingBytes / 4;       // [kThreads][4]: group partial sums (merge area)
     const int nload = nch_ * nsv * vpr;
-    for (int i0 = 0; i0 < nload; i0 += 8 * kThreads) {
-        f32x4 t[8];
+    // rs / nsv as a multiply-high by ceil(2^32 / nsv) (rs itself for one
+    // split, where that would not fit 32 bits): exact here (rs < 2^16,
+    // nsv <= 64), where a division by a runtime value would cost ~25
+    // instructions per load on the combine's critical path
+    const uint32_t nsv_inv = nsv > 1 ? 0xFFFFFFFFu / (uint32_t)nsv + 1u : 0u;
+    auto stage1 = [&](auto vprc) {
+        constexpr int VPR = decltype(vprc)::value;   // the vectors per (row, split): RV or 1
+        for (int i0 = 0; i0 < nload; i0 += 8 * kThreads) {
+            f32x4 t[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int idx = min(i0 + k * kThreads + (int)threadIdx.x, nload - 1);
-            const int rs = idx / vpr, v = idx - rs * vpr;
-            const int ch = rs / nsv, sp = rs - ch * nsv;
-            const int col = ch / GH, h = ch - col * GH;
-            const int vec = whole ? v : HDV;
-            const uint32_t po = (uint32_t)(((((size_t)col * Hq + qh0 + h) * S_ + sp) * stride + vec * 4) * 4);
-            t[k] = local ? ldx4(rp, po) : ldc4(rp, po);
-        }
+            for (int k = 0; k < 8; ++k) {
+                const int idx = min(i0 + k * kThreads + (int)threadIdx.x, nload - 1);
+                const int rs = idx / VPR, v = idx - rs * VPR;
+                const int ch = nsv > 1 ? (int)__umulhi((uint32_t)rs, nsv_inv) : rs, sp = rs - ch * nsv;
+                const int col = ch / GH, h = ch - col * GH;
+                const int vec = VPR == RV ? v : HDV;
+                const uint32_t po = (uint32_t)(((((size_t)col * Hq + qh0 + h) * S_ + sp) * stride + vec * 4) * 4);
+                t[k] = local ? ldx4(rp, po) : ldc4(rp, po);
+            }
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int idx = i0 + k * kThreads + (int)threadIdx.x;
-            if (idx < nload) *reinterpret_cast<MBG_LDS f32x4*>(prt + 4 * idx) = t[k];
+            for (int k = 0; k < 8; ++k) {
+                const int idx = i0 + k * kThreads + (int)threadIdx.x;
+                if (idx < nload) *reinterpret_cast<MBG_LDS f32x4*>(prt + 4 * idx) = t[k];
+            }
         }
-    }
+    };
+    if (whole) stage1(std::integral_constant<int, RV>{});
+    else stage1(std::integral_constant<int, 1>{});
     __syncthreads();
     // stage 2: one wavefront per row, one lane per split: the maximum, the
     // weights and their l-weighted sum are wavefront reductions
@@ -1206,10 +1218,12 @@ __device__ __forceinline__ bool op_attn(Ctx a, uint32_t layer, uint32_t tile, ui
     // A thread owns one 16-byte slice of a row and every ng-th split; ng
     // thread groups then add up in group order.
     const int pairs = nch_ * HDV;
-    const int fit = kThreads / pairs;
-    const int ng = fit >= 8 ? 8 : fit >= 4 ? 4 : fit >= 2 ? 2 : 1;
-    const int tpg = kThreads / ng;
-    const int grp = (int)threadIdx.x / tpg, pl = (int)threadIdx.x - grp * tpg;
+    // ng = 8, 4, 2 or 1 groups of tpg = kThreads / ng threads: as many as
+    // leave every pair a thread (shifts, not runtime divisions)
+    const int lng = pairs <= kThreads / 8 ? 3 : pairs <= kThreads / 4 ? 2 : pairs <= kThreads / 2 ? 1 : 0;
+    const int ng = 1 << lng;
+    const int tpg = kThreads >> lng;
+    const int grp = (int)threadIdx.x >> (kLogThreads - lng), pl = (int)threadIdx.x & (tpg - 1);
     const rsrc_t ra = make_rsrc(a->attn);
     for (int base = 0; base < pairs; base += tpg) {
         const int pr = base + pl;
