@@ -57,7 +57,7 @@ def _code_tokens(text: str) -> str:
         else:
             out.append(c)
             i += 1
-    return "".join(out)
+    return "".join(out).strip()
 
 
 def source_digest() -> str:
