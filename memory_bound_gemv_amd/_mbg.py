@@ -82,6 +82,16 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is missing: build it with memory_bound_gemv_amd.build.build() "
                           "(the decode path has no fallback)")
+    # The library and the caller's PyTorch must share one HIP runtime: PyTorch
+    # ships its own, and when that is loaded first the library's dependency
+    # resolves to it.  Loaded the other way round the process holds two
+    # runtimes, and the library's sees no device once PyTorch has claimed it
+    # (measured: hipGetDevice fails in mbg_decode_init).  So PyTorch, when
+    # installed, is imported before the library is loaded.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = C.CDLL(LIB_PATH)
     sig = {
         "mbg_workspace_size": (C.c_int, [C.POINTER(mbg_config), C.POINTER(C.c_size_t)]),

@@ -433,7 +433,12 @@ int mbg_decode_init(const mbg_config* cfg, const mbg_weights* w, const mbg_kv* k
     const int head_groups = gq / std::min(gq, kAttnHeadsPerTask);
     int S = G / (c.n_kv_heads * head_groups);
     S = std::max(1, std::min(S, kMaxSplits));
-    S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 128)));   // >= ~128 positions per split
+    // at least ~176 positions per split: fewer, longer splits than the grid
+    // allows shorten the combine, which every layer waits for, and measured
+    // best on the dense and routed steps (11 workgroup token slots; 128
+    // positions per split or ~40 % more than 176 were slower)
+    S = std::min<int>(S, (int)std::max<int64_t>(1, cdiv(c.max_pos, 176)));
+    if (S > 4) S -= S % 4;   // whole groups of four splits (the XCD-local placement needs them)
     a.attn_splits = S;
     // prefetch defaults chosen by measurement on the dense 2B step; the
     // environment overrides documented at mbg_decode_init replace them

@@ -1,12 +1,14 @@
 """The kernel-source digest that ties a stored counter summary (profiles/) to
 a build: comments and layout do not change it, code does."""
+import importlib.util
 import os
-import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-sys.path.insert(0, ROOT)
-
-from memory_bound_gemv_amd.build import _code_tokens  # noqa: E402
+# build.py by path: importing the package would load the library
+_spec = importlib.util.spec_from_file_location("_mbg_build", os.path.join(ROOT, "memory_bound_gemv_amd", "build.py"))
+_build = importlib.util.module_from_spec(_spec)
+_spec.loader.exec_module(_build)
+_code_tokens = _build._code_tokens
 
 
 def test_comments_and_layout_are_ignored():

@@ -419,3 +419,27 @@ def test_multi_step_range_checks():
             dm.steps(tok, n, pos, None, out)
         assert e.value.code == M.MBG_E_RANGE
     assert dm.status() == 0
+
+
+def test_package_import_before_torch():
+    """Importing the package before PyTorch still gives a working library
+    (the binding loads PyTorch's HIP runtime first; loaded the other way
+    round, mbg_decode_init found no device).  In a fresh process that imports
+    the package first: a tiny context initialises (no kernel is launched,
+    as this test's own process holds the GPU meanwhile)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("import memory_bound_gemv_amd\n"
+            "from memory_bound_gemv_amd.device_model import DeviceModel\n"
+            "from synth import CONFIGS, gen\n"
+            "cfg = CONFIGS['tiny']\n"
+            "dm = DeviceModel(cfg, gen.dense_weights(cfg), gen.page_table(cfg), device='cuda:0')\n"
+            "dm.init()\n"
+            "assert dm.status() == 0\n"
+            "print('init ok', dm.info().grid)\n"
+            "dm.close()\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout[-2000:] + r.stderr[-2000:]
+    assert "init ok" in r.stdout
