@@ -217,6 +217,31 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
     return max(r[0], r[1]);
 }
 
+// The same over 64-bit keys (both halves move through the same lane
+// permutation, then one 64-bit compare per step).
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    return ((uint64_t)dpp_u32<CTRL>((uint32_t)(v >> 32)) << 32) | dpp_u32<CTRL>((uint32_t)v);
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) {
+    return a > b ? a : b;
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    v = max_u64(v, dpp_u64<0xB1>(v));
+    v = max_u64(v, dpp_u64<0x4E>(v));
+    v = max_u64(v, dpp_u64<0x141>(v));
+    v = max_u64(v, dpp_u64<0x140>(v));
+    uint32_t h = (uint32_t)(v >> 32), l = (uint32_t)v;
+    auto rh = __builtin_amdgcn_permlane16_swap(h, h, false, false);
+    auto rl = __builtin_amdgcn_permlane16_swap(l, l, false, false);
+    v = max_u64(((uint64_t)rh[0] << 32) | rl[0], ((uint64_t)rh[1] << 32) | rl[1]);
+    h = (uint32_t)(v >> 32);
+    l = (uint32_t)v;
+    rh = __builtin_amdgcn_permlane32_swap(h, h, false, false);
+    rl = __builtin_amdgcn_permlane32_swap(l, l, false, false);
+    return max_u64(((uint64_t)rh[0] << 32) | rl[0], ((uint64_t)rh[1] << 32) | rl[1]);
+}
+
 // Inclusive prefix sum within each 16-lane row (Hillis-Steele over row
 // shifts; lanes shifted in from outside the row contribute 0).
 __device__ __forceinline__ uint32_t row_prefix_sum(uint32_t v) {

@@ -1473,10 +1473,14 @@ __device__ __forceinline__ uint32_t ordered_key32(float f) {
 
 // Routing of this step, from the router logits (float32 [k][E]), into
 // s_route.  Wave c < NC picks column c's top-k: lane l holds experts
-// 8l .. 8l+7, each as a 32-bit order key of its logit and a 32-bit key of
-// its index (larger for a lower index); k rounds take the largest (value,
-// then lower index) out one by one, each round a wave maximum of the value
-// keys followed by one of the index keys among the values equal to it.
+// 8l .. 8l+7 and k rounds take the largest (value, then lower index) out
+// one by one.  One column: each expert as a 64-bit key (the order key of
+// its logit above a key of its index, larger for a lower index), a lane's
+// eight keys sorted, each round one wave maximum of the lanes' first keys.
+// Several columns (kernels at their register limit, where the sorted keys
+// would cost registers in the expert streams): a value key and an index key
+// per expert, each round a wave maximum of the value keys and one of the
+// index keys among the values equal to it.
 // Weights are exp(r_j - r_max) / sum over the picked j, which equals the
 // picked softmax probabilities renormalised to sum to one.  The slots (the
 // union of picked experts, by increasing id, then the shared experts) come
@@ -1501,51 +1505,111 @@ __device__ __forceinline__ void route_slots(Ctx a, uint32_t layer) {
     if (wave < NC) {
         const int c = wave;
         const rsrc_t rl = make_rsrc(a->rlogits);
-        uint32_t hi[8], lo[8];
         const bool has = 8 * lane < E;
         f32x4 v0 = {0.f, 0.f, 0.f, 0.f}, v1 = {0.f, 0.f, 0.f, 0.f};
         if (has) {
             v0 = ldc4(rl, (uint32_t)((c * E + 8 * lane) * 4));
             v1 = ldc4(rl, (uint32_t)((c * E + 8 * lane + 4) * 4));
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const float v = i < 4 ? v0[i] : v1[i - 4];
-            hi[i] = has ? ordered_key32(v) : 0u;      // finite logits give keys > 0
-            lo[i] = 0xFFFFFFFFu - (8u * lane + i);
-        }
-        if (threadIdx.x == 0) s_stamp[2] = wall_clock64() | (hi[0] & 1u);   // logits loaded
-        float top_v = 0.f, wsum = 0.f;
-        uint32_t word = 0u;   // lane w < kMaskWords: bit b = expert 32 w + b picked (wave 0, NC = 1)
-#pragma unroll
-        for (int k = 0; k < kMaxTopK; ++k) {
-            if (k >= K) break;
-            uint32_t hm = hi[0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) hm = max(hm, hi[i]);
-            hm = wave_max_u32(hm);
-            uint32_t lm = 0u;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) lm = max(lm, hi[i] == hm ? lo[i] : 0u);
-            lm = wave_max_u32(lm);
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                if (hi[i] == hm && lo[i] == lm) hi[i] = 0u;
-            const int esel = (int)(0xFFFFFFFFu - lm);
-            const float vsel = from_ordered_key32(hm);
-            if (k == 0) top_v = vsel;
-            const float ex = expf(vsel - top_v);
-            wsum += ex;
-            if (lane == 0) {
-                R.sel[c][k] = esel;
-                R.selw[c][k] = ex;
-                if constexpr (NC > 1) atomicOr(&R.mask[esel >> 5], 1u << (esel & 31));
-            }
-            if constexpr (NC == 1) word |= lane == (esel >> 5) ? 1u << (esel & 31) : 0u;
-        }
-        if (lane < K) R.selw[c][lane] = R.selw[c][lane] / wsum;
         if constexpr (NC == 1) {
-            if (lane < kMaskWords) R.mask[lane] = word;
+            // key = (value key << 32) | (2^32 - 1 - index): distinct for every
+            // expert, so the largest key is one lane's and the order is by
+            // value, then by lower index
+            uint64_t s[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = i < 4 ? v0[i] : v1[i - 4];
+                const uint32_t hk = has ? ordered_key32(v) : 0u;      // finite logits give keys > 0
+                s[i] = ((uint64_t)hk << 32) | (0xFFFFFFFFu - (8u * lane + i));
+            }
+            if (threadIdx.x == 0) s_stamp[2] = wall_clock64() | (uint32_t)(s[0] >> 32 & 1u);   // logits loaded
+            // the lane's keys in descending order (odd-even merge network)
+            auto cx = [&](int i, int j) {
+                const uint64_t a = s[i], b = s[j];
+                s[i] = max_u64(a, b);
+                s[j] = a > b ? b : a;
+            };
+            cx(0, 1); cx(2, 3); cx(4, 5); cx(6, 7);
+            cx(0, 2); cx(1, 3); cx(4, 6); cx(5, 7);
+            cx(1, 2); cx(5, 6);
+            cx(0, 4); cx(1, 5); cx(2, 6); cx(3, 7);
+            cx(2, 4); cx(3, 5);
+            cx(1, 2); cx(3, 4); cx(5, 6);
+            // each round: the wave maximum of the lanes' first keys, which its
+            // lane then drops.  The value keys alone decide it unless two lanes
+            // hold the largest value (then the full keys do)
+            uint64_t mine = 0;   // lane k < K: the k-th pick
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {
+                if (k >= K) break;
+                const uint32_t hh = (uint32_t)(s[0] >> 32);
+                const uint32_t hm = wave_max_u32(hh);
+                const uint64_t at = __builtin_amdgcn_ballot_w64(hh == hm);
+                uint64_t m;
+                if (__builtin_popcountll(at) == 1)
+                    m = ((uint64_t)hm << 32) | (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)s[0], __builtin_ctzll(at));
+                else
+                    m = wave_max_u64(s[0]);
+                const bool win = s[0] == m;
+#pragma unroll
+                for (int i = 0; i < 7; ++i) s[i] = win ? s[i + 1] : s[i];
+                s[7] = win ? 0ull : s[7];
+                mine = lane == k ? m : mine;
+            }
+            // weights in pick order: exp(value - first value), summed from the first
+            const float top_v = from_ordered_key32((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(mine >> 32), 0));
+            const float ex = lane < K ? expf(from_ordered_key32((uint32_t)(mine >> 32)) - top_v) : 0.f;
+            float wsum = 0.f;
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {
+                if (k >= K) break;
+                wsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), k));
+            }
+            if (lane < K) {
+                const int esel = (int)(0xFFFFFFFFu - (uint32_t)mine);
+                R.sel[c][lane] = esel;
+                R.selw[c][lane] = ex / wsum;
+                atomicOr(&R.mask[esel >> 5], 1u << (esel & 31));
+            }
+        } else {
+            // several columns (one wave each): per lane a value key and an
+            // index key per expert; each round a wave maximum of the value
+            // keys, then one of the index keys among the values equal to it
+            uint32_t hi[8], lo[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float v = i < 4 ? v0[i] : v1[i - 4];
+                hi[i] = has ? ordered_key32(v) : 0u;      // finite logits give keys > 0
+                lo[i] = 0xFFFFFFFFu - (8u * lane + i);
+            }
+            if (threadIdx.x == 0) s_stamp[2] = wall_clock64() | (hi[0] & 1u);   // logits loaded
+            float top_v = 0.f, wsum = 0.f;
+#pragma unroll
+            for (int k = 0; k < kMaxTopK; ++k) {
+                if (k >= K) break;
+                uint32_t hm = hi[0];
+#pragma unroll
+                for (int i = 1; i < 8; ++i) hm = max(hm, hi[i]);
+                hm = wave_max_u32(hm);
+                uint32_t lm = 0u;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) lm = max(lm, hi[i] == hm ? lo[i] : 0u);
+                lm = wave_max_u32(lm);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if (hi[i] == hm && lo[i] == lm) hi[i] = 0u;
+                const int esel = (int)(0xFFFFFFFFu - lm);
+                const float vsel = from_ordered_key32(hm);
+                if (k == 0) top_v = vsel;
+                const float ex = expf(vsel - top_v);
+                wsum += ex;
+                if (lane == 0) {
+                    R.sel[c][k] = esel;
+                    R.selw[c][k] = ex;
+                    atomicOr(&R.mask[esel >> 5], 1u << (esel & 31));
+                }
+            }
+            if (lane < K) R.selw[c][lane] = R.selw[c][lane] / wsum;
         }
         if (threadIdx.x == 0) s_stamp[3] = wall_clock64();   // top-k picked
     }

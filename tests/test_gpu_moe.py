@@ -173,6 +173,53 @@ def test_moe_small_steps_and_verify():
     _verify(dm2, cfg, cfg.prefill, toks[:2], _steps_only, "moe_small k=2")
 
 
+def test_moe_small_routing_ties():
+    """Equal router logits: every router row is zero except experts 20, 30,
+    31 and 45, and the last three are one row, so each decision holds a tie
+    of three (two experts in one lane of the selection, one in another) and
+    one of the remaining zeros; the top-k takes equal values in index order
+    (the oracle's rule).  Picks and weights match the oracle exactly wherever
+    the three distinct values (a, b, 0) are apart, and a 4-token verify
+    window (one wave per column) matches its single steps."""
+    cfg = MOE_SMALL
+    host = gen.dense_weights(cfg)
+    for li in range(cfg.n_layers):
+        w = np.zeros_like(host[f"l{li}.w_router"])
+        w[20] = host[f"l{li}.w_router"][20]
+        w[[30, 31, 45]] = host[f"l{li}.w_router"][30]
+        host[f"l{li}.w_router"] = w
+    say("moe_small ties build")
+    dm, om, oc = build_moe(cfg, host=host)
+    toks = gen.prompt_tokens(cfg, 4)
+    tok = torch.zeros(1, dtype=torch.int32, device="cuda")
+    logits = torch.empty(cfg.vocab, dtype=torch.float32, device="cuda")
+    amax = torch.zeros(1, dtype=torch.int32, device="cuda")
+    steps, graded, zeros_picked = [], 0, 0
+    for i, t in enumerate(toks):
+        tok.fill_(int(t))
+        dm.step(tok, cfg.prefill + i, logits, amax)
+        torch.cuda.synchronize()
+        g = logits.cpu().numpy()
+        ref = om.step(oc, int(t), cfg.prefill + i)
+        compare_logits(g, ref, rel_tol=LOGIT_REL_L2_MXFP4, what=f"ties step {i}")
+        check_argmax(int(amax.item()), g, ref, what=f"ties step {i}")
+        for li in range(cfg.n_layers):
+            idx, wts = dm.routing(li)
+            sel, owts, r = om.last_routing[li]
+            a, b = float(r[20]), float(r[30])
+            assert r[30] == r[31] == r[45] and np.count_nonzero(r) <= 4
+            if min(abs(a), abs(b), abs(a - b)) > 1e-3:
+                assert list(idx[0]) == [int(e) for e in sel], f"layer {li} step {i}: {idx[0]} vs {sel}"
+                assert np.allclose(wts[0], owts, atol=2e-3), f"layer {li} step {i}: {wts[0]} vs {owts}"
+                graded += 1
+            zeros_picked += int(np.sum(idx[0] < 8))
+        steps.append((g.copy(), ref))
+    say("ties graded", graded, "of", 4 * cfg.n_layers, "zero-logit picks", zeros_picked)
+    assert graded >= 2 * cfg.n_layers and zeros_picked > 0
+    _verify(dm, cfg, cfg.prefill, toks, steps, "moe_small ties")
+    assert dm.status() == 0
+
+
 @pytest.mark.timeout(1500)
 def test_moe_full_step_and_verify():
     """The routed workload at full size: all 8 decode steps at 2048..2055,
