@@ -1482,9 +1482,10 @@ __device__ __forceinline__ uint32_t ordered_key32(float f) {
 // per expert, each round a wave maximum of the value keys and one of the
 // index keys among the values equal to it.
 // Weights are exp(r_j - r_max) / sum over the picked j, which equals the
-// picked softmax probabilities renormalised to sum to one.  The slots (the
-// union of picked experts, by increasing id, then the shared experts) come
-// from a prefix sum over the 16 words of the selection mask.
+// picked softmax probabilities renormalised to sum to one.  The slots are
+// the union of picked experts, by increasing id, then the shared experts:
+// for one column each pick's rank among the picks, for several a prefix sum
+// over the 16 words of the selection mask.
 // Inlined: as a called function the argument block would reach it through a
 // vector register, and every field read would become a vector memory load.
 template <int NC>
@@ -1499,7 +1500,6 @@ __device__ __forceinline__ void route_slots(Ctx a, uint32_t layer) {
         for (int i = threadIdx.x; i < kMaxSlots * 4; i += kThreads) (&R.wt[0][0])[i] = 0.f;
         __syncthreads();
     } else if (wave == 0) {   // wave 0 alone writes it below
-        if (lane < kMaskWords) R.mask[lane] = 0u;
         for (int i = lane; i < kMaxSlots * 4; i += kWave) (&R.wt[0][0])[i] = 0.f;
     }
     if (wave < NC) {
@@ -1565,11 +1565,32 @@ __device__ __forceinline__ void route_slots(Ctx a, uint32_t layer) {
                 if (k >= K) break;
                 wsum += __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ex), k));
             }
+            // the K picks are distinct experts: a pick's slot is its rank
+            // by expert id, and the shared experts follow
+            const int esel = (int)(0xFFFFFFFFu - (uint32_t)mine);
+            int rank = 0;
+#pragma unroll
+            for (int j = 0; j < kMaxTopK; ++j) {
+                if (j >= K) break;
+                rank += __builtin_amdgcn_readlane(esel, j) < esel;
+            }
             if (lane < K) {
-                const int esel = (int)(0xFFFFFFFFu - (uint32_t)mine);
-                R.sel[c][lane] = esel;
-                R.selw[c][lane] = ex / wsum;
-                atomicOr(&R.mask[esel >> 5], 1u << (esel & 31));
+                const float wk = ex / wsum;
+                R.sel[0][lane] = esel;
+                R.selw[0][lane] = wk;
+                R.slot_exp[rank] = esel;
+                R.wt[rank][0] = wk;
+            }
+            const int nsh = a->n_shared;
+            if (lane < nsh) {
+                R.slot_exp[K + lane] = E + lane;
+                R.wt[K + lane][0] = 1.f;
+            }
+            if (lane == 0) {
+                R.nrouted = K;
+                R.nslots = K + nsh;
+                R.layer = layer;
+                R.epoch = a.epoch;
             }
         } else {
             // several columns (one wave each): per lane a value key and an
@@ -1614,6 +1635,7 @@ __device__ __forceinline__ void route_slots(Ctx a, uint32_t layer) {
         if (threadIdx.x == 0) s_stamp[3] = wall_clock64();   // top-k picked
     }
     __syncthreads();
+    if constexpr (NC == 1) return;
     if (wave == 0) {
         const uint32_t m = lane < kMaskWords ? R.mask[lane] : 0u;
         const uint32_t cnt = (uint32_t)__builtin_popcount(m);
