@@ -229,7 +229,7 @@ def _threads():
     return int(max([p.get("num_threads", 1) for p in threadpool_info()] or [1]))
 
 
-def cpu_baseline(cfg, host, min_s: float = 10.0, max_steps: int = 20):
+def cpu_baseline(cfg, host, min_s: float = 10.0, max_steps: int = 200):
     """Time the CPU oracle (float64, as it stands) on a few decode steps of
     the same workload.  One untimed step first converts and caches the
     weights (and, for the routed model, the experts that step routes to);
