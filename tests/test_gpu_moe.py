@@ -173,6 +173,22 @@ def test_moe_small_steps_and_verify():
     _verify(dm2, cfg, cfg.prefill, toks[:2], _steps_only, "moe_small k=2")
 
 
+@pytest.mark.parametrize("top_k,n_shared", [(4, 2), (2, 0)])
+def test_moe_small_other_topk_and_shared(top_k, n_shared):
+    """Top-k and the shared-expert count are run-time: four routed experts
+    plus two shared ones, and two routed with none, on the compiled routed
+    shape; steps (logits, argmax, graded routing decisions and weights) and
+    a 4-token verify window against the oracle and the steps."""
+    cfg = MOE_SMALL.with_(name=f"moe_small_k{top_k}s{n_shared}", top_k=top_k, n_shared=n_shared)
+    say(cfg.name, "build")
+    dm, om, oc = build_moe(cfg)
+    toks = gen.prompt_tokens(cfg, 4)
+    steps, routed = _steps(dm, om, oc, cfg, cfg.prefill, toks, cfg.name)
+    say(cfg.name, "graded routing decisions", routed)
+    assert routed >= 4
+    _verify(dm, cfg, cfg.prefill, toks, steps, cfg.name)
+
+
 def test_moe_small_routing_ties():
     """Equal router logits: every router row is zero except experts 20, 30,
     31 and 45, and the last three are one row, so each decision holds a tie
